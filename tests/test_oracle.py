@@ -1,0 +1,378 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Library conversions (torch's float8/e8m0/bf16 casts), published format
+tables (tests/golden), closed forms, invariants, brute force on tiny inputs
+and exact integer / rational arithmetic on slices.
+"""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from quantized_mixture_experts_moe_amd import synth
+from quantized_mixture_experts_moe_amd.shapes import MoEShape, W4A16_TINY
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_table(name):
+    rows = []
+    for line in open(os.path.join(GOLDEN, name)):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        c, v = line.split()
+        rows.append((int(c, 16), float(v)))
+    return rows
+
+
+# ---------------------------------------------------------------- formats
+
+def test_e2m1_table_matches_ocp_spec():
+    for code, v in _read_table("ocp_e2m1_values.txt"):
+        got = O.E2M1_TABLE[code]
+        assert got == v and math.copysign(1, got) == math.copysign(1, v), (code, got, v)
+
+
+def test_e4m3_points_match_ofp8_spec():
+    for code, v in _read_table("ocp_e4m3_points.txt"):
+        got = O.E4M3_TABLE[code]
+        if math.isnan(v):
+            assert math.isnan(got)
+        else:
+            assert got == v, (hex(code), got, v)
+
+
+def test_e4m3_decode_matches_torch_all_codes():
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    got = O.e4m3_values(np.arange(256, dtype=np.uint8))
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(ref))
+    m = ~np.isnan(ref)
+    np.testing.assert_array_equal(got[m], ref[m])
+
+
+def test_e4m3_encode_matches_torch_rne():
+    rng = np.random.default_rng(5)
+    finite = O.E4M3_TABLE[~np.isnan(O.E4M3_TABLE)]
+    mids = (np.sort(np.unique(finite))[1:] + np.sort(np.unique(finite))[:-1]) / 2
+    vals = np.concatenate([
+        rng.uniform(-448, 448, 20000), rng.standard_normal(20000) * 0.01,
+        rng.standard_normal(20000) * 30, finite, mids, [0.0, -0.0, 2.0 ** -10, 3 * 2.0 ** -10],
+    ]).astype(np.float32)
+    ref = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = O.e4m3_encode(vals)
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, [(vals[i], got[i], ref[i]) for i in bad[:5]]
+
+
+def test_e4m3_encode_saturates():
+    got = O.e4m3_encode(np.array([448.0, 449.0, 470.0, 1e9, -500.0]))
+    np.testing.assert_array_equal(got, [0x7E, 0x7E, 0x7E, 0x7E, 0xFE])
+
+
+def test_e8m0_matches_torch():
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e8m0fnu).double().numpy()
+    got = O.e8m0_values(np.arange(256, dtype=np.uint8))
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(ref))
+    m = ~np.isnan(ref)
+    np.testing.assert_array_equal(got[m], ref[m])
+
+
+def test_bf16_decode_and_round_match_torch():
+    rng = np.random.default_rng(1)
+    v = np.concatenate([rng.standard_normal(50000) * 10.0 ** rng.integers(-30, 30, 50000),
+                        [1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -1.0 - 2 ** -8, 2.0 ** -130,
+                         3 * 2.0 ** -134, 0.0]]).astype(np.float32)
+    ref = torch.from_numpy(v).to(torch.bfloat16)
+    np.testing.assert_array_equal(O.round_to_bf16(v), ref.double().numpy())
+    bits = ref.view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(O.bf16_bits_to_f64(bits), ref.double().numpy())
+    np.testing.assert_array_equal(O.bf16_bits_from_value(ref.double().numpy()), bits)
+
+
+def test_int4_nibbles():
+    got = O.int4_values(np.array([[0x8F, 0x70, 0x12]], np.uint8))
+    np.testing.assert_array_equal(got, [[-1, -8, 0, 7, 2, 1]])
+    allb = np.arange(256, dtype=np.uint8)[None, :]
+    v = O.int4_values(allb).reshape(256, 2)
+    for b in range(256):
+        lo, hi = b & 15, b >> 4
+        assert v[b, 0] == (lo if lo < 8 else lo - 16)
+        assert v[b, 1] == (hi if hi < 8 else hi - 16)
+
+
+# ---------------------------------------------------------------- routing
+
+def _route_brute(L, k):
+    T, E = L.shape
+    ids = np.zeros((T, k), np.int64)
+    w = np.zeros((T, k))
+    for t in range(T):
+        order = sorted(range(E), key=lambda e: (-float(L[t, e]), e))[:k]
+        ids[t] = order
+        ex = [math.exp(float(L[t, e]) - float(L[t, order[0]])) for e in order]
+        w[t] = [v / sum(ex) for v in ex]
+    return ids, w
+
+
+@pytest.mark.parametrize("T,E,k", [(7, 8, 2), (5, 16, 5), (3, 6, 6), (9, 4, 1)])
+def test_route_brute_force(T, E, k):
+    rng = np.random.default_rng(T * 100 + E)
+    L = rng.standard_normal((T, E)).astype(np.float32)
+    L[0, 1] = L[0, 3]  # a tie
+    ids, w = O.route(L, k)
+    ids_b, w_b = _route_brute(L, k)
+    np.testing.assert_array_equal(ids, ids_b)
+    np.testing.assert_allclose(w, w_b, rtol=2 ** -22, atol=0)
+
+
+def test_route_invariants():
+    L = np.random.default_rng(3).standard_normal((500, 64)).astype(np.float32)
+    for k in (1, 2, 8, 64):
+        ids, w = O.route(L, k)
+        assert np.all(np.abs(w.astype(np.float64).sum(1) - 1) <= k * 2.0 ** -23)
+        assert all(len(set(r)) == k for r in ids)
+        if k == 1:
+            assert np.all(w == 1.0)
+        if k == 64:
+            assert np.all(np.sort(ids, 1) == np.arange(64))
+        # descending logits in slot order
+        sel = np.take_along_axis(L, ids.astype(np.int64), 1)
+        assert np.all(np.diff(sel, axis=1) <= 0)
+
+
+def test_route_ties_pick_lower_index():
+    L = np.zeros((2, 6), np.float32)
+    L[1] = [1, 2, 2, 2, 0, 2]
+    ids, w = O.route(L, 3)
+    np.testing.assert_array_equal(ids, [[0, 1, 2], [1, 2, 3]])
+    np.testing.assert_array_equal(w, np.full((2, 3), np.float32(1 / 3)))
+
+
+# ---------------------------------------------------------------- align
+
+def _align_brute(ids, E, bm):
+    flat = list(np.asarray(ids).reshape(-1))
+    P = len(flat)
+    keyed = sorted((int(e), p) for p, e in enumerate(flat) if 0 <= e < E)
+    out, tiles, offs = [], [], [0]
+    for e in range(E):
+        ps = [p for (ee, p) in keyed if ee == e]
+        pad = (len(ps) + bm - 1) // bm * bm
+        out += ps + [P] * (pad - len(ps))
+        tiles += [e] * (pad // bm)
+        offs.append(offs[-1] + pad)
+    return out, tiles, offs
+
+
+@pytest.mark.parametrize("T,k,E,bm", [(16, 2, 8, 4), (33, 3, 7, 16), (1, 1, 1, 32), (20, 4, 64, 8)])
+def test_align_brute_force_and_invariants(T, k, E, bm):
+    rng = np.random.default_rng(T + k + E)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    a = O.align(ids, E, bm)
+    out, tiles, offs = _align_brute(ids, E, bm)
+    np.testing.assert_array_equal(a["sorted_pair_ids"], out)
+    np.testing.assert_array_equal(a["tile_expert"], tiles)
+    np.testing.assert_array_equal(a["expert_offsets"], offs)
+    P = T * k
+    s = a["sorted_pair_ids"]
+    assert sorted(s[s < P].tolist()) == list(range(P))
+    assert np.all(a["expert_offsets"] % bm == 0)
+    counts = np.bincount(ids.reshape(-1), minlength=E)
+    for e in range(E):
+        seg = s[a["expert_offsets"][e]:a["expert_offsets"][e + 1]]
+        assert np.sum(seg < P) == counts[e]
+        assert np.all(np.diff(seg[seg < P]) > 0)
+        assert np.all(seg[counts[e]:] == P)
+
+
+def test_align_drops_out_of_range_ids():
+    ids = np.array([[0, 5], [1, -1]], np.int32)
+    a = O.align(ids, 2, 2)
+    np.testing.assert_array_equal(a["sorted_pair_ids"], [0, 4, 2, 4])
+
+
+# ---------------------------------------------------------------- small layers
+
+def _tiny(scheme, T=24, H=64, I=32, E=4, k=2, seed=7):
+    sh = MoEShape(f"t_{scheme}", scheme, tokens=T, hidden=H, inter=I, experts=E, topk=k,
+                  seed=seed)
+    return sh, synth.make_inputs(sh)
+
+
+def _dense_reference(scheme, inp, e, rows):
+    """Textbook dense FFN of one expert with torch ops, decoding the weights
+    with torch's own format conversions where torch has them."""
+    I = inp["w13"].shape[1] // 2
+    H = inp["w2"].shape[1]
+    if scheme == "w4a16":
+        x = torch.from_numpy(inp["x"][rows].view(np.int16)).view(torch.bfloat16).double()
+
+        def deq(codes, s):
+            b = torch.from_numpy(codes.astype(np.int16))
+            lo = (b & 15) - 16 * ((b & 15) >= 8).to(torch.int16)
+            hi = (b >> 4) - 16 * ((b >> 4) >= 8).to(torch.int16)
+            q = torch.stack([lo, hi], -1).reshape(codes.shape[0], -1).double()
+            return q * torch.from_numpy(s.astype(np.float64)).repeat_interleave(32, 1)
+        W13 = deq(inp["w13"][e], inp["w13_scale"][e])
+        W2 = deq(inp["w2"][e], inp["w2_scale"][e])
+        gu = x @ W13.T
+        h = torch.nn.functional.silu(gu[:, :I]) * gu[:, I:]
+        h = h.float().to(torch.bfloat16).double()
+        return (h @ W2.T).numpy()
+    if scheme == "w8a8":
+        x = torch.from_numpy(inp["x"][rows].astype(np.float64)) * \
+            torch.from_numpy(inp["x_scale"][rows].astype(np.float64))[:, None]
+        W13 = torch.from_numpy(inp["w13"][e].astype(np.float64)) * \
+            torch.from_numpy(inp["w13_scale"][e].astype(np.float64))[:, None]
+        W2 = torch.from_numpy(inp["w2"][e].astype(np.float64)) * \
+            torch.from_numpy(inp["w2_scale"][e].astype(np.float64))[:, None]
+        gu = x @ W13.T
+        h = torch.nn.functional.silu(gu[:, :I]) * gu[:, I:]
+        s = h.abs().amax(1, keepdim=True) / 127
+        hq = torch.clamp(torch.round(h / s), -127, 127) * s
+        return (hq @ W2.T).numpy()
+    # a8w4
+    xt = torch.from_numpy(inp["x"][rows]).view(torch.float8_e4m3fn).double()
+    x = xt * torch.from_numpy(inp["x_scale"][rows].astype(np.float64))[:, None]
+    e2m1 = {c: v for c, v in _read_table("ocp_e2m1_values.txt")}
+
+    def deq(codes, s):
+        lut = np.array([e2m1[c] for c in range(16)])
+        q = np.stack([lut[codes & 15], lut[codes >> 4]], -1).reshape(codes.shape[0], -1)
+        sc = torch.from_numpy(s).view(torch.float8_e8m0fnu).double().repeat_interleave(32, 1)
+        return torch.from_numpy(q) * sc
+    W13 = deq(inp["w13"][e], inp["w13_scale"][e])
+    W2 = deq(inp["w2"][e], inp["w2_scale"][e])
+    gu = x @ W13.T
+    h = torch.nn.functional.silu(gu[:, :I]) * gu[:, I:]
+    s = h.abs().amax(1, keepdim=True) / 448
+    hq = (h / s).float().to(torch.float8_e4m3fn).double() * s
+    return (hq @ W2.T).numpy()
+
+
+@pytest.mark.parametrize("scheme,tol", [("w4a16", 1e-9), ("w8a8", 1e-5), ("a8w4", 1e-4)])
+def test_one_expert_top1_is_dense_ffn(scheme, tol):
+    """E = 1, k = 1: the MoE layer is one dense FFN and every weight is 1."""
+    sh, inp = _tiny(scheme, T=40, H=128, I=64, E=1, k=1)
+    ids, w = O.route(inp["logits"], 1)
+    assert np.all(ids == 0) and np.all(w == 1.0)
+    r = O.moe_forward(scheme, inp["x"], inp["x_scale"], {k: inp[k] for k in
+                      ("w13", "w13_scale", "w2", "w2_scale")}, ids, w)
+    got = r["out32"] if scheme == "w8a8" else r["out"]
+    ref = _dense_reference(scheme, inp, 0, np.arange(40))
+    assert O.rel_l2(got, ref) < tol
+
+
+@pytest.mark.parametrize("scheme", ["w4a16", "w8a8", "a8w4"])
+def test_brute_force_every_expert_then_select(scheme):
+    """Run every expert on every token densely, then pick each token's k
+    outputs and weight them: must equal the grouped oracle."""
+    sh, inp = _tiny(scheme, T=20, H=64, I=32, E=5, k=3)
+    ids, w = O.route(inp["logits"], 3)
+    W = {k: inp[k] for k in ("w13", "w13_scale", "w2", "w2_scale")}
+    r = O.moe_forward(scheme, inp["x"], inp["x_scale"], W, ids, w)
+    allY = []
+    for e in range(5):
+        allY.append(O.expert_ffn(scheme, inp["x"], inp["x_scale"],
+                                 {k: v[e] for k, v in W.items()})["y"])
+    allY = np.stack(allY)  # [E, T, H]
+    T, k = ids.shape
+    if scheme == "w8a8":
+        acc = np.zeros((T, 64), np.float32)
+        for j in range(k):
+            yj = allY[ids[:, j], np.arange(T)].astype(np.float32)
+            acc = (acc + (w[:, j:j + 1] * yj).astype(np.float32)).astype(np.float32)
+        np.testing.assert_array_equal(r["out32"], acc)
+    else:
+        ref = sum(w[:, j:j + 1].astype(np.float64) * allY[ids[:, j], np.arange(T)]
+                  for j in range(k))
+        np.testing.assert_allclose(r["out"], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_w8a8_accumulators_exact_against_python_ints():
+    sh, inp = _tiny("w8a8", T=6, H=96, I=32, E=2, k=1)
+    ids, w = O.route(inp["logits"], 1)
+    W = {k: inp[k] for k in ("w13", "w13_scale", "w2", "w2_scale")}
+    r = O.moe_forward("w8a8", inp["x"], inp["x_scale"], W, ids, w, keep=("acc1", "acc2", "hq"))
+    for p in range(6):
+        e = int(ids[p, 0])
+        for n in (0, 5, 63):
+            ref = sum(int(a) * int(b) for a, b in zip(inp["x"][p], inp["w13"][e, n]))
+            assert r["acc1"][p, n] == ref
+        for n in (0, 17, 95):
+            ref = sum(int(a) * int(b) for a, b in zip(r["hq"][p], inp["w2"][e, n]))
+            assert r["acc2"][p, n] == ref
+
+
+def test_a8w4_accumulators_exact_against_rationals():
+    sh, inp = _tiny("a8w4", T=3, H=128, I=32, E=2, k=1)
+    ids, w = O.route(inp["logits"], 1)
+    W = {k: inp[k] for k in ("w13", "w13_scale", "w2", "w2_scale")}
+    r = O.moe_forward("a8w4", inp["x"], inp["x_scale"], W, ids, w, keep=("acc1",))
+    e2m1 = {c: Fraction(v) for c, v in _read_table("ocp_e2m1_values.txt")}
+    for p in range(3):
+        e = int(ids[p, 0])
+        xs = torch.from_numpy(inp["x"][p]).view(torch.float8_e4m3fn).double().numpy()
+        for n in (0, 33):
+            codes = inp["w13"][e, n]
+            q = [v for c in codes for v in (e2m1[c & 15], e2m1[c >> 4])]
+            sc = [Fraction(2) ** (int(b) - 127) for b in inp["w13_scale"][e, n]]
+            ref = sum(Fraction(float(xs[c])) * q[c] * sc[c // 32] for c in range(128))
+            assert Fraction(float(r["acc1"][p, n])) == ref
+
+
+def test_requant_rows_golden():
+    for line in open(os.path.join(GOLDEN, "w8a8_requant_rows.txt")):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        hs, ss, cs = [part.split() for part in line.split("|")]
+        h = np.array([[float(v) for v in hs]], np.float32)
+        q, s = O.quant_rows_int8(h)
+        assert abs(float(s[0]) - float(ss[0])) <= 1e-7 * max(1.0, float(ss[0]))
+        np.testing.assert_array_equal(q[0], [int(v) for v in cs])
+
+
+def test_requant_e4m3_row_max_maps_to_448():
+    h = np.array([[3.0, -1.5, 0.75, 0.0], [0, 0, 0, 0]], np.float32)
+    q, s = O.quant_rows_e4m3(h)
+    assert s[0] == np.float32(3.0 / 448) and s[1] == 1.0
+    np.testing.assert_array_equal(O.e4m3_values(q[0][:1]), [448.0])
+    assert np.all(q[1] == 0)
+
+
+def test_silu_closed_forms():
+    gu = np.array([[0.0, 100.0, -100.0, 2.0, 1.0, 1.0, 1.0, 3.0]], np.float32)
+    h = O.silu_mul_f32(gu, 4)
+    assert h[0, 0] == 0.0
+    assert h[0, 1] == 100.0
+    assert h[0, 2] == 0.0
+    np.testing.assert_allclose(h[0, 3], 3.0 * 2.0 / (1.0 + math.exp(-2.0)), rtol=1e-6)
+
+
+def test_combine_weights_sum_to_one_reproduces_common_y():
+    """If every slot of a token returns the same y, the combine returns
+    y times the weight sum, which is 1 within k ulps."""
+    rng = np.random.default_rng(0)
+    T, k, H = 5, 4, 8
+    _, w = O.route(rng.standard_normal((T, 16)).astype(np.float32), k)
+    y = np.repeat(rng.standard_normal((T, 1, H)), k, 1).reshape(T * k, H)
+    out = O.combine("w4a16", y, w)["out"]
+    np.testing.assert_allclose(out, y.reshape(T, k, H)[:, 0], rtol=k * 2.0 ** -23)
+
+
+def test_generator_shapes_and_reproducible():
+    a = synth.make_inputs(W4A16_TINY)
+    b = synth.make_inputs(W4A16_TINY)
+    for key in a:
+        if a[key] is not None:
+            np.testing.assert_array_equal(a[key], b[key])
+    assert a["w13"].shape == (8, 256, 128) and a["w13_scale"].shape == (8, 256, 8)
+    assert a["w2"].shape == (8, 256, 64) and a["w2_scale"].shape == (8, 256, 4)
+    e3 = synth.expert_weights(W4A16_TINY, 3)
+    np.testing.assert_array_equal(e3["w2"], a["w2"][3])
