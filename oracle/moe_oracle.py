@@ -165,7 +165,10 @@ def route(logits: np.ndarray, k: int):
     ids = order[:, :k].astype(np.int32)
     sel = np.take_along_axis(L, ids.astype(np.int64), axis=1).astype(f64)
     ex = np.exp(sel - sel[:, :1])
-    w = (ex / ex.sum(axis=1, keepdims=True)).astype(np.float32)
+    den = np.zeros(T, f64)
+    for j in range(k):  # denominator summed in slot order
+        den = den + ex[:, j]
+    w = (ex / den[:, None]).astype(np.float32)
     return ids, w
 
 
