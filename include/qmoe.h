@@ -1,0 +1,184 @@
+/*
+ * qmoe.h -- C ABI of the grouped, weight-quantized Mixture-of-Experts FFN
+ * for MI355X (gfx950).
+ *
+ * The layer: every token t picks k experts from its router logits; for each
+ * (token, slot) pair p = t*k + j routed to expert e
+ *     gu = x[t] . W13[e]^T          (W13 rows 0..I-1 = gate, I..2I-1 = up)
+ *     h  = silu(gate) * up,  silu(g) = g / (1 + exp(-g))
+ *     y[p] = h . W2[e]^T
+ * and out[t] = sum_j w[t, j] * y[t*k + j] in slot order.
+ *
+ * Sources: hip-ep PR "perf(qmoe): group prefill expert matmuls" (description:
+ * symmetric int4 expert projections batched into one launch per projection,
+ * deterministic scatter order); vLLM issue "Evaluate native IU4/IU8 WMMA for
+ * grouped-INT MoE prefill on gfx1151" (Problem: top-k routing, dequantise
+ * then bf16 dot; Constraint: integer matrix products need an activation-
+ * quantised scheme such as W8A8-int8); aiter PR 6090 (Changes: fp8
+ * activations x MXFP4 weights, model_dim 4096, 512 experts, topk 10; Test
+ * Plan: stage1 then stage2 tiles, K tiles no larger than inter_dim).  The
+ * activation function, the routing tie rule and the combine order are not
+ * spelled out on those pages; this library fixes them as stated above.
+ *
+ * Conventions for every call:
+ *  - Every pointer argument is device memory owned by the caller.  The
+ *    library never allocates, frees or keeps a pointer after it returns.
+ *  - Every call is enqueued on `stream` (a hipStream_t; NULL = the null
+ *    stream) and returns without waiting for the GPU, except
+ *    qmoe_check_flags, which synchronises the stream.
+ *  - Arguments are validated on the host before anything is launched; on an
+ *    error nothing is enqueued and the status says why.  No C++ exception
+ *    crosses this interface.  T = 0 is valid: qmoe_align still writes its
+ *    (empty) outputs, the other calls enqueue nothing.
+ *  - Layouts are row-major with K contiguous.  int4 and e2m1 values are
+ *    packed two per byte, the even K index in the low nibble.
+ */
+#ifndef QMOE_H_
+#define QMOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QMOE_ABI_VERSION 1
+
+typedef enum {
+  QMOE_OK = 0,
+  QMOE_ERR_INVALID_ARG = 1, /* null pointer, bad size, workspace too small */
+  QMOE_ERR_UNSUPPORTED = 2, /* valid, but no kernel built for this shape   */
+  QMOE_ERR_HIP = 3          /* the HIP runtime reported an error           */
+} qmoe_status;
+
+/* Weight / activation schemes.
+ * W4A16_G32:  x bf16 [T,H]; W int4 two's complement, one fp16 scale per 32
+ *             values along K: scale [E,N,K/32].  Intermediate h is bf16.
+ * W8A8_PERCHAN: x int8 [T,H] + fp32 per-token scale [T]; W int8 with one
+ *             fp32 scale per output channel [E,N]; int32 accumulation.  h is
+ *             requantized per row to int8 with an fp32 scale.
+ * A8W4_MXFP4: x OCP fp8 e4m3 [T,H] + fp32 per-token scale [T]; W e2m1 with
+ *             one e8m0 scale byte per 32 along K [E,N,K/32].  h is
+ *             requantized per row to e4m3 with an fp32 scale.            */
+typedef enum {
+  QMOE_W4A16_G32 = 0,
+  QMOE_W8A8_PERCHAN = 1,
+  QMOE_A8W4_MXFP4 = 2
+} qmoe_scheme;
+
+typedef enum { QMOE_DT_BF16 = 0, QMOE_DT_F32 = 1 } qmoe_dtype;
+
+/* Debug flag for qmoe_grouped_ffn (W8A8 only): also write the int32
+ * accumulators of both projections into the workspace (see
+ * qmoe_grouped_ffn_debug_offsets).                                       */
+#define QMOE_FLAG_DUMP_ACC 1u
+
+typedef struct {
+  int32_t scheme;   /* qmoe_scheme                                        */
+  int32_t T;        /* tokens                                             */
+  int32_t H;        /* hidden size (K of stage 1, N of stage 2)           */
+  int32_t I;        /* expert intermediate size                           */
+  int32_t E;        /* number of experts                                  */
+  int32_t k;        /* experts per token                                  */
+  int32_t block_m;  /* rows per tile; must equal the one given qmoe_align */
+  uint32_t flags;   /* QMOE_FLAG_*                                        */
+} qmoe_ffn_desc;
+
+/* Per-expert weights, stacked over experts (device pointers).
+ * w13 [E, 2I, H] codes, w13_scale as the scheme says; w2 [E, H, I] codes,
+ * w2_scale likewise.                                                     */
+typedef struct {
+  const void* w13;
+  const void* w13_scale;
+  const void* w2;
+  const void* w2_scale;
+} qmoe_weights;
+
+int qmoe_abi_version(void);
+const char* qmoe_status_str(qmoe_status s);
+/* Raw hipError_t of the last QMOE_ERR_HIP on the calling thread.          */
+int qmoe_last_hip_error(void);
+
+/* ---------------------------------------------------------------------
+ * qmoe_route -- top-k routing from router logits.
+ * Softmax over fp32 logits [T,E], the k largest logits per token (ties go
+ * to the lower expert index) in descending order, weights renormalised
+ * over the k picked: w[t,j] = exp(L[e_j]-L[e_0]) / sum_i exp(L[e_i]-L[e_0]),
+ * evaluated in fp64 and stored as fp32.  (vLLM issue, section Problem:
+ * top-k routing; aiter PR 6090, section Changes: topk 10.)
+ * Out: topk_ids int32 [T,k], topk_w fp32 [T,k].  Requires 1 <= k <= E,
+ * k <= 16 and E <= 1024; logits must be finite.                          */
+qmoe_status qmoe_route(const float* logits, int32_t T, int32_t E, int32_t k,
+                       int32_t* topk_ids, float* topk_w, void* stream);
+
+/* ---------------------------------------------------------------------
+ * qmoe_align -- group the P = T*k (token, slot) pairs by expert.
+ * sorted_pair_ids[cap]: for experts e = 0..E-1 in order, the pair ids
+ *   p = t*k+j with topk_ids[t,j] == e in ascending order, then the sentinel
+ *   P until the expert's segment is a multiple of block_m; experts with no
+ *   pair get no segment.  Entries from num_padded to cap also hold P.
+ * tile_expert[cap/block_m]: expert of each block_m-row tile, -1 past
+ *   num_padded.
+ * expert_offsets[E+1]: start of each expert's segment; [E] = num_padded.
+ * num_padded[1]: total padded rows.
+ * cap = qmoe_align_capacity(T,k,E,block_m) entries must be allocated.
+ * A token's k ids must be distinct.  Ids outside [0,E) are dropped and set
+ * bit 0 of the flag word in `ws`; an id repeated within a token sets bit 1
+ * (one of its pairs is then lost).  Read the word with qmoe_check_flags.
+ * block_m is 16, 32, 64 or 128; E <= 1024.
+ * This is the batching of every expert's rows into one launch per
+ * projection (hip-ep PR, description) with a fixed, stable order.        */
+size_t qmoe_align_capacity(int32_t T, int32_t k, int32_t E, int32_t block_m);
+size_t qmoe_align_workspace(int32_t T, int32_t k, int32_t E);
+qmoe_status qmoe_align(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
+                       int32_t block_m, int32_t* sorted_pair_ids, int32_t* tile_expert,
+                       int32_t* expert_offsets, int32_t* num_padded, void* ws,
+                       size_t ws_bytes, void* stream);
+/* Copies the align flag word to host memory *flags_out (synchronises).  */
+qmoe_status qmoe_check_flags(const void* align_ws, int32_t* flags_out, void* stream);
+
+/* ---------------------------------------------------------------------
+ * qmoe_grouped_ffn -- stage 1 (gate/up projection of every expert in one
+ * launch, fused silu(gate)*up epilogue), the scheme's requantization of h,
+ * stage 2 (down projection of every expert in one launch).  aiter PR 6090,
+ * Test Plan: stage1 and stage2 tiles; vLLM issue, sections Problem and
+ * Constraint: dequantise-then-bf16-dot for W4A16, integer products for
+ * W8A8.
+ * x: see qmoe_scheme; x_scale fp32 [T] (NULL for W4A16).
+ * sorted_pair_ids / tile_expert / num_padded: qmoe_align's outputs for the
+ *   same T, k, E and block_m.
+ * y_pairs: [T*k, H], row p = pair p, unweighted expert output; bf16 for
+ *   W4A16 and A8W4, fp32 for W8A8.
+ * ws: workspace of at least qmoe_grouped_ffn_workspace(d) bytes, 256-byte
+ *   aligned.
+ * Requirements: H % 256 == 0, I % 128 == 0 (I % 256 for A8W4), k <= E.
+ * Errors: QMOE_ERR_INVALID_ARG for null pointers, bad sizes or a short
+ * workspace; QMOE_ERR_UNSUPPORTED for sizes outside the requirements.    */
+size_t qmoe_grouped_ffn_workspace(const qmoe_ffn_desc* d);
+/* Byte offsets inside ws of the int32 debug dumps written with
+ * QMOE_FLAG_DUMP_ACC: acc1 [cap, 2I] and acc2 [cap, H], row = sorted slot.
+ * Returns QMOE_ERR_INVALID_ARG unless the scheme is W8A8.               */
+qmoe_status qmoe_grouped_ffn_debug_offsets(const qmoe_ffn_desc* d, size_t* acc1_off,
+                                           size_t* acc2_off);
+qmoe_status qmoe_grouped_ffn(const qmoe_ffn_desc* d, const void* x, const float* x_scale,
+                             const qmoe_weights* w, const int32_t* sorted_pair_ids,
+                             const int32_t* tile_expert, const int32_t* num_padded,
+                             void* y_pairs, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------
+ * qmoe_combine -- out[t,:] = sum_{j=0}^{k-1} topk_w[t,j] * y_pairs[t*k+j,:]
+ * accumulated in fp32 in slot order j = 0..k-1 (acc = acc + w*y, no fused
+ * multiply-add), one thread per output element group, no atomics, so the
+ * result is bitwise reproducible (hip-ep PR, description: deterministic
+ * scatter order).  y_pairs dtype: QMOE_DT_BF16 or QMOE_DT_F32.
+ * out_bf16 [T,H] (round to nearest even) and/or out_f32 [T,H]; at least
+ * one must be non-NULL.  Requires H % 8 == 0.                            */
+qmoe_status qmoe_combine(const void* y_pairs, int32_t y_dtype, const float* topk_w,
+                         int32_t T, int32_t k, int32_t H, uint16_t* out_bf16,
+                         float* out_f32, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QMOE_H_ */

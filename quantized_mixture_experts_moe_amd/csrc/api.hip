@@ -1,0 +1,272 @@
+// Host side of the C ABI declared in include/qmoe.h: argument validation,
+// workspace layout and kernel dispatch.  Nothing here allocates device
+// memory or synchronises, except qmoe_check_flags.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <mutex>
+
+#include "../../include/qmoe.h"
+#include "qmoe_internal.h"
+
+namespace qmoe {
+
+static thread_local int g_last_hip_error = 0;
+
+static qmoe_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return QMOE_OK;
+  g_last_hip_error = (int)e;
+  return QMOE_ERR_HIP;
+}
+
+int device_cu_count() {
+  static std::mutex mu;
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+      n = 1;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+static bool valid_block_m(int bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128; }
+
+// Layout of qmoe_align's workspace: flag word, per-chunk flags, counts.
+struct AlignWs {
+  size_t flags, chunk_flags, counts, total;
+};
+static AlignWs align_ws_layout(int T, int E) {
+  AlignWs w;
+  const size_t nch = align_chunk_count(T);
+  w.flags = 0;
+  w.chunk_flags = 256;
+  w.counts = align_up(w.chunk_flags + nch * 4, 256);
+  w.total = align_up(w.counts + nch * (size_t)E * 4, 256);
+  return w;
+}
+
+// Layout of qmoe_grouped_ffn's workspace.
+struct FfnWs {
+  size_t h, hq, hs, pmax, acc1, acc2, total;
+};
+static FfnWs ffn_ws_layout(const qmoe_ffn_desc& d) {
+  const size_t cap = qmoe_align_capacity(d.T, d.k, d.E, d.block_m);
+  const size_t I = d.I, H = d.H;
+  FfnWs w{};
+  size_t off = 0;
+  w.h = off;
+  off = align_up(off + cap * I * (d.scheme == QMOE_W4A16_G32 ? 2 : 4), 256);
+  if (d.scheme != QMOE_W4A16_G32) {
+    w.hq = off;
+    off = align_up(off + cap * I, 256);
+    w.hs = off;
+    off = align_up(off + cap * 4, 256);
+    w.pmax = off;
+    off = align_up(off + cap * (I / kStage1Cols) * 4, 256);
+  }
+  if (d.scheme == QMOE_W8A8_PERCHAN && (d.flags & QMOE_FLAG_DUMP_ACC)) {
+    w.acc1 = off;
+    off = align_up(off + cap * 2 * I * 4, 256);
+    w.acc2 = off;
+    off = align_up(off + cap * H * 4, 256);
+  }
+  w.total = std::max<size_t>(off, 256);
+  return w;
+}
+
+static qmoe_status check_desc(const qmoe_ffn_desc* d) {
+  if (d == nullptr) return QMOE_ERR_INVALID_ARG;
+  if (d->scheme < 0 || d->scheme > 2) return QMOE_ERR_INVALID_ARG;
+  if (d->T < 0 || d->H <= 0 || d->I <= 0 || d->E <= 0 || d->k < 1 || d->k > d->E)
+    return QMOE_ERR_INVALID_ARG;
+  if (d->H % 32 != 0 || d->I % 32 != 0) return QMOE_ERR_INVALID_ARG;
+  if (!valid_block_m(d->block_m)) return QMOE_ERR_INVALID_ARG;
+  if ((long long)d->T * d->k > (1ll << 30)) return QMOE_ERR_INVALID_ARG;
+  if (d->flags & ~QMOE_FLAG_DUMP_ACC) return QMOE_ERR_INVALID_ARG;
+  if (d->E > 1024) return QMOE_ERR_UNSUPPORTED;
+  if (d->H % 256 != 0) return QMOE_ERR_UNSUPPORTED;
+  if (d->I % (d->scheme == QMOE_A8W4_MXFP4 ? 256 : 128) != 0) return QMOE_ERR_UNSUPPORTED;
+  return QMOE_OK;
+}
+
+}  // namespace qmoe
+
+using namespace qmoe;
+
+extern "C" {
+
+int qmoe_abi_version(void) { return QMOE_ABI_VERSION; }
+
+const char* qmoe_status_str(qmoe_status s) {
+  switch (s) {
+    case QMOE_OK: return "ok";
+    case QMOE_ERR_INVALID_ARG: return "invalid argument";
+    case QMOE_ERR_UNSUPPORTED: return "unsupported shape or scheme";
+    case QMOE_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int qmoe_last_hip_error(void) { return g_last_hip_error; }
+
+qmoe_status qmoe_route(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* topk_ids,
+                       float* topk_w, void* stream) {
+  if (T < 0 || E < 1 || k < 1 || k > E || k > 16) return QMOE_ERR_INVALID_ARG;
+  if (E > 1024) return QMOE_ERR_UNSUPPORTED;
+  if (T == 0) return QMOE_OK;
+  if (!logits || !topk_ids || !topk_w) return QMOE_ERR_INVALID_ARG;
+  return hip_status(launch_route(logits, T, E, k, topk_ids, topk_w, (hipStream_t)stream));
+}
+
+size_t qmoe_align_capacity(int32_t T, int32_t k, int32_t E, int32_t block_m) {
+  if (T < 0 || k < 1 || E < 1 || !valid_block_m(block_m)) return 0;
+  const size_t P = (size_t)T * k;
+  const size_t cap = P + std::min<size_t>((size_t)E, P) * (size_t)(block_m - 1);
+  return align_up(std::max<size_t>(cap, 1), (size_t)block_m);
+}
+
+size_t qmoe_align_workspace(int32_t T, int32_t k, int32_t E) {
+  (void)k;
+  if (T < 0 || E < 1) return 0;
+  return align_ws_layout(T, E).total;
+}
+
+qmoe_status qmoe_align(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_t block_m,
+                       int32_t* sorted_pair_ids, int32_t* tile_expert, int32_t* expert_offsets,
+                       int32_t* num_padded, void* ws, size_t ws_bytes, void* stream) {
+  if (T < 0 || k < 1 || E < 1 || k > E || !valid_block_m(block_m)) return QMOE_ERR_INVALID_ARG;
+  if ((long long)T * k > (1ll << 30)) return QMOE_ERR_INVALID_ARG;
+  if (E > 1024) return QMOE_ERR_UNSUPPORTED;
+  if (!topk_ids || !sorted_pair_ids || !tile_expert || !expert_offsets || !num_padded || !ws)
+    return QMOE_ERR_INVALID_ARG;
+  const AlignWs lay = align_ws_layout(T, E);
+  if (ws_bytes < lay.total || !aligned(ws, 256)) return QMOE_ERR_INVALID_ARG;
+  const int cap = (int)qmoe_align_capacity(T, k, E, block_m);
+  uint8_t* w = reinterpret_cast<uint8_t*>(ws);
+  return hip_status(launch_align(topk_ids, T, k, E, block_m, sorted_pair_ids, tile_expert,
+                                 expert_offsets, num_padded,
+                                 reinterpret_cast<int32_t*>(w + lay.counts),
+                                 reinterpret_cast<int32_t*>(w + lay.chunk_flags),
+                                 reinterpret_cast<int32_t*>(w + lay.flags), cap,
+                                 (hipStream_t)stream));
+}
+
+qmoe_status qmoe_check_flags(const void* align_ws, int32_t* flags_out, void* stream) {
+  if (!align_ws || !flags_out) return QMOE_ERR_INVALID_ARG;
+  int32_t v = 0;
+  hipError_t e = hipMemcpyAsync(&v, align_ws, sizeof(int32_t), hipMemcpyDeviceToHost,
+                                (hipStream_t)stream);
+  if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return hip_status(e);
+  *flags_out = v;
+  return QMOE_OK;
+}
+
+size_t qmoe_grouped_ffn_workspace(const qmoe_ffn_desc* d) {
+  if (check_desc(d) != QMOE_OK) return 0;
+  return ffn_ws_layout(*d).total;
+}
+
+qmoe_status qmoe_grouped_ffn_debug_offsets(const qmoe_ffn_desc* d, size_t* acc1_off,
+                                           size_t* acc2_off) {
+  const qmoe_status st = check_desc(d);
+  if (st != QMOE_OK) return st;
+  if (d->scheme != QMOE_W8A8_PERCHAN || !(d->flags & QMOE_FLAG_DUMP_ACC) || !acc1_off ||
+      !acc2_off)
+    return QMOE_ERR_INVALID_ARG;
+  const FfnWs lay = ffn_ws_layout(*d);
+  *acc1_off = lay.acc1;
+  *acc2_off = lay.acc2;
+  return QMOE_OK;
+}
+
+qmoe_status qmoe_grouped_ffn(const qmoe_ffn_desc* d, const void* x, const float* x_scale,
+                             const qmoe_weights* w, const int32_t* sorted_pair_ids,
+                             const int32_t* tile_expert, const int32_t* num_padded, void* y_pairs,
+                             void* ws, size_t ws_bytes, void* stream) {
+  const qmoe_status st = check_desc(d);
+  if (st != QMOE_OK) return st;
+  if (d->T == 0) return QMOE_OK;
+  const bool quant_act = d->scheme != QMOE_W4A16_G32;
+  if (!x || !w || !w->w13 || !w->w13_scale || !w->w2 || !w->w2_scale || !sorted_pair_ids ||
+      !tile_expert || !num_padded || !y_pairs || !ws || (quant_act && !x_scale))
+    return QMOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(w->w13, 16) || !aligned(w->w2, 16) || !aligned(ws, 256) ||
+      !aligned(y_pairs, 16) || !aligned(w->w13_scale, 4) || !aligned(w->w2_scale, 4))
+    return QMOE_ERR_INVALID_ARG;
+  const FfnWs lay = ffn_ws_layout(*d);
+  if (ws_bytes < lay.total) return QMOE_ERR_INVALID_ARG;
+  uint8_t* wsb = reinterpret_cast<uint8_t*>(ws);
+  const bool dump = d->scheme == QMOE_W8A8_PERCHAN && (d->flags & QMOE_FLAG_DUMP_ACC);
+  const int cap = (int)qmoe_align_capacity(d->T, d->k, d->E, d->block_m);
+  hipStream_t s = (hipStream_t)stream;
+
+  GemmArgs g1{};
+  g1.T = d->T;
+  g1.H = d->H;
+  g1.I = d->I;
+  g1.E = d->E;
+  g1.k = d->k;
+  g1.P = d->T * d->k;
+  g1.sorted_pair_ids = sorted_pair_ids;
+  g1.tile_expert = tile_expert;
+  g1.num_padded = num_padded;
+  GemmArgs g2 = g1;
+
+  g1.N = 2 * d->I;
+  g1.K = d->H;
+  g1.ntiles_n = d->I / kStage1Cols;
+  g1.a = x;
+  g1.a_scale = x_scale;
+  g1.b = w->w13;
+  g1.b_scale = w->w13_scale;
+  g1.out = wsb + lay.h;
+  g1.row_pmax = quant_act ? reinterpret_cast<float*>(wsb + lay.pmax) : nullptr;
+  g1.dump = dump ? reinterpret_cast<int32_t*>(wsb + lay.acc1) : nullptr;
+  hipError_t e = launch_gemm(d->scheme, 1, d->block_m, g1, s);
+  if (e != hipSuccess) return hip_status(e);
+
+  if (quant_act) {
+    e = launch_requant(d->scheme, sorted_pair_ids, num_padded, g1.P, d->I, g1.ntiles_n, cap,
+                       reinterpret_cast<const float*>(wsb + lay.h),
+                       reinterpret_cast<const float*>(wsb + lay.pmax), wsb + lay.hq,
+                       reinterpret_cast<float*>(wsb + lay.hs), s);
+    if (e != hipSuccess) return hip_status(e);
+  }
+
+  g2.N = d->H;
+  g2.K = d->I;
+  g2.ntiles_n = d->H / kStage2Cols;
+  g2.a = quant_act ? (const void*)(wsb + lay.hq) : (const void*)(wsb + lay.h);
+  g2.a_scale = quant_act ? reinterpret_cast<const float*>(wsb + lay.hs) : nullptr;
+  g2.b = w->w2;
+  g2.b_scale = w->w2_scale;
+  g2.out = y_pairs;
+  g2.row_pmax = nullptr;
+  g2.dump = dump ? reinterpret_cast<int32_t*>(wsb + lay.acc2) : nullptr;
+  e = launch_gemm(d->scheme, 2, d->block_m, g2, s);
+  return hip_status(e);
+}
+
+qmoe_status qmoe_combine(const void* y_pairs, int32_t y_dtype, const float* topk_w, int32_t T,
+                         int32_t k, int32_t H, uint16_t* out_bf16, float* out_f32, void* stream) {
+  if (T < 0 || k < 1 || H <= 0 || H % 8 != 0) return QMOE_ERR_INVALID_ARG;
+  if (y_dtype != QMOE_DT_BF16 && y_dtype != QMOE_DT_F32) return QMOE_ERR_INVALID_ARG;
+  if (!out_bf16 && !out_f32) return QMOE_ERR_INVALID_ARG;
+  if (T == 0) return QMOE_OK;
+  if (!y_pairs || !topk_w) return QMOE_ERR_INVALID_ARG;
+  if (!aligned(y_pairs, 16) || (out_bf16 && !aligned(out_bf16, 16)) ||
+      (out_f32 && !aligned(out_f32, 16)))
+    return QMOE_ERR_INVALID_ARG;
+  return hip_status(launch_combine(y_pairs, y_dtype == QMOE_DT_F32, topk_w, T, k, H, out_bf16,
+                                   out_f32, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,428 @@
+// Grouped expert GEMMs: one launch per projection covers every expert (hip-ep
+// PR "perf(qmoe): group prefill expert matmuls", description: expert
+// projections batched into single launches instead of one per expert).
+//
+//   stage 1: gu = x[token(row)] . W13[e]^T, fused h = silu(gate) * up
+//   stage 2: y_pairs[pair(row)] = h[row] . W2[e]^T
+// (aiter PR 6090, Test Plan: stage1 tiles, then stage2 tiles.)
+//
+// Rows are the expert-sorted, block_m-padded pair slots from moe_align; a
+// row tile never straddles two experts.  One workgroup = 4 waves; each wave
+// owns two 16-column weight sub-tiles (stage 1: the gate column and the up
+// column of the same h column, so silu(gate)*up is formed in registers) and
+// all BM rows.  Weight fragments stream from HBM straight into VGPRs, each
+// weight byte read by exactly one wave; the gathered activation rows are
+// staged once per step in LDS and shared by the 4 waves.  16-row groups past
+// the tile's last real row are skipped.
+//
+// Matrix cores (CDNA4 MFMA), 16x16 output per instruction:
+//   w4a16: v_mfma_f32_16x16x32_bf16, int4 * fp16 group scale rounded to
+//          bf16 in registers (the "dequantise then bf16 dot" lowering of the
+//          vLLM issue "Evaluate native IU4/IU8 WMMA for grouped-INT MoE
+//          prefill on gfx1151", section Constraint);
+//   w8a8:  v_mfma_i32_16x16x64_i8, exact int32 accumulation (same issue,
+//          section Constraint: integer products need int8 activations);
+//   a8w4:  v_mfma_scale_f32_16x16x128_f8f6f4, A = fp8 e4m3, B = fp4 e2m1
+//          with the e8m0 block scale fed per lane (aiter PR 6090, section
+//          Changes: fp8 act, MXFP4 weight).
+//
+// Per-lane fragment layout of a 16x16xK MFMA (lane = 16*q + r): A row r and
+// B column r hold a contiguous quarter q of the instruction's K.  A step
+// loads, per lane, a contiguous run of each weight row; the K order inside
+// a step is permuted identically for A and B, which leaves the dot product
+// unchanged, and every 32-wide scale block stays inside one lane.
+//
+// Schedule: a persistent grid (a multiple of 8 blocks, one slice of the work
+// list per XCD); work item = (row tile, column tile), row tile major, so the
+// blocks of one XCD share the same gathered activation rows in their L2.
+#include <hip/hip_fp16.h>
+
+#include "qmoe_internal.h"
+
+namespace qmoe {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+enum { kW4A16 = 0, kW8A8 = 1, kA8W4 = 2 };
+
+template <int S>
+struct Tr;
+template <>
+struct Tr<kW4A16> {
+  static constexpr int BK = 128;      // K elements per pipeline step
+  static constexpr int A_ELEM = 2;    // bytes per activation element (bf16)
+  static constexpr int A_STEP = 256;  // activation bytes per row per step
+  static constexpr int A_FRAG = 64;   // activation bytes per lane per 16-row group per step
+  static constexpr int B_STEP = 64;   // weight bytes per row per step (int4)
+  static constexpr int B_FRAG = 16;   // weight bytes per lane per sub-tile per step
+  static constexpr int KB_NUM = 1, KB_DEN = 2;  // weight bytes per K element
+  typedef f32x4 Acc;
+};
+template <>
+struct Tr<kW8A8> {
+  static constexpr int BK = 128;
+  static constexpr int A_ELEM = 1;
+  static constexpr int A_STEP = 128;
+  static constexpr int A_FRAG = 32;
+  static constexpr int B_STEP = 128;
+  static constexpr int B_FRAG = 32;
+  static constexpr int KB_NUM = 1, KB_DEN = 1;
+  typedef i32x4 Acc;
+};
+template <>
+struct Tr<kA8W4> {
+  static constexpr int BK = 256;
+  static constexpr int A_ELEM = 1;
+  static constexpr int A_STEP = 256;
+  static constexpr int A_FRAG = 64;
+  static constexpr int B_STEP = 128;
+  static constexpr int B_FRAG = 32;
+  static constexpr int KB_NUM = 1, KB_DEN = 2;
+  typedef f32x4 Acc;
+};
+
+// Weight fragment of one 16-column sub-tile for one step.
+template <int S>
+struct BFrag {
+  uint4 q[Tr<S>::B_FRAG / 16];
+  uint32_t sc;  // w4a16: fp16 group scale bits; a8w4: two e8m0 bytes; w8a8: unused
+};
+
+__device__ inline bf16x8 dequant8_bf16(uint32_t v, float sc) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const int q = __builtin_amdgcn_sbfe((int)v, 4 * i, 4);  // two's-complement nibble
+    r[i] = (__bf16)((float)q * sc);                          // exact product, one RNE rounding
+  }
+  return r;
+}
+
+template <int S>
+__device__ inline void mfma_step(typename Tr<S>::Acc& acc, const uint4* a, const BFrag<S>& b) {
+  if constexpr (S == kW4A16) {
+    const float sc = __half2float(__ushort_as_half((unsigned short)b.sc));
+    const uint32_t w[4] = {b.q[0].x, b.q[0].y, b.q[0].z, b.q[0].w};
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const bf16x8 av = __builtin_bit_cast(bf16x8, a[j]);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, dequant8_bf16(w[j], sc), acc, 0, 0, 0);
+    }
+  } else if constexpr (S == kW8A8) {
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, a[j]),
+                                                 __builtin_bit_cast(i32x4, b.q[j]), acc, 0, 0, 0);
+    }
+  } else {
+    // A fp8 (format 0) with unit scale 2^0 (e8m0 127); B fp4 (format 4) with
+    // the e8m0 byte of its 32-wide block: byte 0 for the first 32 K of the
+    // lane's run, byte 1 for the second.
+    const i32x8 a0 = {(int)a[0].x, (int)a[0].y, (int)a[0].z, (int)a[0].w,
+                      (int)a[1].x, (int)a[1].y, (int)a[1].z, (int)a[1].w};
+    const i32x8 a1 = {(int)a[2].x, (int)a[2].y, (int)a[2].z, (int)a[2].w,
+                      (int)a[3].x, (int)a[3].y, (int)a[3].z, (int)a[3].w};
+    const i32x8 b0 = {(int)b.q[0].x, (int)b.q[0].y, (int)b.q[0].z, (int)b.q[0].w, 0, 0, 0, 0};
+    const i32x8 b1 = {(int)b.q[1].x, (int)b.q[1].y, (int)b.q[1].z, (int)b.q[1].w, 0, 0, 0, 0};
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a0, b0, acc, 0, 4, 0, 127, 0,
+                                                           (int)b.sc);
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a1, b1, acc, 0, 4, 0, 127, 1,
+                                                           (int)b.sc);
+  }
+}
+
+// fp32 epilogue recipe shared by w8a8 (bit-exact contract) and a8w4:
+// ex = f32(exp_f64(-g)); sg = g / (1 + ex); h = sg * u.  w4a16 uses expf.
+template <int S>
+__device__ inline float silu_mul(float g, float u) {
+  float ex;
+  if constexpr (S == kW8A8) {
+    ex = (float)exp(-(double)g);
+  } else {
+    ex = expf(-g);
+  }
+  const float den = 1.0f + ex;
+  const float sg = g / den;
+  return sg * u;
+}
+
+template <int S, int STAGE, int BM>
+__global__ __launch_bounds__(kThreads) void moe_gemm_kernel(GemmArgs g) {
+  using T_ = Tr<S>;
+  using Acc = typename T_::Acc;
+  constexpr int MSUB = BM / 16;
+  constexpr int PITCH = T_::A_STEP + 16;               // LDS row pitch (bytes), padded
+  constexpr int CPR = T_::A_STEP / 16;                 // 16-byte chunks per row per step
+  constexpr int NCH = (BM * CPR + kThreads - 1) / kThreads;  // chunks per thread
+  constexpr int NF = T_::A_FRAG / 16;                  // 16-byte LDS reads per fragment
+
+  __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * PITCH];
+  __shared__ int sRow[BM];
+  __shared__ float sRed[kWaves][BM];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lq = lane >> 4;
+  const int num_m = *g.num_padded / BM;
+  const int total = num_m * g.ntiles_n;
+  const int per_xcd = gridDim.x >> 3;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int chunk = (total + 7) >> 3;
+  const int w_begin = xcd * chunk, w_end = min(total, w_begin + chunk);
+
+  const size_t K = (size_t)g.K;
+  const size_t kbytes = K * T_::KB_NUM / T_::KB_DEN;  // weight bytes per row
+  const int nsteps = g.K / T_::BK;
+  const uint8_t* __restrict__ A = reinterpret_cast<const uint8_t*>(g.a);
+  const uint8_t* __restrict__ B = reinterpret_cast<const uint8_t*>(g.b);
+
+  for (int wi = w_begin + slot; wi < w_end; wi += per_xcd) {
+    const int mt = wi / g.ntiles_n, nt = wi - mt * g.ntiles_n;
+    __syncthreads();  // previous tile's epilogue is done with sRow / sRed
+    int valid_here = 0;
+    if (tid < BM) {
+      const int p = g.sorted_pair_ids[mt * BM + tid];
+      const bool ok = p < g.P;
+      sRow[tid] = ok ? (STAGE == 1 ? p / g.k : p) : -1;
+      valid_here = ok;
+    }
+    const int nvalid = __syncthreads_count(valid_here);
+    const int mvalid = (nvalid + 15) >> 4;
+    const int e = g.tile_expert[mt];
+
+    // Weight rows of this wave's two sub-tiles.
+    int nrow[kNsub];
+    if (STAGE == 1) {
+      nrow[0] = nt * kStage1Cols + wave * 16 + lr;
+      nrow[1] = g.I + nrow[0];
+    } else {
+      nrow[0] = nt * kStage2Cols + wave * 32 + lr;
+      nrow[1] = nrow[0] + 16;
+    }
+    const uint8_t* brow[kNsub];
+    const uint8_t* srow[kNsub];
+#pragma unroll
+    for (int s = 0; s < kNsub; s++) {
+      const size_t r = (size_t)e * g.N + nrow[s];
+      brow[s] = B + r * kbytes + lq * T_::B_FRAG;
+      if (S == kW4A16) srow[s] = reinterpret_cast<const uint8_t*>(g.b_scale) + r * (K / 32) * 2 + lq * 2;
+      else if (S == kA8W4) srow[s] = reinterpret_cast<const uint8_t*>(g.b_scale) + r * (K / 32) + lq * 2;
+      else srow[s] = nullptr;
+    }
+
+    auto load_b = [&](BFrag<S>* bf, int ks) {
+#pragma unroll
+      for (int s = 0; s < kNsub; s++) {
+        const uint4* p = reinterpret_cast<const uint4*>(brow[s] + (size_t)ks * T_::B_STEP);
+#pragma unroll
+        for (int i = 0; i < T_::B_FRAG / 16; i++) bf[s].q[i] = p[i];
+        if (S == kW4A16) {
+          bf[s].sc = *reinterpret_cast<const unsigned short*>(srow[s] + (size_t)ks * 8);
+        } else if (S == kA8W4) {
+          bf[s].sc = *reinterpret_cast<const unsigned short*>(srow[s] + (size_t)ks * 8);
+        } else {
+          bf[s].sc = 0;
+        }
+      }
+    };
+
+    uint4 areg[NCH];
+    auto load_a = [&](int ks) {
+#pragma unroll
+      for (int i = 0; i < NCH; i++) {
+        const int c = tid + i * kThreads;
+        const int row = c / CPR, col = c - row * CPR;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (c < BM * CPR && row < nvalid) {
+          const int ri = sRow[row];
+          const uint8_t* src;
+          if (STAGE == 1)
+            src = A + (size_t)ri * g.H * T_::A_ELEM;
+          else
+            src = A + (size_t)(mt * BM + row) * g.I * T_::A_ELEM;
+          v = *reinterpret_cast<const uint4*>(src + (size_t)ks * T_::A_STEP + col * 16);
+        }
+        areg[i] = v;
+      }
+    };
+    auto store_a = [&](int buf) {
+#pragma unroll
+      for (int i = 0; i < NCH; i++) {
+        const int c = tid + i * kThreads;
+        const int row = c / CPR, col = c - row * CPR;
+        if (c < BM * CPR && row < mvalid * 16)
+          *reinterpret_cast<uint4*>(&sA[buf][row * PITCH + col * 16]) = areg[i];
+      }
+    };
+
+    Acc acc[MSUB][kNsub];
+#pragma unroll
+    for (int m = 0; m < MSUB; m++)
+#pragma unroll
+      for (int s = 0; s < kNsub; s++) acc[m][s] = Acc{0, 0, 0, 0};
+
+    BFrag<S> bcur[kNsub], bnext[kNsub];
+    load_a(0);
+    load_b(bcur, 0);
+    store_a(0);
+    __syncthreads();
+    for (int ks = 0; ks < nsteps; ks++) {
+      const int cur = ks & 1;
+      const bool more = ks + 1 < nsteps;
+      if (more) {
+        load_a(ks + 1);
+        load_b(bnext, ks + 1);
+      }
+#pragma unroll
+      for (int m = 0; m < MSUB; m++) {
+        if (m < mvalid) {
+          uint4 af[NF];
+          const uint8_t* src = &sA[cur][(m * 16 + lr) * PITCH + lq * T_::A_FRAG];
+#pragma unroll
+          for (int f = 0; f < NF; f++) af[f] = *reinterpret_cast<const uint4*>(src + f * 16);
+#pragma unroll
+          for (int s = 0; s < kNsub; s++) mfma_step<S>(acc[m][s], af, bcur[s]);
+        }
+      }
+      if (more) {
+        store_a(cur ^ 1);
+#pragma unroll
+        for (int s = 0; s < kNsub; s++) bcur[s] = bnext[s];
+      }
+      __syncthreads();
+    }
+
+    // ------------------------------------------------------------ epilogue
+    if (STAGE == 1) {
+      const int col = nt * kStage1Cols + wave * 16 + lr;
+      float ws_g = 1.f, ws_u = 1.f;
+      if (S == kW8A8) {
+        const float* ws = reinterpret_cast<const float*>(g.b_scale) + (size_t)e * g.N;
+        ws_g = ws[col];
+        ws_u = ws[g.I + col];
+      }
+#pragma unroll
+      for (int m = 0; m < MSUB; m++) {
+        if (m < mvalid) {
+#pragma unroll
+          for (int r = 0; r < 4; r++) {
+            const int row = m * 16 + lq * 4 + r;
+            const int tok = sRow[row];
+            const size_t orow = (size_t)mt * BM + row;
+            float gf, uf;
+            if constexpr (S == kW8A8) {
+              const float xs = tok >= 0 ? g.a_scale[tok] : 0.f;
+              gf = ((float)acc[m][0][r] * xs) * ws_g;
+              uf = ((float)acc[m][1][r] * xs) * ws_u;
+              if (g.dump != nullptr && tok >= 0) {
+                g.dump[orow * 2 * g.I + col] = acc[m][0][r];
+                g.dump[orow * 2 * g.I + g.I + col] = acc[m][1][r];
+              }
+            } else if constexpr (S == kA8W4) {
+              const float xs = tok >= 0 ? g.a_scale[tok] : 0.f;
+              gf = acc[m][0][r] * xs;
+              uf = acc[m][1][r] * xs;
+            } else {
+              gf = acc[m][0][r];
+              uf = acc[m][1][r];
+            }
+            const float h = tok >= 0 ? silu_mul<S>(gf, uf) : 0.f;
+            if constexpr (S == kW4A16) {
+              if (tok >= 0)
+                reinterpret_cast<__bf16*>(g.out)[orow * g.I + col] = (__bf16)h;
+            } else {
+              if (tok >= 0) reinterpret_cast<float*>(g.out)[orow * g.I + col] = h;
+              float a = fabsf(h);
+#pragma unroll
+              for (int off = 1; off < 16; off <<= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
+              if (lr == 0) sRed[wave][row] = a;
+            }
+          }
+        }
+      }
+      if constexpr (S != kW4A16) {
+        __syncthreads();
+        if (tid < mvalid * 16) {
+          const float a = fmaxf(fmaxf(sRed[0][tid], sRed[1][tid]), fmaxf(sRed[2][tid], sRed[3][tid]));
+          g.row_pmax[((size_t)mt * BM + tid) * g.ntiles_n + nt] = a;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < kNsub; s++) {
+        const int col = nrow[s];
+        float ws2 = 1.f;
+        if (S == kW8A8) ws2 = reinterpret_cast<const float*>(g.b_scale)[(size_t)e * g.N + col];
+#pragma unroll
+        for (int m = 0; m < MSUB; m++) {
+          if (m < mvalid) {
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+              const int row = m * 16 + lq * 4 + r;
+              const int pair = sRow[row];
+              if (pair < 0) continue;
+              const size_t orow = (size_t)mt * BM + row;
+              if constexpr (S == kW8A8) {
+                const float y = ((float)acc[m][s][r] * g.a_scale[orow]) * ws2;
+                reinterpret_cast<float*>(g.out)[(size_t)pair * g.H + col] = y;
+                if (g.dump != nullptr) g.dump[orow * g.H + col] = acc[m][s][r];
+              } else if constexpr (S == kA8W4) {
+                const float y = acc[m][s][r] * g.a_scale[orow];
+                reinterpret_cast<__bf16*>(g.out)[(size_t)pair * g.H + col] = (__bf16)y;
+              } else {
+                reinterpret_cast<__bf16*>(g.out)[(size_t)pair * g.H + col] = (__bf16)acc[m][s][r];
+              }
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int S, int STAGE, int BM>
+hipError_t launch_one(const GemmArgs& g, hipStream_t s) {
+  static int blocks_per_cu = 0;
+  if (blocks_per_cu == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, moe_gemm_kernel<S, STAGE, BM>, kThreads,
+                                                     0) != hipSuccess ||
+        n < 1)
+      n = 1;
+    blocks_per_cu = n;
+  }
+  int nblk = device_cu_count() * blocks_per_cu;
+  nblk = nblk < 8 ? 8 : (nblk / 8) * 8;
+  hipLaunchKernelGGL((moe_gemm_kernel<S, STAGE, BM>), dim3(nblk), dim3(kThreads), 0, s, g);
+  return hipGetLastError();
+}
+
+template <int S, int STAGE>
+hipError_t launch_bm(int block_m, const GemmArgs& g, hipStream_t s) {
+  switch (block_m) {
+    case 16: return launch_one<S, STAGE, 16>(g, s);
+    case 32: return launch_one<S, STAGE, 32>(g, s);
+    case 64: return launch_one<S, STAGE, 64>(g, s);
+    case 128: return launch_one<S, STAGE, 128>(g, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm(int scheme, int stage, int block_m, const GemmArgs& g, hipStream_t s) {
+  switch (scheme * 2 + (stage - 1)) {
+    case 0: return launch_bm<kW4A16, 1>(block_m, g, s);
+    case 1: return launch_bm<kW4A16, 2>(block_m, g, s);
+    case 2: return launch_bm<kW8A8, 1>(block_m, g, s);
+    case 3: return launch_bm<kW8A8, 2>(block_m, g, s);
+    case 4: return launch_bm<kA8W4, 1>(block_m, g, s);
+    case 5: return launch_bm<kA8W4, 2>(block_m, g, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace qmoe

@@ -1,0 +1,48 @@
+// Internal declarations shared by the HIP sources of libqmoe (not installed).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qmoe {
+
+// Tile geometry of the grouped GEMMs (both stages).  256 threads = 4 waves of
+// 64; every wave owns NSUB 16-column sub-tiles and all BM rows of the tile.
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+constexpr int kNsub = 2;
+constexpr int kStage1Cols = 64;   // h columns per stage-1 tile (64 gate + 64 up rows)
+constexpr int kStage2Cols = 128;  // output columns per stage-2 tile
+
+struct GemmArgs {
+  int T, H, I, E, k, P;  // P = T*k pairs
+  int N, K;              // this stage's GEMM N (weight rows) and K
+  int ntiles_n;          // column tiles per row tile
+  const int32_t* sorted_pair_ids;
+  const int32_t* tile_expert;
+  const int32_t* num_padded;
+  const void* a;         // stage 1: x [T,H]; stage 2: h (quantized) [cap, I]
+  const float* a_scale;  // stage 1: x_scale [T]; stage 2: h_scale [cap]
+  const void* b;         // weight codes [E, N, K(/2)]
+  const void* b_scale;   // weight scales
+  void* out;             // stage 1: h (bf16 or f32) [cap, I]; stage 2: y_pairs [P, H]
+  float* row_pmax;       // stage 1 (w8a8/a8w4): |h| max per row and column tile
+  int32_t* dump;         // w8a8 debug accumulators or nullptr
+};
+
+hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w,
+                        hipStream_t s);
+hipError_t launch_align(const int32_t* ids, int T, int k, int E, int block_m, int32_t* sorted,
+                        int32_t* tile_expert, int32_t* offsets, int32_t* num_padded,
+                        int32_t* chunk_counts, int32_t* chunk_flags, int32_t* flags, int cap,
+                        hipStream_t s);
+hipError_t launch_gemm(int scheme, int stage, int block_m, const GemmArgs& g, hipStream_t s);
+hipError_t launch_requant(int scheme, const int32_t* sorted, const int32_t* num_padded,
+                          int P, int I, int ntiles_n, int cap, const float* h32,
+                          const float* pmax, uint8_t* hq, float* hs, hipStream_t s);
+hipError_t launch_combine(const void* y, int y_f32, const float* w, int T, int k, int H,
+                          uint16_t* out_bf16, float* out_f32, hipStream_t s);
+
+size_t align_chunk_count(int T);
+int device_cu_count();
+
+}  // namespace qmoe

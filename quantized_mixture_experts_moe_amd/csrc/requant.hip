@@ -1,0 +1,79 @@
+// Per-row requantization of the intermediate h for the activation-quantized
+// schemes: w8a8 -> int8 (vLLM issue "Evaluate native IU4/IU8 WMMA for
+// grouped-INT MoE prefill on gfx1151", section Constraint: integer matrix
+// products need int8 activations), a8w4 -> fp8 e4m3 (aiter PR 6090, section
+// Changes: fp8 act).  Symmetric, one fp32 scale per row:
+//   s = absmax / qmax (qmax 127 or 448; 1 for an all-zero row),
+//   w8a8: code = clamp(round_half_even(h / s), -127, 127)
+//   a8w4: code = e4m3 round-to-nearest-even of h / s, saturated to +-448.
+// The row absmax is the max of the per-column-tile maxima stage 1 wrote.
+// One wave per row; padding rows are skipped.
+#include "qmoe_internal.h"
+
+namespace qmoe {
+namespace {
+
+__device__ inline uint32_t to_e4m3x4(float a, float b, float c, float d) {
+  // v_cvt_pk_fp8_f32: OCP e4m3 on gfx950, round to nearest even.  Inputs are
+  // clamped to +-448 first so no value can round to NaN.
+  a = fminf(fmaxf(a, -448.f), 448.f);
+  b = fminf(fmaxf(b, -448.f), 448.f);
+  c = fminf(fmaxf(c, -448.f), 448.f);
+  d = fminf(fmaxf(d, -448.f), 448.f);
+  int v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  v = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, v, true);
+  return (uint32_t)v;
+}
+
+__device__ inline uint32_t to_i8x4(float a, float b, float c, float d) {
+  const int qa = (int)fminf(fmaxf(rintf(a), -127.f), 127.f);
+  const int qb = (int)fminf(fmaxf(rintf(b), -127.f), 127.f);
+  const int qc = (int)fminf(fmaxf(rintf(c), -127.f), 127.f);
+  const int qd = (int)fminf(fmaxf(rintf(d), -127.f), 127.f);
+  return (uint32_t)(qa & 0xff) | ((uint32_t)(qb & 0xff) << 8) | ((uint32_t)(qc & 0xff) << 16) |
+         ((uint32_t)(qd & 0xff) << 24);
+}
+
+template <bool FP8>
+__global__ __launch_bounds__(256) void requant_kernel(const int32_t* __restrict__ sorted,
+                                                      const int32_t* __restrict__ num_padded,
+                                                      int P, int I, int ntiles_n,
+                                                      const float* __restrict__ h32,
+                                                      const float* __restrict__ pmax,
+                                                      uint8_t* __restrict__ hq,
+                                                      float* __restrict__ hs) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= *num_padded) return;
+  if (sorted[row] >= P) return;  // padding slot
+  float a = 0.f;
+  for (int i = lane; i < ntiles_n; i += 64) a = fmaxf(a, pmax[(size_t)row * ntiles_n + i]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
+  const float s = a > 0.f ? a / (FP8 ? 448.0f : 127.0f) : 1.0f;
+  if (lane == 0) hs[row] = s;
+  const float4* src = reinterpret_cast<const float4*>(h32 + (size_t)row * I);
+  uint32_t* dst = reinterpret_cast<uint32_t*>(hq + (size_t)row * I);
+  for (int i = lane; i < I / 4; i += 64) {
+    const float4 v = src[i];
+    const float x0 = v.x / s, x1 = v.y / s, x2 = v.z / s, x3 = v.w / s;
+    dst[i] = FP8 ? to_e4m3x4(x0, x1, x2, x3) : to_i8x4(x0, x1, x2, x3);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_requant(int scheme, const int32_t* sorted, const int32_t* num_padded, int P,
+                          int I, int ntiles_n, int cap, const float* h32, const float* pmax,
+                          uint8_t* hq, float* hs, hipStream_t s) {
+  const dim3 grid((cap + 3) / 4), block(256);
+  if (scheme == 2)
+    hipLaunchKernelGGL(requant_kernel<true>, grid, block, 0, s, sorted, num_padded, P, I,
+                       ntiles_n, h32, pmax, hq, hs);
+  else
+    hipLaunchKernelGGL(requant_kernel<false>, grid, block, 0, s, sorted, num_padded, P, I,
+                       ntiles_n, h32, pmax, hq, hs);
+  return hipGetLastError();
+}
+
+}  // namespace qmoe

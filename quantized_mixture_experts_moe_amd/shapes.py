@@ -91,3 +91,17 @@ def shape_by_name(name: str) -> MoEShape:
         if s.name.split("@")[0] == base:
             return s.with_tokens(int(t)) if t else s
     raise KeyError(name)
+
+
+def default_block_m(shape: MoEShape) -> int:
+    """Tile height for a shape: about the mean rows per expert, 16..128.
+
+    Row tiles never straddle experts, so a tile much taller than an expert's
+    row count is mostly padding (skipped in 16-row groups by the kernels);
+    at >= 128 rows per expert the tallest tile is used.
+    """
+    mean_rows = shape.pairs / shape.experts
+    for bm in (16, 32, 64):
+        if mean_rows <= bm:
+            return bm
+    return 128
