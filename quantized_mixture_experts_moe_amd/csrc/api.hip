@@ -144,7 +144,8 @@ qmoe_status qmoe_align(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
   if (T < 0 || k < 1 || E < 1 || k > E || !valid_block_m(block_m)) return QMOE_ERR_INVALID_ARG;
   if ((long long)T * k > (1ll << 30)) return QMOE_ERR_INVALID_ARG;
   if (E > 1024) return QMOE_ERR_UNSUPPORTED;
-  if (!topk_ids || !sorted_pair_ids || !tile_expert || !expert_offsets || !num_padded || !ws)
+  if ((T > 0 && !topk_ids) || !sorted_pair_ids || !tile_expert || !expert_offsets ||
+      !num_padded || !ws)
     return QMOE_ERR_INVALID_ARG;
   const AlignWs lay = align_ws_layout(T, E);
   if (ws_bytes < lay.total || !aligned(ws, 256)) return QMOE_ERR_INVALID_ARG;

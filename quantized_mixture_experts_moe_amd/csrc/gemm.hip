@@ -27,10 +27,16 @@
 //          Changes: fp8 act, MXFP4 weight).
 //
 // Per-lane fragment layout of a 16x16xK MFMA (lane = 16*q + r): A row r and
-// B column r hold a contiguous quarter q of the instruction's K.  A step
-// loads, per lane, a contiguous run of each weight row; the K order inside
-// a step is permuted identically for A and B, which leaves the dot product
-// unchanged, and every 32-wide scale block stays inside one lane.
+// B column r hold a contiguous quarter q of the instruction's K (bf16, i8,
+// and fp4 B of the scaled MFMA).  A step loads, per lane, a contiguous run of
+// each weight row; the K order inside a step is permuted identically for A
+// and B, which leaves the dot product unchanged, and every 32-wide scale
+// block stays inside one lane.  One exception, measured on gfx950: with an
+// fp8 A and an fp4 B the fp8 operand is split in two 16-byte halves, lane
+// group q holding K [16q, 16q+16) in bytes 0-15 and K [64+16q, 64+16q+16)
+// in bytes 16-31, while the fp4 B of lane group q covers K [32q, 32q+32)
+// and takes that block's e8m0 scale from its own lane.  a_frag_offset()
+// gathers the A bytes to match.
 //
 // Schedule: a persistent grid (a multiple of 8 blocks, one slice of the work
 // list per XCD); work item = (row tile, column tile), row tile major, so the
@@ -84,6 +90,22 @@ struct Tr<kA8W4> {
   static constexpr int KB_NUM = 1, KB_DEN = 2;
   typedef f32x4 Acc;
 };
+
+// Byte offset, inside a staged activation row of one step, of the f-th
+// 16-byte piece of lane group q's A fragment (pieces 2j, 2j+1 feed MFMA j).
+template <int S>
+__device__ inline int a_frag_offset(int q, int f) {
+  if constexpr (S == kA8W4) {
+    // B lane group q holds the 32-K blocks 2q (MFMA 0) and 2q+1 (MFMA 1) of
+    // the 256-K step, so MFMA j's logical block b is step block 2b + j.  The
+    // fp8 halves of lane group q map to logical K 16q and 64 + 16q.
+    const int o = 64 * (q >> 1) + 16 * (q & 1);
+    const int j = f >> 1, half = f & 1;
+    return o + 32 * j + 128 * half;
+  } else {
+    return q * Tr<S>::A_FRAG + 16 * f;
+  }
+}
 
 // Weight fragment of one 16-column sub-tile for one step.
 template <int S>
@@ -280,9 +302,10 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_kernel(GemmArgs g) {
       for (int m = 0; m < MSUB; m++) {
         if (m < mvalid) {
           uint4 af[NF];
-          const uint8_t* src = &sA[cur][(m * 16 + lr) * PITCH + lq * T_::A_FRAG];
+          const uint8_t* src = &sA[cur][(m * 16 + lr) * PITCH];
 #pragma unroll
-          for (int f = 0; f < NF; f++) af[f] = *reinterpret_cast<const uint4*>(src + f * 16);
+          for (int f = 0; f < NF; f++)
+            af[f] = *reinterpret_cast<const uint4*>(src + a_frag_offset<S>(lq, f));
 #pragma unroll
           for (int s = 0; s < kNsub; s++) mfma_step<S>(acc[m][s], af, bcur[s]);
         }
