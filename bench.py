@@ -1,0 +1,228 @@
+#!/usr/bin/env python3
+"""Benchmark of the grouped, weight-quantized MoE FFN on one MI355X.
+
+A step is one pass of the whole layer on one batch of synthetic inputs that
+already sit in HBM: route (softmax top-k) -> align (group pairs by expert)
+-> grouped FFN (stage 1 + requant + stage 2) -> combine.  Default workload:
+fp8 activations x MXFP4 weights, hidden 4096, 512 experts, top-10, expert
+inter 1024, 4096 tokens (40960 (token, expert) rows).
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "grouped MoE FFN TFLOP/s + % MFMA/HBM roofline at M=4096 prefill, 1 GPU"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"a8w4": 5000.0, "w8a8": 5000.0, "w4a16": 2500.0}
+DTYPE = {"a8w4": "fp8e4m3*fp4e2m1", "w8a8": "int8", "w4a16": "bf16"}
+# Counter calibration: HBM bytes per KiB reported by FETCH_SIZE / WRITE_SIZE,
+# from a plain device copy of known size (None until measured).
+FETCH_FACTOR = None
+WRITE_FACTOR = None
+# Stage-1 traffic measured with rocprofv3 --pmc for the current kernel, in
+# bytes per launch (None when the kernel changed after the counters were taken).
+STAGE1_TRAFFIC_BYTES = None
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def weight_bytes_per_expert(shape, which: str) -> float:
+    """Codes + scales of one expert's W13 ([2I, H]) or W2 ([H, I])."""
+    n, kdim = (2 * shape.inter, shape.hidden) if which == "w13" else (shape.hidden, shape.inter)
+    if shape.scheme == "w8a8":
+        return n * kdim + n * 4
+    if shape.scheme == "w4a16":
+        return n * kdim / 2 + n * (kdim // 32) * 2
+    return n * kdim / 2 + n * (kdim // 32)  # a8w4: e2m1 + e8m0
+
+
+def algorithmic_bytes(shape, touched: int) -> dict:
+    """Bytes each kernel must move at minimum (the per-unit figures times the
+    units one launch processes): weights of the touched experts, activations
+    in their scheme format, outputs once."""
+    T, H, I, k = shape.tokens, shape.hidden, shape.inter, shape.topk
+    P = T * k
+    xb = 2 if shape.scheme == "w4a16" else 1
+    xs = 0 if shape.scheme == "w4a16" else 4
+    hb = 2 if shape.scheme == "w4a16" else 1
+    yb = 4 if shape.scheme == "w8a8" else 2
+    s1 = touched * weight_bytes_per_expert(shape, "w13") + T * (H * xb + xs) + P * (I * hb + xs)
+    s2 = touched * weight_bytes_per_expert(shape, "w2") + P * (I * hb + xs) + P * H * yb
+    comb = P * H * yb + P * 4 + T * H * 2
+    step = (touched * (weight_bytes_per_expert(shape, "w13") + weight_bytes_per_expert(shape, "w2"))
+            + T * (H * xb + xs) + T * H * 2 + T * shape.experts * 4 + P * 8)
+    return {"stage1": s1, "stage2": s2, "combine": comb, "step": step}
+
+
+def cpu_baseline(shape, inp, target_s: float = 15.0) -> dict:
+    """Time the CPU oracle on a bounded sample of the same workload."""
+    import oracle as O
+    from quantized_mixture_experts_moe_amd import synth
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    rng = np.random.default_rng(0)
+    n_tok = 2
+    elapsed = 0.0
+    total_flops = 0.0
+    total_pairs = 0
+    total_tok = 0
+    while True:
+        toks = rng.choice(shape.tokens, n_tok, replace=False)
+        ids, w = O.route(inp["logits"][toks], shape.topk)
+        experts = sorted(set(ids.reshape(-1).tolist()))
+        wts = {e: synth.expert_weights(shape, e) for e in experts}  # generation: not timed
+        xs = None if inp["x_scale"] is None else inp["x_scale"][toks]
+        t0 = time.perf_counter()
+        O.moe_forward(shape.scheme, inp["x"][toks], xs, lambda e: wts[e], ids, w)
+        dt = time.perf_counter() - t0
+        elapsed += dt
+        total_pairs += n_tok * shape.topk
+        total_tok += n_tok
+        total_flops += 6.0 * shape.hidden * shape.inter * n_tok * shape.topk
+        log(f"cpu oracle: {n_tok} tokens in {dt:.2f}s")
+        if elapsed >= target_s * 0.5 or n_tok >= 256:
+            break
+        n_tok = int(min(256, max(n_tok * 2, n_tok * (target_s - elapsed) / max(dt, 1e-3) / 2)))
+    return {"value": total_flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{total_tok} tokens ({total_pairs} token-expert rows) of {shape.name}, "
+                      f"fp64 numpy oracle, {elapsed:.1f}s; weight generation not timed",
+            "tokens_per_s": total_tok / elapsed}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="a8w4_large@T4096")
+    ap.add_argument("--block-m", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+              "multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from quantized_mixture_experts_moe_amd import ops, synth
+    from quantized_mixture_experts_moe_amd.shapes import default_block_m, shape_by_name
+
+    shape = shape_by_name(args.workload)
+    bm = args.block_m or default_block_m(shape)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.perf_counter()
+    inp = synth.make_inputs(shape)
+    log(f"generated {shape.name} in {time.perf_counter() - t0:.1f}s")
+
+    def gpu(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    g = {k: gpu(v) for k, v in inp.items()}
+    W = {k: g[k] for k in ("w13", "w13_scale", "w2", "w2_scale")}
+    T, E, k, H = shape.tokens, shape.experts, shape.topk, shape.hidden
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    tw = torch.empty((T, k), dtype=torch.float32, device=dev)
+    ops.route(g["logits"], k, ids, tw)
+    al = ops.align(ids, E, bm)
+    y, ws = ops.grouped_ffn(shape.scheme, g["x"], g["x_scale"], W, al, E, k)
+    out_bf16, out_f32 = ops.combine(y, tw, want_bf16=True, want_f32=shape.scheme == "w8a8")
+    torch.cuda.synchronize()
+    touched = int(torch.unique(ids).numel())
+
+    n_ev = 8
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+    for row in evs:  # create the underlying events
+        for e in row:
+            e.record()
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        ops.route(g["logits"], k, ids, tw)
+        if ev is not None:
+            ev[1].record()
+        ops.align(ids, E, bm, out=al)
+        ops.grouped_ffn(shape.scheme, g["x"], g["x_scale"], W, al, E, k, ws=ws, y_pairs=y,
+                        stage_events=None if ev is None else ev[2:6])
+        ops.combine(y, tw, out_bf16=out_bf16, out_f32=out_f32, want_f32=out_f32 is not None)
+        if ev is not None:
+            ev[6].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    def avg(a, b):
+        return float(np.mean([evs[i][a].elapsed_time(evs[i][b]) for i in range(args.steps)]))
+
+    kern = {"route": avg(0, 1), "align": avg(1, 2), "stage1": avg(2, 3), "requant": avg(3, 4),
+            "stage2": avg(4, 5), "combine": avg(5, 6), "step_events": avg(0, 6)}
+    log("per-kernel ms: " + ", ".join(f"{n} {v:.4f}" for n, v in kern.items()))
+
+    flops = shape.useful_flops()
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    ab = algorithmic_bytes(shape, touched)
+    dom = max(("stage1", "stage2", "combine"), key=lambda n: kern[n])
+    achieved = ab[dom] / (kern[dom] * 1e-3) / 1e9
+    traffic = None
+    if dom == "stage1" and STAGE1_TRAFFIC_BYTES is not None:
+        traffic = STAGE1_TRAFFIC_BYTES
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "kernel": f"moe_gemm_kernel {dom} ({shape.scheme}, block_m {bm})",
+            "kernel_ms": round(kern[dom], 4), "algorithmic_bytes": int(ab[dom])}
+    step_gbs = ab["step"] / (ms_per_step * 1e-3) / 1e9
+    res = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": DTYPE[shape.scheme], "data": "synthetic (seeded generator, weights random)",
+        "config": {"workload": shape.name, "scheme": shape.scheme, "tokens": T, "hidden": H,
+                   "inter": shape.inter, "experts": E, "topk": k, "block_m": bm,
+                   "touched_experts": touched, "parallelism": "none (1 GPU)"},
+        "tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
+        "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
+        "step_mfma_frac": round(tflops / MFMA_PEAK_TFLOPS[shape.scheme], 4),
+        "kernel_ms": {n: round(v, 4) for n, v in kern.items()},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(shape, inp, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -166,6 +166,17 @@ qmoe_status qmoe_grouped_ffn(const qmoe_ffn_desc* d, const void* x, const float*
                              const int32_t* tile_expert, const int32_t* num_padded,
                              void* y_pairs, void* ws, size_t ws_bytes, void* stream);
 
+/* Same as qmoe_grouped_ffn, and also records stage_events[0..3] (each a
+ * hipEvent_t created by the caller) on the stream: before stage 1, after
+ * stage 1, after the requantization of h (same point as after stage 1 for
+ * W4A16), after stage 2.  For measuring each kernel inside a timed run.  */
+qmoe_status qmoe_grouped_ffn_profiled(const qmoe_ffn_desc* d, const void* x,
+                                      const float* x_scale, const qmoe_weights* w,
+                                      const int32_t* sorted_pair_ids,
+                                      const int32_t* tile_expert, const int32_t* num_padded,
+                                      void* y_pairs, void* ws, size_t ws_bytes,
+                                      void* const stage_events[4], void* stream);
+
 /* ---------------------------------------------------------------------
  * qmoe_combine -- out[t,:] = sum_{j=0}^{k-1} topk_w[t,j] * y_pairs[t*k+j,:]
  * accumulated in fp32 in slot order j = 0..k-1 (acc = acc + w*y, no fused

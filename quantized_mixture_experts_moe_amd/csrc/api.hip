@@ -188,10 +188,11 @@ qmoe_status qmoe_grouped_ffn_debug_offsets(const qmoe_ffn_desc* d, size_t* acc1_
   return QMOE_OK;
 }
 
-qmoe_status qmoe_grouped_ffn(const qmoe_ffn_desc* d, const void* x, const float* x_scale,
-                             const qmoe_weights* w, const int32_t* sorted_pair_ids,
-                             const int32_t* tile_expert, const int32_t* num_padded, void* y_pairs,
-                             void* ws, size_t ws_bytes, void* stream) {
+static qmoe_status grouped_ffn_impl(const qmoe_ffn_desc* d, const void* x, const float* x_scale,
+                                    const qmoe_weights* w, const int32_t* sorted_pair_ids,
+                                    const int32_t* tile_expert, const int32_t* num_padded,
+                                    void* y_pairs, void* ws, size_t ws_bytes,
+                                    void* const* events, void* stream) {
   const qmoe_status st = check_desc(d);
   if (st != QMOE_OK) return st;
   if (d->T == 0) return QMOE_OK;
@@ -231,7 +232,12 @@ qmoe_status qmoe_grouped_ffn(const qmoe_ffn_desc* d, const void* x, const float*
   g1.out = wsb + lay.h;
   g1.row_pmax = quant_act ? reinterpret_cast<float*>(wsb + lay.pmax) : nullptr;
   g1.dump = dump ? reinterpret_cast<int32_t*>(wsb + lay.acc1) : nullptr;
-  hipError_t e = launch_gemm(d->scheme, 1, d->block_m, g1, s);
+  auto mark = [&](int i) -> hipError_t {
+    return events ? hipEventRecord((hipEvent_t)events[i], s) : hipSuccess;
+  };
+  hipError_t e = mark(0);
+  if (e == hipSuccess) e = launch_gemm(d->scheme, 1, d->block_m, g1, s);
+  if (e == hipSuccess) e = mark(1);
   if (e != hipSuccess) return hip_status(e);
 
   if (quant_act) {
@@ -241,6 +247,8 @@ qmoe_status qmoe_grouped_ffn(const qmoe_ffn_desc* d, const void* x, const float*
                        reinterpret_cast<float*>(wsb + lay.hs), s);
     if (e != hipSuccess) return hip_status(e);
   }
+  e = mark(2);
+  if (e != hipSuccess) return hip_status(e);
 
   g2.N = d->H;
   g2.K = d->I;
@@ -253,7 +261,33 @@ qmoe_status qmoe_grouped_ffn(const qmoe_ffn_desc* d, const void* x, const float*
   g2.row_pmax = nullptr;
   g2.dump = dump ? reinterpret_cast<int32_t*>(wsb + lay.acc2) : nullptr;
   e = launch_gemm(d->scheme, 2, d->block_m, g2, s);
+  if (e == hipSuccess) e = mark(3);
   return hip_status(e);
+}
+
+}  // extern "C" (reopened below)
+
+extern "C" {
+
+qmoe_status qmoe_grouped_ffn(const qmoe_ffn_desc* d, const void* x, const float* x_scale,
+                             const qmoe_weights* w, const int32_t* sorted_pair_ids,
+                             const int32_t* tile_expert, const int32_t* num_padded, void* y_pairs,
+                             void* ws, size_t ws_bytes, void* stream) {
+  return grouped_ffn_impl(d, x, x_scale, w, sorted_pair_ids, tile_expert, num_padded, y_pairs, ws,
+                          ws_bytes, nullptr, stream);
+}
+
+qmoe_status qmoe_grouped_ffn_profiled(const qmoe_ffn_desc* d, const void* x,
+                                      const float* x_scale, const qmoe_weights* w,
+                                      const int32_t* sorted_pair_ids,
+                                      const int32_t* tile_expert, const int32_t* num_padded,
+                                      void* y_pairs, void* ws, size_t ws_bytes,
+                                      void* const stage_events[4], void* stream) {
+  if (!stage_events || !stage_events[0] || !stage_events[1] || !stage_events[2] ||
+      !stage_events[3])
+    return QMOE_ERR_INVALID_ARG;
+  return grouped_ffn_impl(d, x, x_scale, w, sorted_pair_ids, tile_expert, num_padded, y_pairs, ws,
+                          ws_bytes, stage_events, stream);
 }
 
 qmoe_status qmoe_combine(const void* y_pairs, int32_t y_dtype, const float* topk_w, int32_t T,

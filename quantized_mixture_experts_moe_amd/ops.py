@@ -25,7 +25,7 @@ EXPORTS = (
     "qmoe_abi_version", "qmoe_status_str", "qmoe_last_hip_error", "qmoe_route",
     "qmoe_align_capacity", "qmoe_align_workspace", "qmoe_align", "qmoe_check_flags",
     "qmoe_grouped_ffn_workspace", "qmoe_grouped_ffn_debug_offsets", "qmoe_grouped_ffn",
-    "qmoe_combine",
+    "qmoe_grouped_ffn_profiled", "qmoe_combine",
 )
 
 
@@ -80,6 +80,10 @@ def _lib() -> ctypes.CDLL:
     L.qmoe_grouped_ffn.restype = ctypes.c_int
     L.qmoe_grouped_ffn.argtypes = [ctypes.POINTER(FfnDesc), vp, vp, ctypes.POINTER(Weights),
                                    vp, vp, vp, vp, vp, sz, vp]
+    L.qmoe_grouped_ffn_profiled.restype = ctypes.c_int
+    L.qmoe_grouped_ffn_profiled.argtypes = [ctypes.POINTER(FfnDesc), vp, vp,
+                                            ctypes.POINTER(Weights), vp, vp, vp, vp, vp, sz,
+                                            ctypes.POINTER(ctypes.c_void_p), vp]
     L.qmoe_combine.restype = ctypes.c_int
     L.qmoe_combine.argtypes = [vp, i32, vp, i32, i32, i32, vp, vp, vp]
     _LIB = L
@@ -115,12 +119,15 @@ def _ws(nbytes: int, device) -> torch.Tensor:
 
 # ---------------------------------------------------------------- routing
 
-def route(logits: torch.Tensor, k: int):
+def route(logits: torch.Tensor, k: int, ids: Optional[torch.Tensor] = None,
+          w: Optional[torch.Tensor] = None):
     """qmoe_route: (topk_ids int32 [T,k], topk_w fp32 [T,k])."""
     T, E = logits.shape
     assert logits.dtype == torch.float32
-    ids = torch.empty((T, k), dtype=torch.int32, device=logits.device)
-    w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    if ids is None:
+        ids = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    if w is None:
+        w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
     _check(_lib().qmoe_route(_ptr(logits), T, E, k, _ptr(ids), _ptr(w), _stream(logits.device)),
            "qmoe_route")
     return ids, w
@@ -136,18 +143,24 @@ def align_workspace(T: int, k: int, E: int) -> int:
     return int(_lib().qmoe_align_workspace(T, k, E))
 
 
-def align(topk_ids: torch.Tensor, E: int, block_m: int, ws: Optional[torch.Tensor] = None) -> dict:
-    """qmoe_align: expert-sorted, block_m-padded pair slots."""
+def align(topk_ids: torch.Tensor, E: int, block_m: int, ws: Optional[torch.Tensor] = None,
+          out: Optional[dict] = None) -> dict:
+    """qmoe_align: expert-sorted, block_m-padded pair slots (``out`` reuses a
+    previous result's buffers)."""
     T, k = topk_ids.shape
     dev = topk_ids.device
     cap = align_capacity(T, k, E, block_m)
-    out = {
-        "sorted_pair_ids": torch.empty(cap, dtype=torch.int32, device=dev),
-        "tile_expert": torch.empty(cap // block_m, dtype=torch.int32, device=dev),
-        "expert_offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
-        "num_padded": torch.empty(1, dtype=torch.int32, device=dev),
-        "block_m": block_m,
-    }
+    if out is None:
+        out = {
+            "sorted_pair_ids": torch.empty(cap, dtype=torch.int32, device=dev),
+            "tile_expert": torch.empty(cap // block_m, dtype=torch.int32, device=dev),
+            "expert_offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
+            "num_padded": torch.empty(1, dtype=torch.int32, device=dev),
+            "block_m": block_m,
+        }
+        ws = out.get("ws", ws)
+    else:
+        ws = out["ws"]
     need = align_workspace(T, k, E)
     if ws is None or ws.numel() < need:
         ws = _ws(need, dev)
@@ -186,8 +199,9 @@ def grouped_ffn_debug_offsets(desc: FfnDesc):
 
 def grouped_ffn(scheme: str, x: torch.Tensor, x_scale: Optional[torch.Tensor], weights: dict,
                 al: dict, E: int, k: int, flags: int = 0, ws: Optional[torch.Tensor] = None,
-                y_pairs: Optional[torch.Tensor] = None):
-    """qmoe_grouped_ffn; returns (y_pairs [T*k, H], workspace)."""
+                y_pairs: Optional[torch.Tensor] = None, stage_events=None):
+    """qmoe_grouped_ffn (qmoe_grouped_ffn_profiled when four recorded
+    torch.cuda.Event objects are given); returns (y_pairs [T*k, H], ws)."""
     T, H = x.shape
     I = weights["w13"].shape[1] // 2
     dev = x.device
@@ -202,10 +216,15 @@ def grouped_ffn(scheme: str, x: torch.Tensor, x_scale: Optional[torch.Tensor], w
         y_pairs = torch.empty((T * k, H), dtype=ydt, device=dev)
     w = Weights(_ptr(weights["w13"]), _ptr(weights["w13_scale"]), _ptr(weights["w2"]),
                 _ptr(weights["w2_scale"]))
-    _check(_lib().qmoe_grouped_ffn(ctypes.byref(desc), _ptr(x), _ptr(x_scale), ctypes.byref(w),
-                                   _ptr(al["sorted_pair_ids"]), _ptr(al["tile_expert"]),
-                                   _ptr(al["num_padded"]), _ptr(y_pairs), _ptr(ws), ws.numel(),
-                                   _stream(dev)), "qmoe_grouped_ffn")
+    args = (ctypes.byref(desc), _ptr(x), _ptr(x_scale), ctypes.byref(w),
+            _ptr(al["sorted_pair_ids"]), _ptr(al["tile_expert"]), _ptr(al["num_padded"]),
+            _ptr(y_pairs), _ptr(ws), ws.numel())
+    if stage_events is None:
+        _check(_lib().qmoe_grouped_ffn(*args, _stream(dev)), "qmoe_grouped_ffn")
+    else:
+        ev = (ctypes.c_void_p * 4)(*[e.cuda_event for e in stage_events])
+        _check(_lib().qmoe_grouped_ffn_profiled(*args, ev, _stream(dev)),
+               "qmoe_grouped_ffn_profiled")
     return y_pairs, ws
 
 
