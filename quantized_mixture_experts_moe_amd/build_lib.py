@@ -23,6 +23,8 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
     # Keep the compiler from forming packed fp32 arithmetic.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Keep small per-thread arrays in registers rather than moving them to LDS.
+    "-mllvm", "-disable-promote-alloca-to-lds",
     "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include"),
 ]
 

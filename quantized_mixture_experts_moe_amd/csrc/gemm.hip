@@ -7,13 +7,15 @@
 // (aiter PR 6090, Test Plan: stage1 tiles, then stage2 tiles.)
 //
 // Rows are the expert-sorted, block_m-padded pair slots from moe_align; a
-// row tile never straddles two experts.  One workgroup = 4 waves; each wave
-// owns two 16-column weight sub-tiles (stage 1: the gate column and the up
-// column of the same h column, so silu(gate)*up is formed in registers) and
-// all BM rows.  Weight fragments stream from HBM straight into VGPRs, each
-// weight byte read by exactly one wave; the gathered activation rows are
-// staged once per step in LDS and shared by the 4 waves.  16-row groups past
-// the tile's last real row are skipped.
+// row tile never straddles two experts.  One workgroup = 8 waves (two per
+// SIMD); each wave owns two 16-column weight sub-tiles (stage 1: the gate
+// column and the up column of the same h column, so silu(gate)*up is formed
+// in registers) and all BM rows.  Weight fragments stream from HBM straight
+// into VGPRs, each weight byte read by exactly one wave, two K steps ahead of
+// the MFMAs (a ring of three register sets); the gathered activation rows go
+// global -> VGPR -> a three-slot LDS ring, loaded two steps ahead and shared
+// by the 8 waves.  One barrier per K step.  16-row groups past the tile's
+// last real row are skipped.
 //
 // Matrix cores (CDNA4 MFMA), 16x16 output per instruction:
 //   w4a16: v_mfma_f32_16x16x32_bf16, int4 * fp16 group scale rounded to
@@ -52,6 +54,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+// Native 16-byte vector (HIP's uint4 is a struct, which keeps arrays of it
+// out of registers).
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 enum { kW4A16 = 0, kW8A8 = 1, kA8W4 = 2 };
 
@@ -110,7 +115,7 @@ __device__ inline int a_frag_offset(int q, int f) {
 // Weight fragment of one 16-column sub-tile for one step.
 template <int S>
 struct BFrag {
-  uint4 q[Tr<S>::B_FRAG / 16];
+  u32x4 q[Tr<S>::B_FRAG / 16];
   uint32_t sc;  // w4a16: fp16 group scale bits; a8w4: two e8m0 bytes; w8a8: unused
 };
 
@@ -125,7 +130,7 @@ __device__ inline bf16x8 dequant8_bf16(uint32_t v, float sc) {
 }
 
 template <int S>
-__device__ inline void mfma_step(typename Tr<S>::Acc& acc, const uint4* a, const BFrag<S>& b) {
+__device__ inline void mfma_step(typename Tr<S>::Acc& acc, const u32x4* a, const BFrag<S>& b) {
   if constexpr (S == kW4A16) {
     const float sc = __half2float(__ushort_as_half((unsigned short)b.sc));
     const uint32_t w[4] = {b.q[0].x, b.q[0].y, b.q[0].z, b.q[0].w};
@@ -172,17 +177,19 @@ __device__ inline float silu_mul(float g, float u) {
   return sg * u;
 }
 
-template <int S, int STAGE, int BM>
-__global__ __launch_bounds__(kThreads) void moe_gemm_kernel(GemmArgs g) {
+template <int S, int STAGE, int BM, int BPRE>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+moe_gemm_kernel(GemmArgs g) {
   using T_ = Tr<S>;
   using Acc = typename T_::Acc;
   constexpr int MSUB = BM / 16;
-  constexpr int PITCH = T_::A_STEP + 16;               // LDS row pitch (bytes), padded
-  constexpr int CPR = T_::A_STEP / 16;                 // 16-byte chunks per row per step
-  constexpr int NCH = (BM * CPR + kThreads - 1) / kThreads;  // chunks per thread
-  constexpr int NF = T_::A_FRAG / 16;                  // 16-byte LDS reads per fragment
+  constexpr int PITCH = T_::A_STEP + 16;                     // LDS row pitch (bytes), padded
+  constexpr int CPR = T_::A_STEP / 16;                       // 16-byte chunks per row per step
+  constexpr int NCH = (BM * CPR + kThreads - 1) / kThreads;  // chunks per thread per step
+  constexpr int NF = T_::A_FRAG / 16;                        // 16-byte LDS reads per fragment
+  constexpr int HALF = kNsub / 2;                            // stage 1: gate sub-tiles per wave
 
-  __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * PITCH];
+  __shared__ __attribute__((aligned(16))) uint8_t sA[kStages][BM * PITCH];
   __shared__ int sRow[BM];
   __shared__ float sRed[kWaves][BM];
 
@@ -203,7 +210,7 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_kernel(GemmArgs g) {
 
   for (int wi = w_begin + slot; wi < w_end; wi += per_xcd) {
     const int mt = wi / g.ntiles_n, nt = wi - mt * g.ntiles_n;
-    __syncthreads();  // previous tile's epilogue is done with sRow / sRed
+    __syncthreads();  // previous tile is done with sA / sRow / sRed
     int valid_here = 0;
     if (tid < BM) {
       const int p = g.sorted_pair_ids[mt * BM + tid];
@@ -215,68 +222,68 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_kernel(GemmArgs g) {
     const int mvalid = (nvalid + 15) >> 4;
     const int e = g.tile_expert[mt];
 
-    // Weight rows of this wave's two sub-tiles.
+    // Weight rows of this wave's sub-tiles, as 32-bit offsets from the
+    // expert's base (one expert's weights are far below 4 GiB).
     int nrow[kNsub];
-    if (STAGE == 1) {
-      nrow[0] = nt * kStage1Cols + wave * 16 + lr;
-      nrow[1] = g.I + nrow[0];
-    } else {
-      nrow[0] = nt * kStage2Cols + wave * 32 + lr;
-      nrow[1] = nrow[0] + 16;
-    }
-    const uint8_t* brow[kNsub];
-    const uint8_t* srow[kNsub];
 #pragma unroll
     for (int s = 0; s < kNsub; s++) {
-      const size_t r = (size_t)e * g.N + nrow[s];
-      brow[s] = B + r * kbytes + lq * T_::B_FRAG;
-      if (S == kW4A16) srow[s] = reinterpret_cast<const uint8_t*>(g.b_scale) + r * (K / 32) * 2 + lq * 2;
-      else if (S == kA8W4) srow[s] = reinterpret_cast<const uint8_t*>(g.b_scale) + r * (K / 32) + lq * 2;
-      else srow[s] = nullptr;
+      if (STAGE == 1) {
+        const int base = nt * kStage1Cols + wave * HALF * 16 + lr;
+        nrow[s] = s < HALF ? base + s * 16 : g.I + base + (s - HALF) * 16;
+      } else {
+        nrow[s] = nt * kStage2Cols + wave * kNsub * 16 + s * 16 + lr;
+      }
+    }
+    constexpr int SB = S == kW4A16 ? 2 : 1;  // scale bytes (w4a16 fp16, a8w4 e8m0)
+    const uint8_t* __restrict__ Bexp = B + (size_t)e * g.N * kbytes;
+    const uint8_t* __restrict__ Sexp =
+        reinterpret_cast<const uint8_t*>(g.b_scale) + (size_t)e * g.N * (K / 32) * SB;
+    uint32_t boff[kNsub], soff[kNsub];
+#pragma unroll
+    for (int s = 0; s < kNsub; s++) {
+      boff[s] = (uint32_t)nrow[s] * (uint32_t)kbytes + lq * T_::B_FRAG;
+      soff[s] = (uint32_t)nrow[s] * (uint32_t)(K / 32) * SB + lq * 2;
     }
 
-    auto load_b = [&](BFrag<S>* bf, int ks) {
+    auto load_b = [&](BFrag<S>(&bf)[kNsub], int ks) __attribute__((always_inline)) {
 #pragma unroll
       for (int s = 0; s < kNsub; s++) {
-        const uint4* p = reinterpret_cast<const uint4*>(brow[s] + (size_t)ks * T_::B_STEP);
+        const u32x4* p =
+            reinterpret_cast<const u32x4*>(Bexp + boff[s] + (uint32_t)ks * T_::B_STEP);
 #pragma unroll
         for (int i = 0; i < T_::B_FRAG / 16; i++) bf[s].q[i] = p[i];
-        if (S == kW4A16) {
-          bf[s].sc = *reinterpret_cast<const unsigned short*>(srow[s] + (size_t)ks * 8);
-        } else if (S == kA8W4) {
-          bf[s].sc = *reinterpret_cast<const unsigned short*>(srow[s] + (size_t)ks * 8);
-        } else {
+        if (S == kW4A16 || S == kA8W4)
+          bf[s].sc = *reinterpret_cast<const unsigned short*>(Sexp + soff[s] + (uint32_t)ks * 8);
+        else
           bf[s].sc = 0;
-        }
       }
     };
 
-    uint4 areg[NCH];
-    auto load_a = [&](int ks) {
+    // Activation chunks of this thread: fixed rows per tile.  Rows past the
+    // tile's last real row read that row again (their results are dropped),
+    // so every load is in bounds without a branch.
+    uint32_t aoff[NCH];
 #pragma unroll
-      for (int i = 0; i < NCH; i++) {
-        const int c = tid + i * kThreads;
-        const int row = c / CPR, col = c - row * CPR;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (c < BM * CPR && row < nvalid) {
-          const int ri = sRow[row];
-          const uint8_t* src;
-          if (STAGE == 1)
-            src = A + (size_t)ri * g.H * T_::A_ELEM;
-          else
-            src = A + (size_t)(mt * BM + row) * g.I * T_::A_ELEM;
-          v = *reinterpret_cast<const uint4*>(src + (size_t)ks * T_::A_STEP + col * 16);
-        }
-        areg[i] = v;
-      }
+    for (int i = 0; i < NCH; i++) {
+      const int c = min(tid + i * kThreads, BM * CPR - 1);
+      const int row = min(c / CPR, nvalid - 1), col = c % CPR;
+      const uint32_t rbase = STAGE == 1 ? (uint32_t)sRow[row] * (uint32_t)(g.H * T_::A_ELEM)
+                                        : (uint32_t)(mt * BM + row) * (uint32_t)(g.I * T_::A_ELEM);
+      aoff[i] = rbase + col * 16;
+    }
+    u32x4 areg[NCH];
+    auto load_a = [&](int ks) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < NCH; i++)
+        areg[i] = *reinterpret_cast<const u32x4*>(A + aoff[i] + (uint32_t)ks * T_::A_STEP);
     };
-    auto store_a = [&](int buf) {
+    auto store_a = [&](int stage) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < NCH; i++) {
         const int c = tid + i * kThreads;
         const int row = c / CPR, col = c - row * CPR;
-        if (c < BM * CPR && row < mvalid * 16)
-          *reinterpret_cast<uint4*>(&sA[buf][row * PITCH + col * 16]) = areg[i];
+        if (NCH * kThreads == BM * CPR || c < BM * CPR)
+          *reinterpret_cast<u32x4*>(&sA[stage][row * PITCH + col * 16]) = areg[i];
       }
     };
 
@@ -286,90 +293,145 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int s = 0; s < kNsub; s++) acc[m][s] = Acc{0, 0, 0, 0};
 
-    BFrag<S> bcur[kNsub], bnext[kNsub];
-    load_a(0);
-    load_b(bcur, 0);
-    store_a(0);
-    __syncthreads();
-    for (int ks = 0; ks < nsteps; ks++) {
-      const int cur = ks & 1;
-      const bool more = ks + 1 < nsteps;
-      if (more) {
-        load_a(ks + 1);
-        load_b(bnext, ks + 1);
-      }
+    // Activation fragments are read from LDS one 16-row group ahead of the
+    // MFMAs that use them; the scheduling fences keep the compiler from
+    // hoisting every group's reads (which would need ~8x the registers).
+    auto read_frag = [&](u32x4(&af)[NF], int stage, int m) __attribute__((always_inline)) {
+      const uint8_t* src = &sA[stage][(m * 16 + lr) * PITCH];
+#pragma unroll
+      for (int f = 0; f < NF; f++)
+        af[f] = *reinterpret_cast<const u32x4*>(src + a_frag_offset<S>(lq, f));
+    };
+    auto compute = [&](int stage, const BFrag<S>(&bc)[kNsub]) __attribute__((always_inline)) {
+      u32x4 fa[NF], fb[NF];
+      read_frag(fa, stage, 0);
 #pragma unroll
       for (int m = 0; m < MSUB; m++) {
         if (m < mvalid) {
-          uint4 af[NF];
-          const uint8_t* src = &sA[cur][(m * 16 + lr) * PITCH];
+          if (m + 1 < MSUB && m + 1 < mvalid) read_frag((m & 1) ? fa : fb, stage, m + 1);
 #pragma unroll
-          for (int f = 0; f < NF; f++)
-            af[f] = *reinterpret_cast<const uint4*>(src + a_frag_offset<S>(lq, f));
-#pragma unroll
-          for (int s = 0; s < kNsub; s++) mfma_step<S>(acc[m][s], af, bcur[s]);
+          for (int s = 0; s < kNsub; s++) mfma_step<S>(acc[m][s], (m & 1) ? fb : fa, bc[s]);
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      if (more) {
-        store_a(cur ^ 1);
-#pragma unroll
-        for (int s = 0; s < kNsub; s++) bcur[s] = bnext[s];
+    };
+
+    // K loop: step s computes from LDS slot s%3, while the activation rows
+    // of step s+1 are written to LDS and those of step s+2 are in flight.
+    // Weights are loaded BPRE steps ahead into a ring of BPRE+1 register sets.
+    const int n = nsteps;
+    load_a(0);
+    store_a(0);
+    if (n > 1) load_a(1);
+    if constexpr (BPRE == 2) {
+      BFrag<S> b0[kNsub], b1[kNsub], b2[kNsub];
+      auto step = [&](int s, const BFrag<S>(&bc)[kNsub], BFrag<S>(&bl)[kNsub]) __attribute__((always_inline)) {
+        if (s >= n) return;
+        if (s + 1 < n) store_a((s + 1) % kStages);
+        if (s + 2 < n) {
+          load_a(s + 2);
+          load_b(bl, s + 2);
+        }
+        __syncthreads();
+        compute(s % kStages, bc);
+      };
+      load_b(b0, 0);
+      if (n > 1) load_b(b1, 1);
+      for (int s = 0; s < n; s += 3) {
+        step(s, b0, b2);
+        step(s + 1, b1, b0);
+        step(s + 2, b2, b1);
       }
-      __syncthreads();
+    } else {
+      BFrag<S> b0[kNsub], b1[kNsub];
+      auto step = [&](int s, const BFrag<S>(&bc)[kNsub], BFrag<S>(&bl)[kNsub]) __attribute__((always_inline)) {
+        if (s >= n) return;
+        if (s + 1 < n) {
+          store_a((s + 1) % kStages);
+          load_b(bl, s + 1);
+        }
+        if (s + 2 < n) load_a(s + 2);
+        __syncthreads();
+        compute(s % kStages, bc);
+      };
+      load_b(b0, 0);
+      for (int s = 0; s < n; s += 2) {
+        step(s, b0, b1);
+        step(s + 1, b1, b0);
+      }
     }
 
     // ------------------------------------------------------------ epilogue
     if (STAGE == 1) {
-      const int col = nt * kStage1Cols + wave * 16 + lr;
-      float ws_g = 1.f, ws_u = 1.f;
-      if (S == kW8A8) {
-        const float* ws = reinterpret_cast<const float*>(g.b_scale) + (size_t)e * g.N;
-        ws_g = ws[col];
-        ws_u = ws[g.I + col];
-      }
+      const float* ws = S == kW8A8 ? reinterpret_cast<const float*>(g.b_scale) + (size_t)e * g.N
+                                   : nullptr;
+      float amax[MSUB][4];
 #pragma unroll
-      for (int m = 0; m < MSUB; m++) {
-        if (m < mvalid) {
+      for (int m = 0; m < MSUB; m++)
 #pragma unroll
-          for (int r = 0; r < 4; r++) {
-            const int row = m * 16 + lq * 4 + r;
-            const int tok = sRow[row];
-            const size_t orow = (size_t)mt * BM + row;
-            float gf, uf;
-            if constexpr (S == kW8A8) {
-              const float xs = tok >= 0 ? g.a_scale[tok] : 0.f;
-              gf = ((float)acc[m][0][r] * xs) * ws_g;
-              uf = ((float)acc[m][1][r] * xs) * ws_u;
-              if (g.dump != nullptr && tok >= 0) {
-                g.dump[orow * 2 * g.I + col] = acc[m][0][r];
-                g.dump[orow * 2 * g.I + g.I + col] = acc[m][1][r];
+        for (int r = 0; r < 4; r++) amax[m][r] = 0.f;
+#pragma unroll
+      for (int s = 0; s < HALF; s++) {
+        const int col = nrow[s];
+        float ws_g = 1.f, ws_u = 1.f;
+        if (S == kW8A8) {
+          ws_g = ws[col];
+          ws_u = ws[g.I + col];
+        }
+#pragma unroll
+        for (int m = 0; m < MSUB; m++) {
+          if (m < mvalid) {
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+              const int row = m * 16 + lq * 4 + r;
+              const int tok = sRow[row];
+              const size_t orow = (size_t)mt * BM + row;
+              float gf, uf;
+              if constexpr (S == kW8A8) {
+                const float xs = tok >= 0 ? g.a_scale[tok] : 0.f;
+                gf = ((float)acc[m][s][r] * xs) * ws_g;
+                uf = ((float)acc[m][s + HALF][r] * xs) * ws_u;
+                if (g.dump != nullptr && tok >= 0) {
+                  g.dump[orow * 2 * g.I + col] = acc[m][s][r];
+                  g.dump[orow * 2 * g.I + g.I + col] = acc[m][s + HALF][r];
+                }
+              } else if constexpr (S == kA8W4) {
+                const float xs = tok >= 0 ? g.a_scale[tok] : 0.f;
+                gf = acc[m][s][r] * xs;
+                uf = acc[m][s + HALF][r] * xs;
+              } else {
+                gf = acc[m][s][r];
+                uf = acc[m][s + HALF][r];
               }
-            } else if constexpr (S == kA8W4) {
-              const float xs = tok >= 0 ? g.a_scale[tok] : 0.f;
-              gf = acc[m][0][r] * xs;
-              uf = acc[m][1][r] * xs;
-            } else {
-              gf = acc[m][0][r];
-              uf = acc[m][1][r];
-            }
-            const float h = tok >= 0 ? silu_mul<S>(gf, uf) : 0.f;
-            if constexpr (S == kW4A16) {
-              if (tok >= 0)
-                reinterpret_cast<__bf16*>(g.out)[orow * g.I + col] = (__bf16)h;
-            } else {
-              if (tok >= 0) reinterpret_cast<float*>(g.out)[orow * g.I + col] = h;
-              float a = fabsf(h);
-#pragma unroll
-              for (int off = 1; off < 16; off <<= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
-              if (lr == 0) sRed[wave][row] = a;
+              const float h = tok >= 0 ? silu_mul<S>(gf, uf) : 0.f;
+              if constexpr (S == kW4A16) {
+                if (tok >= 0) reinterpret_cast<__bf16*>(g.out)[orow * g.I + col] = (__bf16)h;
+              } else {
+                if (tok >= 0) reinterpret_cast<float*>(g.out)[orow * g.I + col] = h;
+                amax[m][r] = fmaxf(amax[m][r], fabsf(h));
+              }
             }
           }
         }
       }
       if constexpr (S != kW4A16) {
+#pragma unroll
+        for (int m = 0; m < MSUB; m++) {
+          if (m < mvalid) {
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+              float a = amax[m][r];
+#pragma unroll
+              for (int off = 1; off < 16; off <<= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
+              if (lr == 0) sRed[wave][m * 16 + lq * 4 + r] = a;
+            }
+          }
+        }
         __syncthreads();
         if (tid < mvalid * 16) {
-          const float a = fmaxf(fmaxf(sRed[0][tid], sRed[1][tid]), fmaxf(sRed[2][tid], sRed[3][tid]));
+          float a = sRed[0][tid];
+#pragma unroll
+          for (int w = 1; w < kWaves; w++) a = fmaxf(a, sRed[w][tid]);
           g.row_pmax[((size_t)mt * BM + tid) * g.ntiles_n + nt] = a;
         }
       }
@@ -406,12 +468,12 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_kernel(GemmArgs g) {
   }
 }
 
-template <int S, int STAGE, int BM>
+template <int S, int STAGE, int BM, int BPRE = 2>
 hipError_t launch_one(const GemmArgs& g, hipStream_t s) {
   static int blocks_per_cu = 0;
   if (blocks_per_cu == 0) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, moe_gemm_kernel<S, STAGE, BM>, kThreads,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, moe_gemm_kernel<S, STAGE, BM, BPRE>, kThreads,
                                                      0) != hipSuccess ||
         n < 1)
       n = 1;
@@ -419,7 +481,7 @@ hipError_t launch_one(const GemmArgs& g, hipStream_t s) {
   }
   int nblk = device_cu_count() * blocks_per_cu;
   nblk = nblk < 8 ? 8 : (nblk / 8) * 8;
-  hipLaunchKernelGGL((moe_gemm_kernel<S, STAGE, BM>), dim3(nblk), dim3(kThreads), 0, s, g);
+  hipLaunchKernelGGL((moe_gemm_kernel<S, STAGE, BM, BPRE>), dim3(nblk), dim3(kThreads), 0, s, g);
   return hipGetLastError();
 }
 

@@ -5,13 +5,15 @@
 
 namespace qmoe {
 
-// Tile geometry of the grouped GEMMs (both stages).  256 threads = 4 waves of
-// 64; every wave owns NSUB 16-column sub-tiles and all BM rows of the tile.
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
+// Tile geometry of the grouped GEMMs (both stages).  512 threads = 8 waves of
+// 64 (two per SIMD); every wave owns kNsub 16-column weight sub-tiles and all
+// BM rows of the tile, so a block covers 256 weight rows.
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
 constexpr int kNsub = 2;
-constexpr int kStage1Cols = 64;   // h columns per stage-1 tile (64 gate + 64 up rows)
-constexpr int kStage2Cols = 128;  // output columns per stage-2 tile
+constexpr int kStages = 3;                           // pipeline depth (K steps in flight)
+constexpr int kStage1Cols = kWaves * kNsub * 16 / 2;  // h columns per stage-1 tile (128)
+constexpr int kStage2Cols = kWaves * kNsub * 16;      // output columns per stage-2 tile (256)
 
 struct GemmArgs {
   int T, H, I, E, k, P;  // P = T*k pairs
