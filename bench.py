@@ -117,6 +117,9 @@ def main():
     ap.add_argument("--block-m", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB "
+                         "(--steps times); used to scale the FETCH_SIZE/WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
@@ -124,6 +127,19 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / args.steps
+        print(json.dumps({"copy_bytes": n, "ms": dt * 1e3, "GBps_read": n / dt / 1e9}))
+        return
 
     from quantized_mixture_experts_moe_amd import ops, synth
     from quantized_mixture_experts_moe_amd.shapes import default_block_m, shape_by_name

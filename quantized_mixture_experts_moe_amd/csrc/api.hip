@@ -6,7 +6,7 @@
 #include <algorithm>
 #include <mutex>
 
-#include "../../include/qmoe.h"
+#include "qmoe.h"
 #include "qmoe_internal.h"
 
 namespace qmoe {

@@ -60,6 +60,10 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 enum { kW4A16 = 0, kW8A8 = 1, kA8W4 = 2 };
 
+// s_waitcnt immediate (gfx9 encoding) waiting for vmcnt == 0 only:
+// vmcnt bits [3:0] and [15:14] = 0, expcnt [6:4] = 7, lgkmcnt [11:8] = 15.
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 template <int S>
 struct Tr;
 template <>
@@ -177,7 +181,7 @@ __device__ inline float silu_mul(float g, float u) {
   return sg * u;
 }
 
-template <int S, int STAGE, int BM, int BPRE>
+template <int S, int STAGE, int BM>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 moe_gemm_kernel(GemmArgs g) {
   using T_ = Tr<S>;
@@ -189,9 +193,17 @@ moe_gemm_kernel(GemmArgs g) {
   constexpr int NF = T_::A_FRAG / 16;                        // 16-byte LDS reads per fragment
   constexpr int HALF = kNsub / 2;                            // stage 1: gate sub-tiles per wave
 
-  __shared__ __attribute__((aligned(16))) uint8_t sA[kStages][BM * PITCH];
+  // Epilogue tile: the block's BM x COLS outputs, staged in LDS (over the
+  // activation ring) so that global stores are 16 contiguous bytes per lane.
+  constexpr int COLS = STAGE == 1 ? kStage1Cols : kStage2Cols;
+  constexpr int OUT_ES = STAGE == 1 ? (S == kW4A16 ? 2 : 4) : (S == kW8A8 ? 4 : 2);
+  constexpr int EPITCH = COLS * OUT_ES + 16;
+  constexpr int RING = kStages * BM * PITCH;
+  constexpr int SMEM = RING > BM * EPITCH ? RING : BM * EPITCH;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
   __shared__ int sRow[BM];
-  __shared__ float sRed[kWaves][BM];
+  __shared__ float sScale[BM];
+  auto sA = [&](int stage) __attribute__((always_inline)) { return smem + stage * BM * PITCH; };
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lq = lane >> 4;
@@ -202,25 +214,46 @@ moe_gemm_kernel(GemmArgs g) {
   const int chunk = (total + 7) >> 3;
   const int w_begin = xcd * chunk, w_end = min(total, w_begin + chunk);
 
+  static_assert(kThreads % CPR == 0, "chunk rows must be thread-invariant");
+  const int lds_w = (tid / CPR) * PITCH + (tid % CPR) * 16;  // this thread's LDS store slot
   const size_t K = (size_t)g.K;
   const size_t kbytes = K * T_::KB_NUM / T_::KB_DEN;  // weight bytes per row
   const int nsteps = g.K / T_::BK;
   const uint8_t* __restrict__ A = reinterpret_cast<const uint8_t*>(g.a);
   const uint8_t* __restrict__ B = reinterpret_cast<const uint8_t*>(g.b);
 
+  // Tile metadata (pair ids of the rows, the expert) is fetched one tile
+  // ahead, so a tile starts without waiting on those loads.
+  int next_pair = g.P, next_expert = 0;
+  auto fetch_meta = [&](int w) __attribute__((always_inline)) {
+    if (w < w_end) {
+      const int m = w / g.ntiles_n;
+      if (tid < BM) next_pair = g.sorted_pair_ids[m * BM + tid];
+      next_expert = g.tile_expert[m];
+    }
+  };
+  fetch_meta(w_begin + slot);
   for (int wi = w_begin + slot; wi < w_end; wi += per_xcd) {
     const int mt = wi / g.ntiles_n, nt = wi - mt * g.ntiles_n;
-    __syncthreads();  // previous tile is done with sA / sRow / sRed
+    __syncthreads();  // previous tile is done with the LDS tiles and sRow / sScale
+    const int e = next_expert;
     int valid_here = 0;
+    float row_scale = 0.f;
     if (tid < BM) {
-      const int p = g.sorted_pair_ids[mt * BM + tid];
+      const int p = next_pair;
       const bool ok = p < g.P;
-      sRow[tid] = ok ? (STAGE == 1 ? p / g.k : p) : -1;
+      const int ri = ok ? (STAGE == 1 ? p / g.k : p) : -1;
+      sRow[tid] = ri;
       valid_here = ok;
+      // Per-row scale used by the epilogue (token scale in stage 1, the
+      // requantized h scale in stage 2); written to LDS after the K loop, so
+      // the load's latency is covered by the loop.
+      if constexpr (S != kW4A16)
+        row_scale = ok ? g.a_scale[STAGE == 1 ? ri : (size_t)mt * BM + tid] : 0.f;
     }
     const int nvalid = __syncthreads_count(valid_here);
     const int mvalid = (nvalid + 15) >> 4;
-    const int e = g.tile_expert[mt];
+    fetch_meta(wi + per_xcd);
 
     // Weight rows of this wave's sub-tiles, as 32-bit offsets from the
     // expert's base (one expert's weights are far below 4 GiB).
@@ -245,15 +278,17 @@ moe_gemm_kernel(GemmArgs g) {
       soff[s] = (uint32_t)nrow[s] * (uint32_t)(K / 32) * SB + lq * 2;
     }
 
+    // Every address below is a wave-uniform base plus one 32-bit per-lane
+    // offset, so the loads use the scalar-base + 32-bit-offset form.
     auto load_b = [&](BFrag<S>(&bf)[kNsub], int ks) __attribute__((always_inline)) {
 #pragma unroll
       for (int s = 0; s < kNsub; s++) {
-        const u32x4* p =
-            reinterpret_cast<const u32x4*>(Bexp + boff[s] + (uint32_t)ks * T_::B_STEP);
+        const uint32_t o = boff[s] + (uint32_t)ks * T_::B_STEP;
 #pragma unroll
-        for (int i = 0; i < T_::B_FRAG / 16; i++) bf[s].q[i] = p[i];
+        for (int i = 0; i < T_::B_FRAG / 16; i++)
+          bf[s].q[i] = *reinterpret_cast<const u32x4*>(Bexp + (uint32_t)(o + 16 * i));
         if (S == kW4A16 || S == kA8W4)
-          bf[s].sc = *reinterpret_cast<const unsigned short*>(Sexp + soff[s] + (uint32_t)ks * 8);
+          bf[s].sc = *reinterpret_cast<const unsigned short*>(Sexp + (uint32_t)(soff[s] + ks * 8));
         else
           bf[s].sc = 0;
       }
@@ -265,25 +300,23 @@ moe_gemm_kernel(GemmArgs g) {
     uint32_t aoff[NCH];
 #pragma unroll
     for (int i = 0; i < NCH; i++) {
-      const int c = min(tid + i * kThreads, BM * CPR - 1);
-      const int row = min(c / CPR, nvalid - 1), col = c % CPR;
+      const int row = min(tid / CPR + i * (kThreads / CPR), nvalid - 1), col = tid % CPR;
       const uint32_t rbase = STAGE == 1 ? (uint32_t)sRow[row] * (uint32_t)(g.H * T_::A_ELEM)
                                         : (uint32_t)(mt * BM + row) * (uint32_t)(g.I * T_::A_ELEM);
       aoff[i] = rbase + col * 16;
     }
-    u32x4 areg[NCH];
-    auto load_a = [&](int ks) __attribute__((always_inline)) {
+    auto load_a = [&](u32x4(&ar)[NCH], int ks) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < NCH; i++)
-        areg[i] = *reinterpret_cast<const u32x4*>(A + aoff[i] + (uint32_t)ks * T_::A_STEP);
+        ar[i] = *reinterpret_cast<const u32x4*>(A + (uint32_t)(aoff[i] + ks * T_::A_STEP));
     };
-    auto store_a = [&](int stage) __attribute__((always_inline)) {
+    // Chunk i of this thread lands at LDS row (tid/CPR + i*kThreads/CPR).
+    auto store_a = [&](const u32x4(&ar)[NCH], int stage) __attribute__((always_inline)) {
+      uint8_t* dst = sA(stage) + lds_w;
 #pragma unroll
       for (int i = 0; i < NCH; i++) {
-        const int c = tid + i * kThreads;
-        const int row = c / CPR, col = c - row * CPR;
-        if (NCH * kThreads == BM * CPR || c < BM * CPR)
-          *reinterpret_cast<u32x4*>(&sA[stage][row * PITCH + col * 16]) = areg[i];
+        if (NCH * kThreads == BM * CPR || tid + i * kThreads < BM * CPR)
+          *reinterpret_cast<u32x4*>(dst + i * (kThreads / CPR) * PITCH) = ar[i];
       }
     };
 
@@ -297,106 +330,102 @@ moe_gemm_kernel(GemmArgs g) {
     // MFMAs that use them; the scheduling fences keep the compiler from
     // hoisting every group's reads (which would need ~8x the registers).
     auto read_frag = [&](u32x4(&af)[NF], int stage, int m) __attribute__((always_inline)) {
-      const uint8_t* src = &sA[stage][(m * 16 + lr) * PITCH];
+      const uint8_t* src = sA(stage) + (m * 16 + lr) * PITCH;
 #pragma unroll
       for (int f = 0; f < NF; f++)
         af[f] = *reinterpret_cast<const u32x4*>(src + a_frag_offset<S>(lq, f));
     };
+    // With FRAG2 the reads run one group ahead (two fragment buffers);
+    // otherwise each group's reads directly precede its MFMAs and the other
+    // wave on the SIMD covers the LDS latency.
+    constexpr bool FRAG2 = !(S == kA8W4 && BM >= 128);
     auto compute = [&](int stage, const BFrag<S>(&bc)[kNsub]) __attribute__((always_inline)) {
       u32x4 fa[NF], fb[NF];
-      read_frag(fa, stage, 0);
+      if constexpr (FRAG2) read_frag(fa, stage, 0);
 #pragma unroll
       for (int m = 0; m < MSUB; m++) {
         if (m < mvalid) {
-          if (m + 1 < MSUB && m + 1 < mvalid) read_frag((m & 1) ? fa : fb, stage, m + 1);
+          if constexpr (FRAG2) {
+            if (m + 1 < MSUB && m + 1 < mvalid) read_frag((m & 1) ? fa : fb, stage, m + 1);
 #pragma unroll
-          for (int s = 0; s < kNsub; s++) mfma_step<S>(acc[m][s], (m & 1) ? fb : fa, bc[s]);
+            for (int s = 0; s < kNsub; s++) mfma_step<S>(acc[m][s], (m & 1) ? fb : fa, bc[s]);
+          } else {
+            read_frag(fa, stage, m);
+#pragma unroll
+            for (int s = 0; s < kNsub; s++) mfma_step<S>(acc[m][s], fa, bc[s]);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
     };
 
-    // K loop: step s computes from LDS slot s%3, while the activation rows
-    // of step s+1 are written to LDS and those of step s+2 are in flight.
-    // Weights are loaded BPRE steps ahead into a ring of BPRE+1 register sets.
+    // K loop.  Step s computes from LDS slot s%2 and weight register set
+    // s%3.  Weights are loaded two steps ahead; the activation rows of step
+    // s+1 (loaded one step ahead into registers) are written to the other
+    // LDS slot after the MFMAs, then one barrier.  Within a step the weight
+    // loads are issued before the activation loads, so waiting for the
+    // activations never waits for younger weight loads (load counters
+    // complete in order).  Loads past the last step re-read the last step
+    // (cache hits): every step has the same shape and the compiler's counter
+    // waits stay exact.
     const int n = nsteps;
-    load_a(0);
-    store_a(0);
-    if (n > 1) load_a(1);
-    if constexpr (BPRE == 2) {
-      BFrag<S> b0[kNsub], b1[kNsub], b2[kNsub];
-      auto step = [&](int s, const BFrag<S>(&bc)[kNsub], BFrag<S>(&bl)[kNsub]) __attribute__((always_inline)) {
-        if (s >= n) return;
-        if (s + 1 < n) store_a((s + 1) % kStages);
-        if (s + 2 < n) {
-          load_a(s + 2);
-          load_b(bl, s + 2);
-        }
-        __syncthreads();
-        compute(s % kStages, bc);
-      };
-      load_b(b0, 0);
-      if (n > 1) load_b(b1, 1);
-      for (int s = 0; s < n; s += 3) {
-        step(s, b0, b2);
-        step(s + 1, b1, b0);
-        step(s + 2, b2, b1);
-      }
-    } else {
-      BFrag<S> b0[kNsub], b1[kNsub];
-      auto step = [&](int s, const BFrag<S>(&bc)[kNsub], BFrag<S>(&bl)[kNsub]) __attribute__((always_inline)) {
-        if (s >= n) return;
-        if (s + 1 < n) {
-          store_a((s + 1) % kStages);
-          load_b(bl, s + 1);
-        }
-        if (s + 2 < n) load_a(s + 2);
-        __syncthreads();
-        compute(s % kStages, bc);
-      };
-      load_b(b0, 0);
-      for (int s = 0; s < n; s += 2) {
-        step(s, b0, b1);
-        step(s + 1, b1, b0);
-      }
+    u32x4 ar[NCH];
+    BFrag<S> b0[kNsub], b1[kNsub], b2[kNsub];
+    auto step = [&](int s, const BFrag<S>(&bc)[kNsub], BFrag<S>(&bl)[kNsub])
+        __attribute__((always_inline)) {
+      load_b(bl, min(s + 2, n - 1));
+      if (s < n) compute(s & 1, bc);
+      store_a(ar, (s + 1) & 1);
+      load_a(ar, min(s + 2, n - 1));
+      __syncthreads();
+    };
+    load_a(ar, 0);
+    load_b(b0, 0);
+    load_b(b1, min(1, n - 1));
+    // The previous tile's output stores are still in flight.  On gfx9 stores
+    // and loads share one counter, and pending stores would turn every wait
+    // of the pipelined loop into a full drain; drain them here, where the
+    // wait for this tile's first loads has to happen anyway.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    store_a(ar, 0);
+    load_a(ar, min(1, n - 1));
+    __syncthreads();
+    for (int s = 0; s < n; s += 3) {
+      step(s, b0, b2);
+      step(s + 1, b1, b0);
+      step(s + 2, b2, b1);
     }
 
     // ------------------------------------------------------------ epilogue
-    if (STAGE == 1) {
-      const float* ws = S == kW8A8 ? reinterpret_cast<const float*>(g.b_scale) + (size_t)e * g.N
-                                   : nullptr;
-      float amax[MSUB][4];
+    // Phase 1: registers -> LDS tile (row = tile row, column = the block's
+    // output column), after every wave is done with the activation ring.
+    if (S != kW4A16 && tid < BM) sScale[tid] = row_scale;
+    __syncthreads();
 #pragma unroll
-      for (int m = 0; m < MSUB; m++)
+    for (int m = 0; m < MSUB; m++) {
+      if (m < mvalid) {
 #pragma unroll
-        for (int r = 0; r < 4; r++) amax[m][r] = 0.f;
+        for (int r = 0; r < 4; r++) {
+          const int row = m * 16 + lq * 4 + r;
+          const size_t orow = (size_t)mt * BM + row;
+          uint8_t* trow = smem + row * EPITCH;
+          if constexpr (STAGE == 1) {
+            const int tok = sRow[row];
 #pragma unroll
-      for (int s = 0; s < HALF; s++) {
-        const int col = nrow[s];
-        float ws_g = 1.f, ws_u = 1.f;
-        if (S == kW8A8) {
-          ws_g = ws[col];
-          ws_u = ws[g.I + col];
-        }
-#pragma unroll
-        for (int m = 0; m < MSUB; m++) {
-          if (m < mvalid) {
-#pragma unroll
-            for (int r = 0; r < 4; r++) {
-              const int row = m * 16 + lq * 4 + r;
-              const int tok = sRow[row];
-              const size_t orow = (size_t)mt * BM + row;
+            for (int s = 0; s < HALF; s++) {
+              const int cl = wave * HALF * 16 + s * 16 + lr;  // h column inside the tile
               float gf, uf;
               if constexpr (S == kW8A8) {
-                const float xs = tok >= 0 ? g.a_scale[tok] : 0.f;
-                gf = ((float)acc[m][s][r] * xs) * ws_g;
-                uf = ((float)acc[m][s + HALF][r] * xs) * ws_u;
+                const float* ws = reinterpret_cast<const float*>(g.b_scale) + (size_t)e * g.N;
+                const float xs = sScale[row];
+                gf = ((float)acc[m][s][r] * xs) * ws[nrow[s]];
+                uf = ((float)acc[m][s + HALF][r] * xs) * ws[nrow[s + HALF]];
                 if (g.dump != nullptr && tok >= 0) {
-                  g.dump[orow * 2 * g.I + col] = acc[m][s][r];
-                  g.dump[orow * 2 * g.I + g.I + col] = acc[m][s + HALF][r];
+                  g.dump[orow * 2 * g.I + nrow[s]] = acc[m][s][r];
+                  g.dump[orow * 2 * g.I + nrow[s + HALF]] = acc[m][s + HALF][r];
                 }
               } else if constexpr (S == kA8W4) {
-                const float xs = tok >= 0 ? g.a_scale[tok] : 0.f;
+                const float xs = sScale[row];
                 gf = acc[m][s][r] * xs;
                 uf = acc[m][s + HALF][r] * xs;
               } else {
@@ -404,76 +433,74 @@ moe_gemm_kernel(GemmArgs g) {
                 uf = acc[m][s + HALF][r];
               }
               const float h = tok >= 0 ? silu_mul<S>(gf, uf) : 0.f;
-              if constexpr (S == kW4A16) {
-                if (tok >= 0) reinterpret_cast<__bf16*>(g.out)[orow * g.I + col] = (__bf16)h;
-              } else {
-                if (tok >= 0) reinterpret_cast<float*>(g.out)[orow * g.I + col] = h;
-                amax[m][r] = fmaxf(amax[m][r], fabsf(h));
-              }
+              if constexpr (S == kW4A16)
+                *reinterpret_cast<__bf16*>(trow + cl * 2) = (__bf16)h;
+              else
+                *reinterpret_cast<float*>(trow + cl * 4) = h;
             }
-          }
-        }
-      }
-      if constexpr (S != kW4A16) {
+          } else {
+            const int pair = sRow[row];
+            float rs = 1.f;
+            if constexpr (S != kW4A16) rs = sScale[row];
 #pragma unroll
-        for (int m = 0; m < MSUB; m++) {
-          if (m < mvalid) {
-#pragma unroll
-            for (int r = 0; r < 4; r++) {
-              float a = amax[m][r];
-#pragma unroll
-              for (int off = 1; off < 16; off <<= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
-              if (lr == 0) sRed[wave][m * 16 + lq * 4 + r] = a;
-            }
-          }
-        }
-        __syncthreads();
-        if (tid < mvalid * 16) {
-          float a = sRed[0][tid];
-#pragma unroll
-          for (int w = 1; w < kWaves; w++) a = fmaxf(a, sRed[w][tid]);
-          g.row_pmax[((size_t)mt * BM + tid) * g.ntiles_n + nt] = a;
-        }
-      }
-    } else {
-#pragma unroll
-      for (int s = 0; s < kNsub; s++) {
-        const int col = nrow[s];
-        float ws2 = 1.f;
-        if (S == kW8A8) ws2 = reinterpret_cast<const float*>(g.b_scale)[(size_t)e * g.N + col];
-#pragma unroll
-        for (int m = 0; m < MSUB; m++) {
-          if (m < mvalid) {
-#pragma unroll
-            for (int r = 0; r < 4; r++) {
-              const int row = m * 16 + lq * 4 + r;
-              const int pair = sRow[row];
-              if (pair < 0) continue;
-              const size_t orow = (size_t)mt * BM + row;
+            for (int s = 0; s < kNsub; s++) {
+              const int cl = wave * kNsub * 16 + s * 16 + lr;  // output column inside the tile
               if constexpr (S == kW8A8) {
-                const float y = ((float)acc[m][s][r] * g.a_scale[orow]) * ws2;
-                reinterpret_cast<float*>(g.out)[(size_t)pair * g.H + col] = y;
-                if (g.dump != nullptr) g.dump[orow * g.H + col] = acc[m][s][r];
+                const float ws2 =
+                    reinterpret_cast<const float*>(g.b_scale)[(size_t)e * g.N + nrow[s]];
+                *reinterpret_cast<float*>(trow + cl * 4) = ((float)acc[m][s][r] * rs) * ws2;
+                if (g.dump != nullptr && pair >= 0) g.dump[orow * g.H + nrow[s]] = acc[m][s][r];
               } else if constexpr (S == kA8W4) {
-                const float y = acc[m][s][r] * g.a_scale[orow];
-                reinterpret_cast<__bf16*>(g.out)[(size_t)pair * g.H + col] = (__bf16)y;
+                *reinterpret_cast<__bf16*>(trow + cl * 2) = (__bf16)(acc[m][s][r] * rs);
               } else {
-                reinterpret_cast<__bf16*>(g.out)[(size_t)pair * g.H + col] = (__bf16)acc[m][s][r];
+                *reinterpret_cast<__bf16*>(trow + cl * 2) = (__bf16)acc[m][s][r];
               }
             }
           }
         }
       }
     }
+    __syncthreads();
+    // Phase 2: LDS tile -> global, 16 bytes per lane along each output row;
+    // stage 1 of the requantized schemes also reduces each row's |h| max.
+    {
+      constexpr int CPRO = COLS * OUT_ES / 16;  // 16-byte chunks per output row
+      constexpr int RPP = kThreads / CPRO;      // rows per pass
+      static_assert(CPRO <= 64 && kThreads % CPRO == 0, "row chunks must fit a wave");
+      const int prow = tid / CPRO, chunk = tid % CPRO;
+      uint8_t* __restrict__ O = reinterpret_cast<uint8_t*>(g.out);
+      for (int row0 = 0; row0 < mvalid * 16; row0 += RPP) {
+        const int row = row0 + prow;
+        const bool ok = row < nvalid;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(smem + (row < BM ? row : 0) * EPITCH +
+                                                         chunk * 16);
+        if constexpr (STAGE == 1) {
+          if (ok)
+            *reinterpret_cast<u32x4*>(O + ((size_t)mt * BM + row) * g.I * OUT_ES +
+                                      (size_t)nt * COLS * OUT_ES + chunk * 16) = v;
+          if constexpr (S != kW4A16) {
+            float a = fmaxf(fmaxf(fabsf(__uint_as_float(v.x)), fabsf(__uint_as_float(v.y))),
+                            fmaxf(fabsf(__uint_as_float(v.z)), fabsf(__uint_as_float(v.w))));
+#pragma unroll
+            for (int off = 1; off < CPRO; off <<= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
+            if (ok && chunk == 0) g.row_pmax[((size_t)mt * BM + row) * g.ntiles_n + nt] = a;
+          }
+        } else {
+          if (ok)
+            *reinterpret_cast<u32x4*>(O + (size_t)sRow[row] * g.H * OUT_ES +
+                                      (size_t)nt * COLS * OUT_ES + chunk * 16) = v;
+        }
+      }
+    }
   }
 }
 
-template <int S, int STAGE, int BM, int BPRE = 2>
+template <int S, int STAGE, int BM>
 hipError_t launch_one(const GemmArgs& g, hipStream_t s) {
   static int blocks_per_cu = 0;
   if (blocks_per_cu == 0) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, moe_gemm_kernel<S, STAGE, BM, BPRE>, kThreads,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, moe_gemm_kernel<S, STAGE, BM>, kThreads,
                                                      0) != hipSuccess ||
         n < 1)
       n = 1;
@@ -481,7 +508,7 @@ hipError_t launch_one(const GemmArgs& g, hipStream_t s) {
   }
   int nblk = device_cu_count() * blocks_per_cu;
   nblk = nblk < 8 ? 8 : (nblk / 8) * 8;
-  hipLaunchKernelGGL((moe_gemm_kernel<S, STAGE, BM, BPRE>), dim3(nblk), dim3(kThreads), 0, s, g);
+  hipLaunchKernelGGL((moe_gemm_kernel<S, STAGE, BM>), dim3(nblk), dim3(kThreads), 0, s, g);
   return hipGetLastError();
 }
 

@@ -5,15 +5,17 @@
 
 namespace qmoe {
 
-// Tile geometry of the grouped GEMMs (both stages).  512 threads = 8 waves of
-// 64 (two per SIMD); every wave owns kNsub 16-column weight sub-tiles and all
-// BM rows of the tile, so a block covers 256 weight rows.
-constexpr int kThreads = 512;
+// Tile geometry of the grouped GEMMs (both stages).  A block is 256
+// threads = 4 waves and two blocks share a CU (one wave of each per SIMD),
+// so one block's loads, epilogue and tile set-up overlap the other's MFMAs.
+// Every wave owns kNsub 16-column weight sub-tiles and all BM rows of the
+// tile, so a block covers 128 weight rows.
+constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kNsub = 2;
-constexpr int kStages = 3;                           // pipeline depth (K steps in flight)
-constexpr int kStage1Cols = kWaves * kNsub * 16 / 2;  // h columns per stage-1 tile (128)
-constexpr int kStage2Cols = kWaves * kNsub * 16;      // output columns per stage-2 tile (256)
+constexpr int kStages = 2;                            // LDS slots of the activation ring
+constexpr int kStage1Cols = kWaves * kNsub * 16 / 2;  // h columns per stage-1 tile (64)
+constexpr int kStage2Cols = kWaves * kNsub * 16;      // output columns per stage-2 tile (128)
 
 struct GemmArgs {
   int T, H, I, E, k, P;  // P = T*k pairs
