@@ -12,6 +12,7 @@ Prints one JSON line on stdout; progress goes to stderr.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -27,13 +28,31 @@ METRIC = "grouped MoE FFN TFLOP/s + % MFMA/HBM roofline at M=4096 prefill, 1 GPU
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"a8w4": 5000.0, "w8a8": 5000.0, "w4a16": 2500.0}
 DTYPE = {"a8w4": "fp8e4m3*fp4e2m1", "w8a8": "int8", "w4a16": "bf16"}
-# Counter calibration: HBM bytes per KiB reported by FETCH_SIZE / WRITE_SIZE,
-# from a plain device copy of known size (None until measured).
-FETCH_FACTOR = None
-WRITE_FACTOR = None
-# Stage-1 traffic measured with rocprofv3 --pmc for the current kernel, in
-# bytes per launch (None when the kernel changed after the counters were taken).
-STAGE1_TRAFFIC_BYTES = None
+# Counter calibration: HBM bytes per KiB that FETCH_SIZE / WRITE_SIZE report,
+# measured on a plain 1 GiB device copy (__amd_rocclr_copyBuffer, run with
+# --copy-calibration-mib 1024): FETCH_SIZE reads 524,300 KiB for 1 GiB read,
+# WRITE_SIZE 1,048,576 KiB for 1 GiB written.
+FETCH_FACTOR = 1024 * 2.0
+WRITE_FACTOR = 1024 * 1.0
+# FETCH_SIZE / WRITE_SIZE (KiB per launch, mean of 5 launches) of the
+# dominant kernel on the default workload, and the hash of the kernel sources
+# they were taken with; traffic is reported only while the sources match.
+DOMINANT_COUNTERS = {
+    "kernel": "stage1",
+    "fetch_kib": 1225450.5,
+    "write_kib": 167934.2,
+    "sources_sha256_16": "05844688bada118c",
+}
+KERNEL_SOURCES = ("quantized_mixture_experts_moe_amd/csrc/gemm.hip",
+                  "quantized_mixture_experts_moe_amd/csrc/qmoe_internal.h")
+
+
+def kernel_sources_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def log(*a):
@@ -214,8 +233,10 @@ def main():
     dom = max(("stage1", "stage2", "combine"), key=lambda n: kern[n])
     achieved = ab[dom] / (kern[dom] * 1e-3) / 1e9
     traffic = None
-    if dom == "stage1" and STAGE1_TRAFFIC_BYTES is not None:
-        traffic = STAGE1_TRAFFIC_BYTES
+    c = DOMINANT_COUNTERS
+    if (dom == c["kernel"] and shape.name == "a8w4_large@T4096" and bm == 128
+            and kernel_sources_hash() == c["sources_sha256_16"]):
+        traffic = int(round(c["fetch_kib"] * FETCH_FACTOR + c["write_kib"] * WRITE_FACTOR))
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
             "kernel": f"moe_gemm_kernel {dom} ({shape.scheme}, block_m {bm})",

@@ -7,15 +7,16 @@
 // (aiter PR 6090, Test Plan: stage1 tiles, then stage2 tiles.)
 //
 // Rows are the expert-sorted, block_m-padded pair slots from moe_align; a
-// row tile never straddles two experts.  One workgroup = 8 waves (two per
-// SIMD); each wave owns two 16-column weight sub-tiles (stage 1: the gate
-// column and the up column of the same h column, so silu(gate)*up is formed
-// in registers) and all BM rows.  Weight fragments stream from HBM straight
-// into VGPRs, each weight byte read by exactly one wave, two K steps ahead of
-// the MFMAs (a ring of three register sets); the gathered activation rows go
-// global -> VGPR -> a three-slot LDS ring, loaded two steps ahead and shared
-// by the 8 waves.  One barrier per K step.  16-row groups past the tile's
-// last real row are skipped.
+// row tile never straddles two experts.  One workgroup = 4 waves (one per
+// SIMD), two workgroups per CU; each wave owns two 16-column weight
+// sub-tiles (stage 1: the gate column and the up column of the same h
+// column, so silu(gate)*up is formed in registers) and all BM rows.  Weight
+// fragments stream from HBM straight into VGPRs, each weight byte read by
+// exactly one wave, three K steps ahead of the MFMAs (a ring of four
+// register sets); the gathered activation rows go global -> VGPR -> a
+// two-slot LDS ring, loaded two steps ahead and shared by the 4 waves.  One
+// barrier per K step.  16-row groups past the tile's last real row are
+// skipped.
 //
 // Matrix cores (CDNA4 MFMA), 16x16 output per instruction:
 //   w4a16: v_mfma_f32_16x16x32_bf16, int4 * fp16 group scale rounded to
@@ -360,28 +361,29 @@ moe_gemm_kernel(GemmArgs g) {
     };
 
     // K loop.  Step s computes from LDS slot s%2 and weight register set
-    // s%3.  Weights are loaded two steps ahead; the activation rows of step
-    // s+1 (loaded one step ahead into registers) are written to the other
-    // LDS slot after the MFMAs, then one barrier.  Within a step the weight
-    // loads are issued before the activation loads, so waiting for the
-    // activations never waits for younger weight loads (load counters
-    // complete in order).  Loads past the last step re-read the last step
-    // (cache hits): every step has the same shape and the compiler's counter
-    // waits stay exact.
+    // s%4.  A step first writes the activation rows of step s+1 (loaded one
+    // step earlier) to the other LDS slot, then issues the activation loads
+    // of step s+2 and the weight loads of step s+3, then runs the MFMAs of
+    // step s; one barrier ends the step.  Load counters complete in order,
+    // so this order lets the wait for the activations skip the younger
+    // weight loads, which keep three steps to arrive.  Loads past the last
+    // step re-read the last step (cache hits): every step has the same shape
+    // and the compiler's counter waits stay exact.
     const int n = nsteps;
     u32x4 ar[NCH];
-    BFrag<S> b0[kNsub], b1[kNsub], b2[kNsub];
+    BFrag<S> b0[kNsub], b1[kNsub], b2[kNsub], b3[kNsub];
     auto step = [&](int s, const BFrag<S>(&bc)[kNsub], BFrag<S>(&bl)[kNsub])
         __attribute__((always_inline)) {
-      load_b(bl, min(s + 2, n - 1));
-      if (s < n) compute(s & 1, bc);
       store_a(ar, (s + 1) & 1);
       load_a(ar, min(s + 2, n - 1));
+      load_b(bl, min(s + 3, n - 1));
+      if (s < n) compute(s & 1, bc);
       __syncthreads();
     };
     load_a(ar, 0);
     load_b(b0, 0);
     load_b(b1, min(1, n - 1));
+    load_b(b2, min(2, n - 1));
     // The previous tile's output stores are still in flight.  On gfx9 stores
     // and loads share one counter, and pending stores would turn every wait
     // of the pipelined loop into a full drain; drain them here, where the
@@ -390,10 +392,11 @@ moe_gemm_kernel(GemmArgs g) {
     store_a(ar, 0);
     load_a(ar, min(1, n - 1));
     __syncthreads();
-    for (int s = 0; s < n; s += 3) {
-      step(s, b0, b2);
+    for (int s = 0; s < n; s += 4) {
+      step(s, b0, b3);
       step(s + 1, b1, b0);
       step(s + 2, b2, b1);
+      step(s + 3, b3, b2);
     }
 
     // ------------------------------------------------------------ epilogue
