@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define QMOE_ABI_VERSION 1
+#define QMOE_ABI_VERSION 2
 
 typedef enum {
   QMOE_OK = 0,
@@ -73,6 +73,9 @@ typedef enum { QMOE_DT_BF16 = 0, QMOE_DT_F32 = 1 } qmoe_dtype;
  * accumulators of both projections into the workspace (see
  * qmoe_grouped_ffn_debug_offsets).                                       */
 #define QMOE_FLAG_DUMP_ACC 1u
+/* Flag for qmoe_grouped_ffn: the codes and scales of w13 and w2 are in the
+ * streaming layout written by qmoe_prepack instead of the canonical one.  */
+#define QMOE_FLAG_PREPACKED 2u
 
 typedef struct {
   int32_t scheme;   /* qmoe_scheme                                        */
@@ -94,6 +97,32 @@ typedef struct {
   const void* w2;
   const void* w2_scale;
 } qmoe_weights;
+
+/* ---------------------------------------------------------------------
+ * qmoe_prepack -- rewrite one stacked weight tensor (codes [E,N,K] and its
+ * scales, canonical layout) into the library's streaming layout, once, at
+ * set-up time; qmoe_grouped_ffn reads it when QMOE_FLAG_PREPACKED is set.
+ * It moves bytes only (the values are unchanged) and is not part of a
+ * forward pass.  The pages fix no weight layout beyond the formats; this one
+ * makes every 16-byte load of a 64-lane wave part of one contiguous 1 KiB
+ * run and every scale load part of one 128-byte run.
+ * Let S = weight bytes per row per K step (A8W4: 256 K = 128 B; W8A8: 128 K
+ * = 128 B; W4A16: 128 K = 64 B), F = S/4, KB = bytes per row, G = n/16*16.
+ * Codes: byte b of row n of expert e, with ks = b/S, r = b%S, q = r/F,
+ *   i = (r%F)/16, c = r%16, goes to
+ *   (e*N + G)*KB + ks*16*S + i*1024 + (16*q + n%16)*16 + c.
+ * Scales (A8W4 e8m0 bytes, W4A16 fp16 values; SB = bytes per entry, R =
+ *   K/32*SB bytes per row, BK = K elements per step): for q = 0..3 the 2
+ *   bytes of row n at canonical row offset (ks*BK + q*BK/4)/32*SB (the
+ *   scales of K elements [ks*BK + q*BK/4, ks*BK + (q+1)*BK/4)) go to
+ *   (e*N + G)*R + ks*128 + (16*q + n%16)*2.
+ * W8A8 per-channel fp32 scales are copied unchanged (scales_out may be
+ * NULL for W8A8, then nothing is copied).
+ * codes_out / scales_out have the byte sizes of codes / scales and must not
+ * overlap them.  Requires N % 16 == 0 and K a multiple of 256 (A8W4) or
+ * 128 (W4A16, W8A8).  QMOE_ERR_INVALID_ARG otherwise.                    */
+qmoe_status qmoe_prepack(int32_t scheme, int32_t E, int32_t N, int32_t K, const void* codes,
+                         const void* scales, void* codes_out, void* scales_out, void* stream);
 
 int qmoe_abi_version(void);
 const char* qmoe_status_str(qmoe_status s);

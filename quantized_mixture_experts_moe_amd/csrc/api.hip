@@ -89,7 +89,7 @@ static qmoe_status check_desc(const qmoe_ffn_desc* d) {
   if (d->H % 32 != 0 || d->I % 32 != 0) return QMOE_ERR_INVALID_ARG;
   if (!valid_block_m(d->block_m)) return QMOE_ERR_INVALID_ARG;
   if ((long long)d->T * d->k > (1ll << 30)) return QMOE_ERR_INVALID_ARG;
-  if (d->flags & ~QMOE_FLAG_DUMP_ACC) return QMOE_ERR_INVALID_ARG;
+  if (d->flags & ~(QMOE_FLAG_DUMP_ACC | QMOE_FLAG_PREPACKED)) return QMOE_ERR_INVALID_ARG;
   if (d->E > 1024) return QMOE_ERR_UNSUPPORTED;
   if (d->H % 256 != 0) return QMOE_ERR_UNSUPPORTED;
   if (d->I % (d->scheme == QMOE_A8W4_MXFP4 ? 256 : 128) != 0) return QMOE_ERR_UNSUPPORTED;
@@ -236,7 +236,8 @@ static qmoe_status grouped_ffn_impl(const qmoe_ffn_desc* d, const void* x, const
     return events ? hipEventRecord((hipEvent_t)events[i], s) : hipSuccess;
   };
   hipError_t e = mark(0);
-  if (e == hipSuccess) e = launch_gemm(d->scheme, 1, d->block_m, g1, s);
+  const bool packed = (d->flags & QMOE_FLAG_PREPACKED) != 0;
+  if (e == hipSuccess) e = launch_gemm(d->scheme, 1, d->block_m, packed, g1, s);
   if (e == hipSuccess) e = mark(1);
   if (e != hipSuccess) return hip_status(e);
 
@@ -260,7 +261,7 @@ static qmoe_status grouped_ffn_impl(const qmoe_ffn_desc* d, const void* x, const
   g2.out = y_pairs;
   g2.row_pmax = nullptr;
   g2.dump = dump ? reinterpret_cast<int32_t*>(wsb + lay.acc2) : nullptr;
-  e = launch_gemm(d->scheme, 2, d->block_m, g2, s);
+  e = launch_gemm(d->scheme, 2, d->block_m, packed, g2, s);
   if (e == hipSuccess) e = mark(3);
   return hip_status(e);
 }
@@ -288,6 +289,30 @@ qmoe_status qmoe_grouped_ffn_profiled(const qmoe_ffn_desc* d, const void* x,
     return QMOE_ERR_INVALID_ARG;
   return grouped_ffn_impl(d, x, x_scale, w, sorted_pair_ids, tile_expert, num_padded, y_pairs, ws,
                           ws_bytes, stage_events, stream);
+}
+
+qmoe_status qmoe_prepack(int32_t scheme, int32_t E, int32_t N, int32_t K, const void* codes,
+                         const void* scales, void* codes_out, void* scales_out, void* stream) {
+  if (scheme < 0 || scheme > 2 || E < 1 || N < 1 || K < 1) return QMOE_ERR_INVALID_ARG;
+  if (N % 16 != 0 || K % (scheme == QMOE_A8W4_MXFP4 ? 256 : 128) != 0) return QMOE_ERR_INVALID_ARG;
+  if ((long long)E * N > (1ll << 31)) return QMOE_ERR_INVALID_ARG;
+  if (!codes || !codes_out || !scales) return QMOE_ERR_INVALID_ARG;
+  if (scheme != QMOE_W8A8_PERCHAN && !scales_out) return QMOE_ERR_INVALID_ARG;
+  if (!aligned(codes, 16) || !aligned(codes_out, 16) || !aligned(scales, 4) ||
+      (scales_out && !aligned(scales_out, 4)))
+    return QMOE_ERR_INVALID_ARG;
+  const size_t cb = (size_t)E * N * (scheme == QMOE_W8A8_PERCHAN ? K : K / 2);
+  const size_t sbytes = scheme == QMOE_W8A8_PERCHAN ? (size_t)E * N * 4
+                                                    : (size_t)E * N * (K / 32) * (scheme == 0 ? 2 : 1);
+  auto overlap = [](const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+  };
+  if (overlap(codes, cb, codes_out, cb) ||
+      (scales_out && overlap(scales, sbytes, scales_out, sbytes)))
+    return QMOE_ERR_INVALID_ARG;
+  return hip_status(launch_prepack(scheme, E, N, K, codes, scales, codes_out, scales_out,
+                                   (hipStream_t)stream));
 }
 
 qmoe_status qmoe_combine(const void* y_pairs, int32_t y_dtype, const float* topk_w, int32_t T,

@@ -182,7 +182,7 @@ __device__ inline float silu_mul(float g, float u) {
   return sg * u;
 }
 
-template <int S, int STAGE, int BM>
+template <int S, int STAGE, int BM, bool PK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 moe_gemm_kernel(GemmArgs g) {
   using T_ = Tr<S>;
@@ -272,24 +272,39 @@ moe_gemm_kernel(GemmArgs g) {
     const uint8_t* __restrict__ Bexp = B + (size_t)e * g.N * kbytes;
     const uint8_t* __restrict__ Sexp =
         reinterpret_cast<const uint8_t*>(g.b_scale) + (size_t)e * g.N * (K / 32) * SB;
+    // Canonical layout: lane (lq, lr) reads row nrow's bytes [lq*B_FRAG,
+    // (lq+1)*B_FRAG) of each step and the two scale bytes of that run.
+    // Streaming layout (qmoe_prepack): the 16 rows x step bytes of a sub-tile
+    // are one contiguous block in which the same bytes sit at
+    // i*1024 + lane*16, and the step's scales are 128 contiguous bytes.
     uint32_t boff[kNsub], soff[kNsub];
 #pragma unroll
     for (int s = 0; s < kNsub; s++) {
-      boff[s] = (uint32_t)nrow[s] * (uint32_t)kbytes + lq * T_::B_FRAG;
-      soff[s] = (uint32_t)nrow[s] * (uint32_t)(K / 32) * SB + lq * 2;
+      if constexpr (PK) {
+        const uint32_t g16 = (uint32_t)(nrow[s] - lr);  // first row of the 16-row group
+        boff[s] = g16 * (uint32_t)kbytes + lane * 16;
+        soff[s] = g16 * (uint32_t)(K / 32) * SB + lane * 2;
+      } else {
+        boff[s] = (uint32_t)nrow[s] * (uint32_t)kbytes + lq * T_::B_FRAG;
+        soff[s] = (uint32_t)nrow[s] * (uint32_t)(K / 32) * SB + lq * 2;
+      }
     }
+    constexpr uint32_t B_KS = PK ? 16 * T_::B_STEP : T_::B_STEP;  // code bytes per step
+    constexpr uint32_t B_PIECE = PK ? 1024 : 16;                   // between a lane's pieces
+    constexpr uint32_t S_KS = PK ? 128 : 8;                         // scale bytes per step
 
     // Every address below is a wave-uniform base plus one 32-bit per-lane
     // offset, so the loads use the scalar-base + 32-bit-offset form.
     auto load_b = [&](BFrag<S>(&bf)[kNsub], int ks) __attribute__((always_inline)) {
 #pragma unroll
       for (int s = 0; s < kNsub; s++) {
-        const uint32_t o = boff[s] + (uint32_t)ks * T_::B_STEP;
+        const uint32_t o = boff[s] + (uint32_t)ks * B_KS;
 #pragma unroll
         for (int i = 0; i < T_::B_FRAG / 16; i++)
-          bf[s].q[i] = *reinterpret_cast<const u32x4*>(Bexp + (uint32_t)(o + 16 * i));
+          bf[s].q[i] = *reinterpret_cast<const u32x4*>(Bexp + (uint32_t)(o + B_PIECE * i));
         if (S == kW4A16 || S == kA8W4)
-          bf[s].sc = *reinterpret_cast<const unsigned short*>(Sexp + (uint32_t)(soff[s] + ks * 8));
+          bf[s].sc =
+              *reinterpret_cast<const unsigned short*>(Sexp + (uint32_t)(soff[s] + ks * S_KS));
         else
           bf[s].sc = 0;
       }
@@ -479,8 +494,9 @@ moe_gemm_kernel(GemmArgs g) {
                                                          chunk * 16);
         if constexpr (STAGE == 1) {
           if (ok)
-            *reinterpret_cast<u32x4*>(O + ((size_t)mt * BM + row) * g.I * OUT_ES +
-                                      (size_t)nt * COLS * OUT_ES + chunk * 16) = v;
+            __builtin_nontemporal_store(
+                v, reinterpret_cast<u32x4*>(O + ((size_t)mt * BM + row) * g.I * OUT_ES +
+                                            (size_t)nt * COLS * OUT_ES + chunk * 16));
           if constexpr (S != kW4A16) {
             float a = fmaxf(fmaxf(fabsf(__uint_as_float(v.x)), fabsf(__uint_as_float(v.y))),
                             fmaxf(fabsf(__uint_as_float(v.z)), fabsf(__uint_as_float(v.w))));
@@ -490,52 +506,60 @@ moe_gemm_kernel(GemmArgs g) {
           }
         } else {
           if (ok)
-            *reinterpret_cast<u32x4*>(O + (size_t)sRow[row] * g.H * OUT_ES +
-                                      (size_t)nt * COLS * OUT_ES + chunk * 16) = v;
+            __builtin_nontemporal_store(
+                v, reinterpret_cast<u32x4*>(O + (size_t)sRow[row] * g.H * OUT_ES +
+                                            (size_t)nt * COLS * OUT_ES + chunk * 16));
         }
       }
     }
   }
 }
 
-template <int S, int STAGE, int BM>
+template <int S, int STAGE, int BM, bool PK>
 hipError_t launch_one(const GemmArgs& g, hipStream_t s) {
   static int blocks_per_cu = 0;
   if (blocks_per_cu == 0) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, moe_gemm_kernel<S, STAGE, BM>, kThreads,
-                                                     0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, moe_gemm_kernel<S, STAGE, BM, PK>,
+                                                     kThreads, 0) != hipSuccess ||
         n < 1)
       n = 1;
     blocks_per_cu = n;
   }
   int nblk = device_cu_count() * blocks_per_cu;
   nblk = nblk < 8 ? 8 : (nblk / 8) * 8;
-  hipLaunchKernelGGL((moe_gemm_kernel<S, STAGE, BM>), dim3(nblk), dim3(kThreads), 0, s, g);
+  hipLaunchKernelGGL((moe_gemm_kernel<S, STAGE, BM, PK>), dim3(nblk), dim3(kThreads), 0, s, g);
   return hipGetLastError();
 }
 
-template <int S, int STAGE>
+template <int S, int STAGE, bool PK>
 hipError_t launch_bm(int block_m, const GemmArgs& g, hipStream_t s) {
   switch (block_m) {
-    case 16: return launch_one<S, STAGE, 16>(g, s);
-    case 32: return launch_one<S, STAGE, 32>(g, s);
-    case 64: return launch_one<S, STAGE, 64>(g, s);
-    case 128: return launch_one<S, STAGE, 128>(g, s);
+    case 16: return launch_one<S, STAGE, 16, PK>(g, s);
+    case 32: return launch_one<S, STAGE, 32, PK>(g, s);
+    case 64: return launch_one<S, STAGE, 64, PK>(g, s);
+    case 128: return launch_one<S, STAGE, 128, PK>(g, s);
     default: return hipErrorInvalidValue;
   }
 }
 
+template <int S, int STAGE>
+hipError_t launch_layout(bool packed, int block_m, const GemmArgs& g, hipStream_t s) {
+  return packed ? launch_bm<S, STAGE, true>(block_m, g, s)
+                : launch_bm<S, STAGE, false>(block_m, g, s);
+}
+
 }  // namespace
 
-hipError_t launch_gemm(int scheme, int stage, int block_m, const GemmArgs& g, hipStream_t s) {
+hipError_t launch_gemm(int scheme, int stage, int block_m, bool packed, const GemmArgs& g,
+                       hipStream_t s) {
   switch (scheme * 2 + (stage - 1)) {
-    case 0: return launch_bm<kW4A16, 1>(block_m, g, s);
-    case 1: return launch_bm<kW4A16, 2>(block_m, g, s);
-    case 2: return launch_bm<kW8A8, 1>(block_m, g, s);
-    case 3: return launch_bm<kW8A8, 2>(block_m, g, s);
-    case 4: return launch_bm<kA8W4, 1>(block_m, g, s);
-    case 5: return launch_bm<kA8W4, 2>(block_m, g, s);
+    case 0: return launch_layout<kW4A16, 1>(packed, block_m, g, s);
+    case 1: return launch_layout<kW4A16, 2>(packed, block_m, g, s);
+    case 2: return launch_layout<kW8A8, 1>(packed, block_m, g, s);
+    case 3: return launch_layout<kW8A8, 2>(packed, block_m, g, s);
+    case 4: return launch_layout<kA8W4, 1>(packed, block_m, g, s);
+    case 5: return launch_layout<kA8W4, 2>(packed, block_m, g, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -1,0 +1,89 @@
+// qmoe_prepack: canonical expert weights -> the streaming layout the grouped
+// GEMM reads with QMOE_FLAG_PREPACKED.  Pure byte movement.
+//
+// Canonical: row n of expert e is KB contiguous bytes (K along the row), its
+// scales R contiguous bytes.  Streaming: for each group of 16 rows and each
+// K step, one block of 16*S bytes in which lane L = 16*q + r of a wave finds
+// its F = S/4 bytes of row r (the quarter q of the step's row bytes) as
+// 16-byte pieces at i*1024 + L*16; the two scale bytes of that quarter sit
+// at 128*ks + 2*L of the group's scale block.
+#include "qmoe_internal.h"
+
+namespace qmoe {
+namespace {
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// One thread per 16-byte output piece; grid-stride over all pieces.
+// rows = E*N, KB = bytes per row, S = bytes per row per step.
+__global__ void prepack_codes_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
+                                     size_t rows, int KB, int S) {
+  const size_t per_group = (size_t)KB;  // 16-byte pieces per 16-row group (16*KB bytes)
+  const size_t total = rows / 16 * per_group;
+  const int F = S / 4;
+  for (size_t oc = (size_t)blockIdx.x * blockDim.x + threadIdx.x; oc < total;
+       oc += (size_t)gridDim.x * blockDim.x) {
+    const size_t grp = oc / per_group;
+    const int rem = (int)(oc - grp * per_group);  // piece inside the group
+    const int ks = rem / S, rem2 = rem - ks * S;  // S pieces per step (16*S bytes)
+    const int i = rem2 >> 6, L = rem2 & 63;
+    const int q = L >> 4, r = L & 15;
+    const size_t row = grp * 16 + r;
+    const size_t sb = row * KB + (size_t)ks * S + q * F + i * 16;
+    *reinterpret_cast<u32x4*>(dst + oc * 16) = *reinterpret_cast<const u32x4*>(src + sb);
+  }
+}
+
+// One thread per 2-byte output entry.  R = scale bytes per row, BK = K per
+// step, SB = bytes per scale entry, nsteps = K / BK.
+__global__ void prepack_scales_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
+                                      size_t rows, int R, int BK, int SB, int nsteps) {
+  const size_t per_group = (size_t)nsteps * 64;  // entries per 16-row group
+  const size_t total = rows / 16 * per_group;
+  for (size_t oc = (size_t)blockIdx.x * blockDim.x + threadIdx.x; oc < total;
+       oc += (size_t)gridDim.x * blockDim.x) {
+    const size_t grp = oc / per_group;
+    const int rem = (int)(oc - grp * per_group);
+    const int ks = rem >> 6, L = rem & 63;
+    const int q = L >> 4, r = L & 15;
+    const size_t row = grp * 16 + r;
+    const size_t sb = row * R + (size_t)((ks * BK + q * (BK / 4)) / 32) * SB;
+    *reinterpret_cast<uint16_t*>(dst + oc * 2) = *reinterpret_cast<const uint16_t*>(src + sb);
+  }
+}
+
+int grid_for(size_t total) {
+  const size_t want = (total + 255) / 256;
+  const size_t cap = (size_t)device_cu_count() * 16;
+  return (int)(want < cap ? (want > 0 ? want : 1) : cap);
+}
+
+}  // namespace
+
+hipError_t launch_prepack(int scheme, int E, int N, int K, const void* codes, const void* scales,
+                          void* codes_out, void* scales_out, hipStream_t s) {
+  const size_t rows = (size_t)E * N;
+  const int KB = scheme == 1 ? K : K / 2;          // W8A8 int8, others 4-bit
+  const int BK = scheme == 2 ? 256 : 128;          // K elements per step
+  const int S = scheme == 1 ? BK : BK / 2;         // bytes per row per step
+  const size_t pieces = rows / 16 * KB;
+  hipLaunchKernelGGL(prepack_codes_kernel, dim3(grid_for(pieces)), dim3(256), 0, s,
+                     reinterpret_cast<const uint8_t*>(codes), reinterpret_cast<uint8_t*>(codes_out),
+                     rows, KB, S);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (scheme == 1) {
+    if (scales_out == nullptr) return hipSuccess;
+    return hipMemcpyAsync(scales_out, scales, rows * sizeof(float), hipMemcpyDeviceToDevice, s);
+  }
+  const int SB = scheme == 0 ? 2 : 1;
+  const int R = K / 32 * SB;
+  const int nsteps = K / BK;
+  const size_t entries = rows / 16 * nsteps * 64;
+  hipLaunchKernelGGL(prepack_scales_kernel, dim3(grid_for(entries)), dim3(256), 0, s,
+                     reinterpret_cast<const uint8_t*>(scales),
+                     reinterpret_cast<uint8_t*>(scales_out), rows, R, BK, SB, nsteps);
+  return hipGetLastError();
+}
+
+}  // namespace qmoe

@@ -39,7 +39,10 @@ hipError_t launch_align(const int32_t* ids, int T, int k, int E, int block_m, in
                         int32_t* tile_expert, int32_t* offsets, int32_t* num_padded,
                         int32_t* chunk_counts, int32_t* chunk_flags, int32_t* flags, int cap,
                         hipStream_t s);
-hipError_t launch_gemm(int scheme, int stage, int block_m, const GemmArgs& g, hipStream_t s);
+hipError_t launch_gemm(int scheme, int stage, int block_m, bool packed, const GemmArgs& g,
+                       hipStream_t s);
+hipError_t launch_prepack(int scheme, int E, int N, int K, const void* codes, const void* scales,
+                          void* codes_out, void* scales_out, hipStream_t s);
 hipError_t launch_requant(int scheme, const int32_t* sorted, const int32_t* num_padded,
                           int P, int I, int ntiles_n, int cap, const float* h32,
                           const float* pmax, uint8_t* hq, float* hs, hipStream_t s);

@@ -19,13 +19,14 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqmoe.so"
 QMOE_OK, QMOE_ERR_INVALID_ARG, QMOE_ERR_UNSUPPORTED, QMOE_ERR_HIP = 0, 1, 2, 3
 QMOE_DT_BF16, QMOE_DT_F32 = 0, 1
 QMOE_FLAG_DUMP_ACC = 1
+QMOE_FLAG_PREPACKED = 2
 
 # Every symbol include/qmoe.h declares.
 EXPORTS = (
     "qmoe_abi_version", "qmoe_status_str", "qmoe_last_hip_error", "qmoe_route",
     "qmoe_align_capacity", "qmoe_align_workspace", "qmoe_align", "qmoe_check_flags",
     "qmoe_grouped_ffn_workspace", "qmoe_grouped_ffn_debug_offsets", "qmoe_grouped_ffn",
-    "qmoe_grouped_ffn_profiled", "qmoe_combine",
+    "qmoe_grouped_ffn_profiled", "qmoe_combine", "qmoe_prepack",
 )
 
 
@@ -86,6 +87,8 @@ def _lib() -> ctypes.CDLL:
                                             ctypes.POINTER(ctypes.c_void_p), vp]
     L.qmoe_combine.restype = ctypes.c_int
     L.qmoe_combine.argtypes = [vp, i32, vp, i32, i32, i32, vp, vp, vp]
+    L.qmoe_prepack.restype = ctypes.c_int
+    L.qmoe_prepack.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp]
     _LIB = L
     return L
 
@@ -197,6 +200,29 @@ def grouped_ffn_debug_offsets(desc: FfnDesc):
     return int(a1.value), int(a2.value)
 
 
+def prepack(scheme: str, codes: torch.Tensor, scales: torch.Tensor):
+    """qmoe_prepack of one stacked weight tensor (codes [E, N, K bytes]);
+    returns (codes, scales) in the streaming layout, same shapes and dtypes.
+    W8A8 scales are per-channel and stay as they are (returned as given)."""
+    E, N = codes.shape[0], codes.shape[1]
+    K = codes.shape[2] * (1 if scheme == "w8a8" else 2)
+    c_out = torch.empty_like(codes)
+    s_out = scales if scheme == "w8a8" else torch.empty_like(scales)
+    _check(_lib().qmoe_prepack(SCHEME_CODE[scheme], E, N, K, _ptr(codes), _ptr(scales),
+                               _ptr(c_out), None if scheme == "w8a8" else _ptr(s_out),
+                               _stream(codes.device)), "qmoe_prepack")
+    return c_out, s_out
+
+
+def prepack_weights(scheme: str, weights: dict) -> dict:
+    """Both projections of a weight dict in the streaming layout; the
+    returned dict carries prepacked=True, which grouped_ffn turns into
+    QMOE_FLAG_PREPACKED."""
+    w13, w13s = prepack(scheme, weights["w13"], weights["w13_scale"])
+    w2, w2s = prepack(scheme, weights["w2"], weights["w2_scale"])
+    return {"w13": w13, "w13_scale": w13s, "w2": w2, "w2_scale": w2s, "prepacked": True}
+
+
 def grouped_ffn(scheme: str, x: torch.Tensor, x_scale: Optional[torch.Tensor], weights: dict,
                 al: dict, E: int, k: int, flags: int = 0, ws: Optional[torch.Tensor] = None,
                 y_pairs: Optional[torch.Tensor] = None, stage_events=None):
@@ -205,6 +231,8 @@ def grouped_ffn(scheme: str, x: torch.Tensor, x_scale: Optional[torch.Tensor], w
     T, H = x.shape
     I = weights["w13"].shape[1] // 2
     dev = x.device
+    if weights.get("prepacked", False):
+        flags |= QMOE_FLAG_PREPACKED
     desc = make_desc(scheme, T, H, I, E, k, al["block_m"], flags)
     need = grouped_ffn_workspace(desc)
     if need == 0:

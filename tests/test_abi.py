@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = ops.lib()
-    assert L.qmoe_abi_version() == 1
+    assert L.qmoe_abi_version() == 2
     for s in range(4):
         assert L.qmoe_status_str(s)
     assert L.qmoe_status_str(99) == b"unknown status"
@@ -124,3 +124,20 @@ def test_combine_validation():
     assert L.qmoe_combine(p, 7, p, 4, 2, 16, p, None, None) == ops.QMOE_ERR_INVALID_ARG  # dtype
     assert L.qmoe_combine(p, 0, p, 4, 2, 16, None, None, None) == ops.QMOE_ERR_INVALID_ARG
     assert L.qmoe_combine(None, 0, None, 0, 2, 16, p, None, None) == ops.QMOE_OK  # T = 0
+
+
+def test_prepack_validation():
+    """Every bad argument of qmoe_prepack is refused on the host."""
+    L = ops.lib()
+    a, b, c, d = (ctypes.c_void_p(x) for x in (0x100000, 0x200000, 0x10000000, 0x20000000))
+    INV = ops.QMOE_ERR_INVALID_ARG
+    assert L.qmoe_prepack(3, 2, 32, 256, a, b, c, d, None) == INV          # scheme
+    assert L.qmoe_prepack(2, 0, 32, 256, a, b, c, d, None) == INV          # E
+    assert L.qmoe_prepack(2, 2, 24, 256, a, b, c, d, None) == INV          # N % 16
+    assert L.qmoe_prepack(2, 2, 32, 128, a, b, c, d, None) == INV          # a8w4 K % 256
+    assert L.qmoe_prepack(0, 2, 32, 64, a, b, c, d, None) == INV           # K % 128
+    assert L.qmoe_prepack(2, 2, 32, 256, None, b, c, d, None) == INV       # null codes
+    assert L.qmoe_prepack(2, 2, 32, 256, a, b, None, d, None) == INV       # null output
+    assert L.qmoe_prepack(2, 2, 32, 256, a, b, c, None, None) == INV       # a8w4 needs scales_out
+    assert L.qmoe_prepack(2, 2, 32, 256, a, b, ctypes.c_void_p(0x100010), d, None) == INV  # overlap
+    assert L.qmoe_prepack(2, 2, 32, 256, ctypes.c_void_p(0x100008), b, c, d, None) == INV  # align

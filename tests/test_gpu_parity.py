@@ -120,9 +120,11 @@ def test_combine_matches_oracle(T, k, H, f32):
 
 # ------------------------------------------------------------------ full layer
 
-def _run_gpu(shape, inp, bm=None, flags=0):
+def _run_gpu(shape, inp, bm=None, flags=0, prepacked=False):
     g = gpu_inputs(inp)
     W = {k: g[k] for k in WEIGHT_KEYS}
+    if prepacked:
+        W = ops.prepack_weights(shape.scheme, W)
     r = ops.moe_forward(shape.scheme, g["logits"], g["x"], g["x_scale"], W, shape.topk,
                         bm or default_block_m(shape), flags=flags,
                         want_f32=shape.scheme == "w8a8")
@@ -139,11 +141,11 @@ def _unsort(dump_rows, sorted_ids, P):
     return out
 
 
-def _parity_full(shape, bm=None):
-    _flush(f"ffn full {shape.name} bm={bm or default_block_m(shape)}")
+def _parity_full(shape, bm=None, prepacked=False):
+    _flush(f"ffn full {shape.name} bm={bm or default_block_m(shape)} prepacked={prepacked}")
     inp = synth.make_inputs(shape)
     flags = ops.QMOE_FLAG_DUMP_ACC if shape.scheme == "w8a8" else 0
-    r = _run_gpu(shape, inp, bm, flags)
+    r = _run_gpu(shape, inp, bm, flags, prepacked)
     ids_o, w_o = O.route(inp["logits"], shape.topk)
     np.testing.assert_array_equal(r["topk_ids"].cpu().numpy(), ids_o)
     W = {k: inp[k] for k in WEIGHT_KEYS}
@@ -173,36 +175,44 @@ def _parity_full(shape, bm=None):
         assert err <= TOL[shape.scheme]
 
 
+LAYOUTS = pytest.mark.parametrize("prepacked", [False, True], ids=["canonical", "prepacked"])
+
+
+@LAYOUTS
 @pytest.mark.parametrize("bm", [16, 32, 64, 128])
-def test_tiny_w4a16_all_block_sizes(bm):
-    _parity_full(W4A16_TINY, bm)
+def test_tiny_w4a16_all_block_sizes(bm, prepacked):
+    _parity_full(W4A16_TINY, bm, prepacked)
 
 
-def test_qwen3moe_w4a16_full():
-    _parity_full(W4A16_QWEN3MOE)
+@LAYOUTS
+def test_qwen3moe_w4a16_full(prepacked):
+    _parity_full(W4A16_QWEN3MOE, prepacked=prepacked)
 
 
-def test_w8a8_full_bitexact_accumulators():
-    _parity_full(W8A8_T2048)
+@LAYOUTS
+def test_w8a8_full_bitexact_accumulators(prepacked):
+    _parity_full(W8A8_T2048, prepacked=prepacked)
 
 
+@LAYOUTS
 @pytest.mark.parametrize("bm", [16, 128])
-def test_a8w4_t256_full(bm):
-    _parity_full(A8W4_LARGE.with_tokens(256), bm)
+def test_a8w4_t256_full(bm, prepacked):
+    _parity_full(A8W4_LARGE.with_tokens(256), bm, prepacked)
 
 
+@LAYOUTS
 @pytest.mark.parametrize("scheme", ["w8a8", "a8w4"])
-def test_small_shapes_other_schemes(scheme):
+def test_small_shapes_other_schemes(scheme, prepacked):
     sh = MoEShape(f"small_{scheme}", scheme, tokens=200, hidden=512, inter=256, experts=16,
                   topk=4, seed=77)
     for bm in (16, 64):
-        _parity_full(sh, bm)
+        _parity_full(sh, bm, prepacked)
 
 
-def _parity_sampled(shape, n_sample=24):
-    _flush(f"ffn sampled {shape.name}")
+def _parity_sampled(shape, n_sample=24, prepacked=False):
+    _flush(f"ffn sampled {shape.name} prepacked={prepacked}")
     inp = synth.make_inputs(shape)
-    r = _run_gpu(shape, inp)
+    r = _run_gpu(shape, inp, prepacked=prepacked)
     ids_o, _ = O.route(inp["logits"], shape.topk)
     np.testing.assert_array_equal(r["topk_ids"].cpu().numpy(), ids_o)
     rng = np.random.default_rng(shape.seed)
@@ -215,16 +225,59 @@ def _parity_sampled(shape, n_sample=24):
     assert err <= TOL[shape.scheme]
 
 
-def test_a8w4_t4096_sampled():
-    _parity_sampled(A8W4_LARGE)
+@LAYOUTS
+def test_a8w4_t4096_sampled(prepacked):
+    _parity_sampled(A8W4_LARGE, prepacked=prepacked)
 
 
 def test_a8w4_t8192_sampled():
-    _parity_sampled(A8W4_LARGE.with_tokens(8192))
+    _parity_sampled(A8W4_LARGE.with_tokens(8192), prepacked=True)
 
 
-def test_skewed_w4a16_t8192_sampled():
-    _parity_sampled(W4A16_SKEWED)
+@LAYOUTS
+def test_skewed_w4a16_t8192_sampled(prepacked):
+    _parity_sampled(W4A16_SKEWED, prepacked=prepacked)
+
+
+# ------------------------------------------------------------------ prepack layout
+
+def _np_prepack(scheme, codes, scales):
+    """The streaming layout written out from its definition in qmoe.h:
+    codes [E, N, KB] -> blocks [E, N/16, step, piece i, lane group q, row r,
+    16 bytes]; scale bytes [E, N, R] -> [E, N/16, step, q, r, 2 bytes]."""
+    E, N, KB = codes.shape
+    S = 128 if scheme in ("a8w4", "w8a8") else 64  # code bytes per row per step
+    F = S // 4
+    c = codes.reshape(E, N // 16, 16, KB // S, 4, F // 16, 16)
+    c = c.transpose(0, 1, 3, 5, 4, 2, 6).reshape(E, N, KB)
+    if scheme == "w8a8":
+        return c, scales
+    sb = np.ascontiguousarray(scales).view(np.uint8).reshape(E, N, -1)
+    nsteps = KB // S
+    sc = sb.reshape(E, N // 16, 16, nsteps, 4, 2).transpose(0, 1, 3, 4, 2, 5)
+    return c, np.ascontiguousarray(sc).reshape(sb.shape).view(scales.dtype).reshape(scales.shape)
+
+
+@pytest.mark.parametrize("scheme,E,N,K", [("a8w4", 3, 48, 512), ("w4a16", 2, 32, 384),
+                                          ("w8a8", 2, 64, 256), ("a8w4", 2, 2048, 4096)])
+def test_prepack_layout_bitexact(scheme, E, N, K):
+    _flush(f"prepack {scheme} E={E} N={N} K={K}")
+    rng = np.random.default_rng(11)
+    KB = K if scheme == "w8a8" else K // 2
+    codes = rng.integers(0, 256, (E, N, KB), dtype=np.uint8)
+    if scheme == "w8a8":
+        codes = codes.view(np.int8)
+        scales = rng.random((E, N), dtype=np.float32)
+    elif scheme == "w4a16":
+        scales = rng.random((E, N, K // 32)).astype(np.float16)
+    else:
+        scales = rng.integers(0, 256, (E, N, K // 32), dtype=np.uint8)
+    c_out, s_out = ops.prepack(scheme, to_gpu(codes), to_gpu(scales))
+    torch.cuda.synchronize()
+    c_ref, s_ref = _np_prepack(scheme, codes, scales)
+    np.testing.assert_array_equal(c_out.cpu().numpy().view(np.uint8), c_ref.view(np.uint8))
+    np.testing.assert_array_equal(s_out.cpu().numpy().view(np.uint8),
+                                  np.ascontiguousarray(s_ref).view(np.uint8))
 
 
 # ------------------------------------------------------------------ robustness
