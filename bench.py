@@ -7,7 +7,14 @@ already sit in HBM: route (softmax top-k) -> align (group pairs by expert)
 fp8 activations x MXFP4 weights, hidden 4096, 512 experts, top-10, expert
 inter 1024, 4096 tokens (40960 (token, expert) rows).
 
-Prints one JSON line on stdout; progress goes to stderr.
+Weights are rewritten once into the library's streaming layout
+(qmoe_prepack) at set-up.  Before every timed step a 512 MiB buffer is
+written to flush the 256 MB memory-side cache; each step is timed with HIP
+events on the launch stream (the flush sits outside them) and ms_per_step
+is their mean over the timed steps.
+
+Prints one JSON line on stdout (one per workload with --sweep); progress
+goes to stderr.
 """
 from __future__ import annotations
 
@@ -42,6 +49,8 @@ DOMINANT_COUNTERS = {
     "fetch_kib": 1225450.5,
     "write_kib": 167934.2,
     "sources_sha256_16": "05844688bada118c",
+    "workload": "a8w4_large@T4096",
+    "block_m": 128,
     "weight_layout": "canonical",
 }
 KERNEL_SOURCES = ("quantized_mixture_experts_moe_amd/csrc/gemm.hip",
@@ -128,16 +137,168 @@ def cpu_baseline(shape, inp, target_s: float = 15.0) -> dict:
             "tokens_per_s": total_tok / elapsed}
 
 
+SWEEP = ("w4a16_qwen3moe_t128", "w8a8_t2048", "a8w4_large@T256", "a8w4_large@T1024",
+         "a8w4_large@T4096", "a8w4_large@T8192", "w4a16_skewed_t8192")
+
+
+def stage_flops(shape) -> dict:
+    """Useful FLOPs of each GEMM stage (2 per multiply-add, no padding rows)."""
+    P = shape.tokens * shape.topk
+    return {"stage1": 4.0 * shape.hidden * shape.inter * P,
+            "stage2": 2.0 * shape.hidden * shape.inter * P, "combine": 0.0}
+
+
+def run_workload(name: str, args, torch, with_cpu: bool) -> dict:
+    from quantized_mixture_experts_moe_amd import ops, synth
+    from quantized_mixture_experts_moe_amd.shapes import default_block_m, shape_by_name
+
+    shape = shape_by_name(name)
+    bm = args.block_m or default_block_m(shape)
+    dev = torch.device("cuda:0")
+    t0 = time.perf_counter()
+    inp = synth.make_inputs(shape)
+    log(f"generated {shape.name} in {time.perf_counter() - t0:.1f}s")
+
+    def gpu(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    g = {k: gpu(v) for k, v in inp.items()}
+    W = {k: g[k] for k in ("w13", "w13_scale", "w2", "w2_scale")}
+    layout = "canonical" if args.canonical else "prepacked"
+    if not args.canonical:
+        W = ops.prepack_weights(shape.scheme, W)  # once, at set-up, outside the timed steps
+        for key in ("w13", "w13_scale", "w2", "w2_scale"):
+            del g[key]
+    T, E, k, H = shape.tokens, shape.experts, shape.topk, shape.hidden
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    tw = torch.empty((T, k), dtype=torch.float32, device=dev)
+    ops.route(g["logits"], k, ids, tw)
+    al = ops.align(ids, E, bm)
+    y, ws = ops.grouped_ffn(shape.scheme, g["x"], g["x_scale"], W, al, E, k)
+    out_bf16, out_f32 = ops.combine(y, tw, want_bf16=True, want_f32=shape.scheme == "w8a8")
+    torch.cuda.synchronize()
+    touched = int(torch.unique(ids).numel())
+    # The memory-side cache (256 MB) is flushed before every timed step by
+    # writing a 512 MiB buffer; the flush sits between the step's events.
+    flush = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    n_ev = 7
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+    for row in evs:  # create the underlying events
+        for e in row:
+            e.record()
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        if flush is not None:
+            flush.fill_(i & 255)
+        if ev is not None:
+            ev[0].record()
+        ops.route(g["logits"], k, ids, tw)
+        if ev is not None:
+            ev[1].record()
+        ops.align(ids, E, bm, out=al)
+        ops.grouped_ffn(shape.scheme, g["x"], g["x_scale"], W, al, E, k, ws=ws, y_pairs=y,
+                        stage_events=None if ev is None else ev[2:6])
+        ops.combine(y, tw, out_bf16=out_bf16, out_f32=out_f32, want_f32=out_f32 is not None)
+        if ev is not None:
+            ev[6].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    def per_step(a, b):
+        return np.array([evs[i][a].elapsed_time(evs[i][b]) for i in range(args.steps)])
+
+    step_ms = per_step(0, 6)
+    # Whole-step time: the mean of the timed steps' GPU time (event 0 -> 6),
+    # which leaves out the cache flush between steps; without the flush the
+    # steps run back to back and the host clock is used.
+    ms_per_step = float(step_ms.mean()) if flush is not None else wall_ms
+    kern = {"route": per_step(0, 1).mean(), "align": per_step(1, 2).mean(),
+            "stage1": per_step(2, 3).mean(), "requant": per_step(3, 4).mean(),
+            "stage2": per_step(4, 5).mean(), "combine": per_step(5, 6).mean(),
+            "step_events": step_ms.mean()}
+    kern = {n: float(v) for n, v in kern.items()}
+    log(f"{shape.name}: per-kernel ms: " + ", ".join(f"{n} {v:.4f}" for n, v in kern.items()))
+
+    flops = shape.useful_flops()
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    ab = algorithmic_bytes(shape, touched)
+    sf = stage_flops(shape)
+    dom = max(("stage1", "stage2", "combine"), key=lambda n: kern[n])
+    peak_tf = MFMA_PEAK_TFLOPS[shape.scheme]
+    # Bound of the dominant kernel: arithmetic intensity against the ridge
+    # point peak_flops / peak_bandwidth.
+    ai = sf[dom] / ab[dom]
+    mfma_bound = ai > peak_tf * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if mfma_bound:
+        achieved = sf[dom] / (kern[dom] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak_tf,
+                "unit": "TFLOP/s", "frac": round(achieved / peak_tf, 4)}
+    else:
+        achieved = ab[dom] / (kern[dom] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    traffic = None
+    c = DOMINANT_COUNTERS
+    if (dom == c["kernel"] and shape.name == c["workload"] and bm == c["block_m"]
+            and layout == c["weight_layout"] and kernel_sources_hash() == c["sources_sha256_16"]):
+        traffic = int(round(c["fetch_kib"] * FETCH_FACTOR + c["write_kib"] * WRITE_FACTOR))
+    roof.update({"traffic": traffic,
+                 "kernel": f"moe_gemm_kernel {dom} ({shape.scheme}, block_m {bm})",
+                 "kernel_ms": round(kern[dom], 4), "algorithmic_bytes": int(ab[dom]),
+                 "algorithmic_flops": sf[dom]})
+    step_gbs = ab["step"] / (ms_per_step * 1e-3) / 1e9
+    res = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": DTYPE[shape.scheme], "data": "synthetic (seeded generator, weights random)",
+        "config": {"workload": shape.name, "scheme": shape.scheme, "tokens": T, "hidden": H,
+                   "inter": shape.inter, "experts": E, "topk": k, "block_m": bm,
+                   "touched_experts": touched, "weight_layout": layout,
+                   "cache_flush_between_steps": flush is not None,
+                   "parallelism": "none (1 GPU)"},
+        "ms_per_step_median": round(float(np.median(step_ms)), 4),
+        "wall_ms_per_step": round(wall_ms, 4),
+        "tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
+        "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
+        "step_mfma_frac": round(tflops / peak_tf, 4),
+        "kernel_ms": {n: round(v, 4) for n, v in kern.items()},
+        "roofline": roof,
+    }
+    if with_cpu:
+        res["cpu_baseline"] = cpu_baseline(shape, inp, args.cpu_seconds)
+    del g, W, y, ws, flush
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="a8w4_large@T4096")
+    ap.add_argument("--sweep", action="store_true",
+                    help="run every workload of the sweep, one JSON line each (no CPU baseline)")
     ap.add_argument("--block-m", type=int, default=0)
     ap.add_argument("--canonical", action="store_true",
                     help="feed the weights in their canonical layout (default: the streaming "
                          "layout qmoe_prepack writes once at set-up, outside the timed steps)")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="no cache flush between timed steps (steps run back to back)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -164,111 +325,12 @@ def main():
         print(json.dumps({"copy_bytes": n, "ms": dt * 1e3, "GBps_read": n / dt / 1e9}))
         return
 
-    from quantized_mixture_experts_moe_amd import ops, synth
-    from quantized_mixture_experts_moe_amd.shapes import default_block_m, shape_by_name
-
-    shape = shape_by_name(args.workload)
-    bm = args.block_m or default_block_m(shape)
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    t0 = time.perf_counter()
-    inp = synth.make_inputs(shape)
-    log(f"generated {shape.name} in {time.perf_counter() - t0:.1f}s")
-
-    def gpu(a):
-        if a is None:
-            return None
-        if a.dtype == np.uint16:
-            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
-        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
-
-    g = {k: gpu(v) for k, v in inp.items()}
-    W = {k: g[k] for k in ("w13", "w13_scale", "w2", "w2_scale")}
-    if not args.canonical:
-        W = ops.prepack_weights(shape.scheme, W)
-        for key in ("w13", "w13_scale", "w2", "w2_scale"):
-            del g[key]
-    T, E, k, H = shape.tokens, shape.experts, shape.topk, shape.hidden
-    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
-    tw = torch.empty((T, k), dtype=torch.float32, device=dev)
-    ops.route(g["logits"], k, ids, tw)
-    al = ops.align(ids, E, bm)
-    y, ws = ops.grouped_ffn(shape.scheme, g["x"], g["x_scale"], W, al, E, k)
-    out_bf16, out_f32 = ops.combine(y, tw, want_bf16=True, want_f32=shape.scheme == "w8a8")
-    torch.cuda.synchronize()
-    touched = int(torch.unique(ids).numel())
-
-    n_ev = 8
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
-    for row in evs:  # create the underlying events
-        for e in row:
-            e.record()
-    torch.cuda.synchronize()
-
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record()
-        ops.route(g["logits"], k, ids, tw)
-        if ev is not None:
-            ev[1].record()
-        ops.align(ids, E, bm, out=al)
-        ops.grouped_ffn(shape.scheme, g["x"], g["x_scale"], W, al, E, k, ws=ws, y_pairs=y,
-                        stage_events=None if ev is None else ev[2:6])
-        ops.combine(y, tw, out_bf16=out_bf16, out_f32=out_f32, want_f32=out_f32 is not None)
-        if ev is not None:
-            ev[6].record()
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-
-    def avg(a, b):
-        return float(np.mean([evs[i][a].elapsed_time(evs[i][b]) for i in range(args.steps)]))
-
-    kern = {"route": avg(0, 1), "align": avg(1, 2), "stage1": avg(2, 3), "requant": avg(3, 4),
-            "stage2": avg(4, 5), "combine": avg(5, 6), "step_events": avg(0, 6)}
-    log("per-kernel ms: " + ", ".join(f"{n} {v:.4f}" for n, v in kern.items()))
-
-    flops = shape.useful_flops()
-    tflops = flops / (ms_per_step * 1e-3) / 1e12
-    ab = algorithmic_bytes(shape, touched)
-    dom = max(("stage1", "stage2", "combine"), key=lambda n: kern[n])
-    achieved = ab[dom] / (kern[dom] * 1e-3) / 1e9
-    traffic = None
-    c = DOMINANT_COUNTERS
-    layout = "canonical" if args.canonical else "prepacked"
-    if (dom == c["kernel"] and shape.name == "a8w4_large@T4096" and bm == 128
-            and layout == c["weight_layout"] and kernel_sources_hash() == c["sources_sha256_16"]):
-        traffic = int(round(c["fetch_kib"] * FETCH_FACTOR + c["write_kib"] * WRITE_FACTOR))
-    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": f"moe_gemm_kernel {dom} ({shape.scheme}, block_m {bm})",
-            "kernel_ms": round(kern[dom], 4), "algorithmic_bytes": int(ab[dom])}
-    step_gbs = ab["step"] / (ms_per_step * 1e-3) / 1e9
-    res = {
-        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": DTYPE[shape.scheme], "data": "synthetic (seeded generator, weights random)",
-        "config": {"workload": shape.name, "scheme": shape.scheme, "tokens": T, "hidden": H,
-                   "inter": shape.inter, "experts": E, "topk": k, "block_m": bm,
-                   "touched_experts": touched,
-                   "weight_layout": "canonical" if args.canonical else "prepacked",
-                   "parallelism": "none (1 GPU)"},
-        "tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
-        "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
-        "step_mfma_frac": round(tflops / MFMA_PEAK_TFLOPS[shape.scheme], 4),
-        "kernel_ms": {n: round(v, 4) for n, v in kern.items()},
-        "roofline": roof,
-    }
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(shape, inp, args.cpu_seconds)
+    torch.cuda.set_device(torch.device("cuda:0"))
+    if args.sweep:
+        for name in SWEEP:
+            print(json.dumps(run_workload(name, args, torch, False)), flush=True)
+        return
+    res = run_workload(args.workload, args, torch, not args.no_cpu_baseline)
     print(json.dumps(res), flush=True)
 
 

@@ -107,15 +107,15 @@ typedef struct {
  * makes every 16-byte load of a 64-lane wave part of one contiguous 1 KiB
  * run and every scale load part of one 128-byte run.
  * Let S = weight bytes per row per K step (A8W4: 256 K = 128 B; W8A8: 128 K
- * = 128 B; W4A16: 128 K = 64 B), F = S/4, KB = bytes per row, G = n/16*16.
- * Codes: byte b of row n of expert e, with ks = b/S, r = b%S, q = r/F,
- *   i = (r%F)/16, c = r%16, goes to
+ * = 128 B; W4A16: 128 K = 64 B), KB = bytes per row, G = n/16*16.
+ * Codes: byte b of row n of expert e, with ks = b/S, r = b%S, i = r/64,
+ *   q = (r%64)/16, c = r%16, goes to
  *   (e*N + G)*KB + ks*16*S + i*1024 + (16*q + n%16)*16 + c.
- * Scales (A8W4 e8m0 bytes, W4A16 fp16 values; SB = bytes per entry, R =
- *   K/32*SB bytes per row, BK = K elements per step): for q = 0..3 the 2
- *   bytes of row n at canonical row offset (ks*BK + q*BK/4)/32*SB (the
- *   scales of K elements [ks*BK + q*BK/4, ks*BK + (q+1)*BK/4)) go to
- *   (e*N + G)*R + ks*128 + (16*q + n%16)*2.
+ * Scales (R = scale bytes per row; 8 bytes per row per step in both
+ *   schemes): for q = 0..3, row n and step ks, the two bytes at
+ *   (e*N + G)*R + ks*128 + (16*q + n%16)*2 hold, for A8W4, the e8m0 bytes
+ *   of the 32-K blocks 8*ks + q and 8*ks + 4 + q of the row (in that
+ *   order); for W4A16, the fp16 scale of group 4*ks + q.
  * W8A8 per-channel fp32 scales are copied unchanged (scales_out may be
  * NULL for W8A8, then nothing is copied).
  * codes_out / scales_out have the byte sizes of codes / scales and must not

@@ -102,10 +102,17 @@ struct Tr<kA8W4> {
 };
 
 // Byte offset, inside a staged activation row of one step, of the f-th
-// 16-byte piece of lane group q's A fragment (pieces 2j, 2j+1 feed MFMA j).
-template <int S>
+// 16-byte piece of lane group q's A fragment (a8w4: pieces 2j, 2j+1 feed
+// MFMA j; w8a8 and w4a16: piece j feeds MFMA j).  With the streaming weight
+// layout every MFMA of a step covers one contiguous K range, so the pieces
+// sit at 16q + 64f for the 8-bit schemes (a pattern free of LDS bank
+// conflicts on gfx950, measured); the canonical layout keeps each lane's
+// weight bytes contiguous and the A pieces follow it.
+template <int S, bool PK>
 __device__ inline int a_frag_offset(int q, int f) {
-  if constexpr (S == kA8W4) {
+  if constexpr (PK && S != kW4A16) {
+    return 16 * q + 64 * f;
+  } else if constexpr (S == kA8W4) {
     // B lane group q holds the 32-K blocks 2q (MFMA 0) and 2q+1 (MFMA 1) of
     // the 256-K step, so MFMA j's logical block b is step block 2b + j.  The
     // fp8 halves of lane group q map to logical K 16q and 64 + 16q.
@@ -152,8 +159,8 @@ __device__ inline void mfma_step(typename Tr<S>::Acc& acc, const u32x4* a, const
     }
   } else {
     // A fp8 (format 0) with unit scale 2^0 (e8m0 127); B fp4 (format 4) with
-    // the e8m0 byte of its 32-wide block: byte 0 for the first 32 K of the
-    // lane's run, byte 1 for the second.
+    // the e8m0 byte of its 32-wide block: byte 0 for MFMA 0, byte 1 for
+    // MFMA 1.
     const i32x8 a0 = {(int)a[0].x, (int)a[0].y, (int)a[0].z, (int)a[0].w,
                       (int)a[1].x, (int)a[1].y, (int)a[1].z, (int)a[1].w};
     const i32x8 a1 = {(int)a[2].x, (int)a[2].y, (int)a[2].z, (int)a[2].w,
@@ -327,6 +334,8 @@ moe_gemm_kernel(GemmArgs g) {
         ar[i] = *reinterpret_cast<const u32x4*>(A + (uint32_t)(aoff[i] + ks * T_::A_STEP));
     };
     // Chunk i of this thread lands at LDS row (tid/CPR + i*kThreads/CPR).
+    // (Skipping the rows of unused 16-row groups here was measured slower:
+    // the branches cost more registers than the LDS writes they save.)
     auto store_a = [&](const u32x4(&ar)[NCH], int stage) __attribute__((always_inline)) {
       uint8_t* dst = sA(stage) + lds_w;
 #pragma unroll
@@ -349,7 +358,7 @@ moe_gemm_kernel(GemmArgs g) {
       const uint8_t* src = sA(stage) + (m * 16 + lr) * PITCH;
 #pragma unroll
       for (int f = 0; f < NF; f++)
-        af[f] = *reinterpret_cast<const u32x4*>(src + a_frag_offset<S>(lq, f));
+        af[f] = *reinterpret_cast<const u32x4*>(src + a_frag_offset<S, PK>(lq, f));
     };
     // With FRAG2 the reads run one group ahead (two fragment buffers);
     // otherwise each group's reads directly precede its MFMAs and the other

@@ -3,10 +3,14 @@
 //
 // Canonical: row n of expert e is KB contiguous bytes (K along the row), its
 // scales R contiguous bytes.  Streaming: for each group of 16 rows and each
-// K step, one block of 16*S bytes in which lane L = 16*q + r of a wave finds
-// its F = S/4 bytes of row r (the quarter q of the step's row bytes) as
-// 16-byte pieces at i*1024 + L*16; the two scale bytes of that quarter sit
-// at 128*ks + 2*L of the group's scale block.
+// K step (S code bytes per row), one block of 16*S bytes in which lane
+// L = 16*q + r of a wave finds, as its 16-byte piece i at i*1024 + L*16, the
+// step bytes [64*i + 16*q, 64*i + 16*q + 16) of row r.  Each MFMA of a step
+// then covers one contiguous K range (bytes [64*i, 64*i + 64)), which keeps
+// the activation fragment reads free of LDS bank conflicts.  The two scale
+// bytes of a lane sit at 128*ks + 2*L of the group's scale block: for A8W4
+// the e8m0 bytes of 32-K blocks q and 4 + q of the step (one per MFMA), for
+// W4A16 the fp16 scale of group q.
 #include "qmoe_internal.h"
 
 namespace qmoe {
@@ -20,7 +24,6 @@ __global__ void prepack_codes_kernel(const uint8_t* __restrict__ src, uint8_t* _
                                      size_t rows, int KB, int S) {
   const size_t per_group = (size_t)KB;  // 16-byte pieces per 16-row group (16*KB bytes)
   const size_t total = rows / 16 * per_group;
-  const int F = S / 4;
   for (size_t oc = (size_t)blockIdx.x * blockDim.x + threadIdx.x; oc < total;
        oc += (size_t)gridDim.x * blockDim.x) {
     const size_t grp = oc / per_group;
@@ -29,15 +32,16 @@ __global__ void prepack_codes_kernel(const uint8_t* __restrict__ src, uint8_t* _
     const int i = rem2 >> 6, L = rem2 & 63;
     const int q = L >> 4, r = L & 15;
     const size_t row = grp * 16 + r;
-    const size_t sb = row * KB + (size_t)ks * S + q * F + i * 16;
+    const size_t sb = row * KB + (size_t)ks * S + i * 64 + q * 16;
     *reinterpret_cast<u32x4*>(dst + oc * 16) = *reinterpret_cast<const u32x4*>(src + sb);
   }
 }
 
-// One thread per 2-byte output entry.  R = scale bytes per row, BK = K per
-// step, SB = bytes per scale entry, nsteps = K / BK.
+// One thread per 2-byte output entry.  R = scale bytes per row, nsteps =
+// steps per row; fp16 (W4A16: one entry of 4 per step) or e8m0 (A8W4: the
+// entries q and 4 + q of 8 per step).
 __global__ void prepack_scales_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
-                                      size_t rows, int R, int BK, int SB, int nsteps) {
+                                      size_t rows, int R, bool e8m0, int nsteps) {
   const size_t per_group = (size_t)nsteps * 64;  // entries per 16-row group
   const size_t total = rows / 16 * per_group;
   for (size_t oc = (size_t)blockIdx.x * blockDim.x + threadIdx.x; oc < total;
@@ -47,8 +51,14 @@ __global__ void prepack_scales_kernel(const uint8_t* __restrict__ src, uint8_t* 
     const int ks = rem >> 6, L = rem & 63;
     const int q = L >> 4, r = L & 15;
     const size_t row = grp * 16 + r;
-    const size_t sb = row * R + (size_t)((ks * BK + q * (BK / 4)) / 32) * SB;
-    *reinterpret_cast<uint16_t*>(dst + oc * 2) = *reinterpret_cast<const uint16_t*>(src + sb);
+    if (e8m0) {
+      const uint8_t* p = src + row * R + (size_t)ks * 8;
+      dst[oc * 2] = p[q];
+      dst[oc * 2 + 1] = p[4 + q];
+    } else {
+      *reinterpret_cast<uint16_t*>(dst + oc * 2) =
+          *reinterpret_cast<const uint16_t*>(src + row * R + (size_t)ks * 8 + q * 2);
+    }
   }
 }
 
@@ -82,7 +92,7 @@ hipError_t launch_prepack(int scheme, int E, int N, int K, const void* codes, co
   const size_t entries = rows / 16 * nsteps * 64;
   hipLaunchKernelGGL(prepack_scales_kernel, dim3(grid_for(entries)), dim3(256), 0, s,
                      reinterpret_cast<const uint8_t*>(scales),
-                     reinterpret_cast<uint8_t*>(scales_out), rows, R, BK, SB, nsteps);
+                     reinterpret_cast<uint8_t*>(scales_out), rows, R, scheme == 2, nsteps);
   return hipGetLastError();
 }
 

@@ -244,18 +244,22 @@ def test_skewed_w4a16_t8192_sampled(prepacked):
 def _np_prepack(scheme, codes, scales):
     """The streaming layout written out from its definition in qmoe.h:
     codes [E, N, KB] -> blocks [E, N/16, step, piece i, lane group q, row r,
-    16 bytes]; scale bytes [E, N, R] -> [E, N/16, step, q, r, 2 bytes]."""
+    16 bytes] where piece i of lane group q is step bytes 64i + 16q;
+    scales -> [E, N/16, step, q, r, 2 bytes]."""
     E, N, KB = codes.shape
     S = 128 if scheme in ("a8w4", "w8a8") else 64  # code bytes per row per step
-    F = S // 4
-    c = codes.reshape(E, N // 16, 16, KB // S, 4, F // 16, 16)
-    c = c.transpose(0, 1, 3, 5, 4, 2, 6).reshape(E, N, KB)
+    c = codes.reshape(E, N // 16, 16, KB // S, S // 64, 4, 16)  # [.., r, ks, i, q, c]
+    c = c.transpose(0, 1, 3, 4, 5, 2, 6).reshape(E, N, KB)
     if scheme == "w8a8":
         return c, scales
-    sb = np.ascontiguousarray(scales).view(np.uint8).reshape(E, N, -1)
     nsteps = KB // S
-    sc = sb.reshape(E, N // 16, 16, nsteps, 4, 2).transpose(0, 1, 3, 4, 2, 5)
-    return c, np.ascontiguousarray(sc).reshape(sb.shape).view(scales.dtype).reshape(scales.shape)
+    if scheme == "a8w4":  # e8m0 bytes: blocks (q, 4 + q) of each step's 8
+        sb = scales.reshape(E, N // 16, 16, nsteps, 2, 4)           # [.., r, ks, half, q]
+        sc = sb.transpose(0, 1, 3, 5, 2, 4)                          # [.., ks, q, r, half]
+        return c, np.ascontiguousarray(sc).reshape(scales.shape)
+    sb = scales.reshape(E, N // 16, 16, nsteps, 4)                   # fp16 [.., r, ks, q]
+    sc = sb.transpose(0, 1, 3, 4, 2)                                 # [.., ks, q, r]
+    return c, np.ascontiguousarray(sc).reshape(scales.shape)
 
 
 @pytest.mark.parametrize("scheme,E,N,K", [("a8w4", 3, 48, 512), ("w4a16", 2, 32, 384),
