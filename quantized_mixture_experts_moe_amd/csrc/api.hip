@@ -27,7 +27,8 @@ int device_cu_count() {
   std::lock_guard<std::mutex> lock(mu);
   if (cached[dev] == 0) {
     int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n < 1)
       n = 1;
     cached[dev] = n;
   }
@@ -69,7 +70,7 @@ static FfnWs ffn_ws_layout(const qmoe_ffn_desc& d) {
     w.hs = off;
     off = align_up(off + cap * 4, 256);
     w.pmax = off;
-    off = align_up(off + cap * (I / kStage1Cols) * 4, 256);
+    off = align_up(off + cap * (I / kMinStage1Cols) * 4, 256);
   }
   if (d.scheme == QMOE_W8A8_PERCHAN && (d.flags & QMOE_FLAG_DUMP_ACC)) {
     w.acc1 = off;
@@ -79,6 +80,25 @@ static FfnWs ffn_ws_layout(const qmoe_ffn_desc& d) {
   }
   w.total = std::max<size_t>(off, 256);
   return w;
+}
+
+// Block shape of the grouped GEMMs: sub-tiles per wave and waves per block.
+// 8-wave blocks (one per CU) halve the activation traffic per weight byte;
+// measured on the 128-row tiles they win for stage 1 of the 4-bit-weight
+// schemes and stage 2 of W8A8, and the 4-wave blocks (two per CU) win the
+// other stage.  Smaller tiles keep 4-wave blocks.  The wide tiles (one
+// 4-wave block per CU, AGPR accumulators) measured slower everywhere and are
+// built only with QMOE_ENABLE_WIDE.
+struct GemmShape {
+  int nsub, waves;
+};
+static GemmShape choose_shape(int scheme, int stage, int block_m) {
+#ifdef QMOE_ENABLE_WIDE
+  if (block_m >= 64) return {4, 4};
+#endif
+  const int wide_stage = scheme == QMOE_W8A8_PERCHAN ? 2 : 1;
+  if (block_m >= 128 && stage == wide_stage) return {2, 8};
+  return {2, 4};
 }
 
 static qmoe_status check_desc(const qmoe_ffn_desc* d) {
@@ -224,7 +244,9 @@ static qmoe_status grouped_ffn_impl(const qmoe_ffn_desc* d, const void* x, const
 
   g1.N = 2 * d->I;
   g1.K = d->H;
-  g1.ntiles_n = d->I / kStage1Cols;
+  const GemmShape gs1 = choose_shape(d->scheme, 1, d->block_m);
+  const GemmShape gs2 = choose_shape(d->scheme, 2, d->block_m);
+  g1.ntiles_n = d->I / stage_cols(1, gs1.nsub, gs1.waves);
   g1.a = x;
   g1.a_scale = x_scale;
   g1.b = w->w13;
@@ -237,7 +259,8 @@ static qmoe_status grouped_ffn_impl(const qmoe_ffn_desc* d, const void* x, const
   };
   hipError_t e = mark(0);
   const bool packed = (d->flags & QMOE_FLAG_PREPACKED) != 0;
-  if (e == hipSuccess) e = launch_gemm(d->scheme, 1, d->block_m, packed, g1, s);
+  if (e == hipSuccess)
+    e = launch_gemm(d->scheme, 1, d->block_m, packed, gs1.nsub, gs1.waves, g1, s);
   if (e == hipSuccess) e = mark(1);
   if (e != hipSuccess) return hip_status(e);
 
@@ -253,7 +276,7 @@ static qmoe_status grouped_ffn_impl(const qmoe_ffn_desc* d, const void* x, const
 
   g2.N = d->H;
   g2.K = d->I;
-  g2.ntiles_n = d->H / kStage2Cols;
+  g2.ntiles_n = d->H / stage_cols(2, gs2.nsub, gs2.waves);
   g2.a = quant_act ? (const void*)(wsb + lay.hq) : (const void*)(wsb + lay.h);
   g2.a_scale = quant_act ? reinterpret_cast<const float*>(wsb + lay.hs) : nullptr;
   g2.b = w->w2;
@@ -261,7 +284,7 @@ static qmoe_status grouped_ffn_impl(const qmoe_ffn_desc* d, const void* x, const
   g2.out = y_pairs;
   g2.row_pmax = nullptr;
   g2.dump = dump ? reinterpret_cast<int32_t*>(wsb + lay.acc2) : nullptr;
-  e = launch_gemm(d->scheme, 2, d->block_m, packed, g2, s);
+  e = launch_gemm(d->scheme, 2, d->block_m, packed, gs2.nsub, gs2.waves, g2, s);
   if (e == hipSuccess) e = mark(3);
   return hip_status(e);
 }
@@ -302,8 +325,9 @@ qmoe_status qmoe_prepack(int32_t scheme, int32_t E, int32_t N, int32_t K, const 
       (scales_out && !aligned(scales_out, 4)))
     return QMOE_ERR_INVALID_ARG;
   const size_t cb = (size_t)E * N * (scheme == QMOE_W8A8_PERCHAN ? K : K / 2);
-  const size_t sbytes = scheme == QMOE_W8A8_PERCHAN ? (size_t)E * N * 4
-                                                    : (size_t)E * N * (K / 32) * (scheme == 0 ? 2 : 1);
+  const size_t sbytes = scheme == QMOE_W8A8_PERCHAN
+                            ? (size_t)E * N * 4
+                            : (size_t)E * N * (K / 32) * (scheme == QMOE_W4A16_G32 ? 2 : 1);
   auto overlap = [](const void* a, size_t na, const void* b, size_t nb) {
     const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
     return x < y + nb && y < x + na;

@@ -8,15 +8,15 @@
 //
 // Rows are the expert-sorted, block_m-padded pair slots from moe_align; a
 // row tile never straddles two experts.  One workgroup = 4 waves (one per
-// SIMD), two workgroups per CU; each wave owns two 16-column weight
-// sub-tiles (stage 1: the gate column and the up column of the same h
-// column, so silu(gate)*up is formed in registers) and all BM rows.  Weight
-// fragments stream from HBM straight into VGPRs, each weight byte read by
-// exactly one wave, three K steps ahead of the MFMAs (a ring of four
-// register sets); the gathered activation rows go global -> VGPR -> a
-// two-slot LDS ring, loaded two steps ahead and shared by the 4 waves.  One
-// barrier per K step.  16-row groups past the tile's last real row are
-// skipped.
+// SIMD, two workgroups per CU) or 8 waves (two per SIMD, one workgroup per
+// CU); each wave owns two 16-column weight sub-tiles (stage 1: the gate
+// column and the up column of the same h column, so silu(gate)*up is formed
+// in registers) and all BM rows.  Weight fragments stream from HBM straight
+// into VGPRs, each weight byte read by exactly one wave, three K steps ahead
+// of the MFMAs (a ring of four register sets); the gathered activation rows
+// go global -> VGPR -> a two-slot LDS ring, loaded two steps ahead and
+// shared by the block's waves.  One barrier per K step.  16-row groups past
+// the tile's last real row are skipped.
 //
 // Matrix cores (CDNA4 MFMA), 16x16 output per instruction:
 //   w4a16: v_mfma_f32_16x16x32_bf16, int4 * fp16 group scale rounded to
@@ -141,23 +141,50 @@ __device__ inline bf16x8 dequant8_bf16(uint32_t v, float sc) {
   return r;
 }
 
+// A step's weight fragment in the form the MFMAs take: w4a16 dequantizes
+// its int4 codes to bf16 once per step (the result is reused by every
+// 16-row group of the tile); the 8-bit schemes feed the codes as they are.
 template <int S>
-__device__ inline void mfma_step(typename Tr<S>::Acc& acc, const u32x4* a, const BFrag<S>& b) {
+struct BReady {
+  BFrag<S> f;
+};
+template <>
+struct BReady<kW4A16> {
+  bf16x8 v[4];
+};
+
+template <int S>
+__device__ inline BReady<S> prepare_b(const BFrag<S>& b) {
   if constexpr (S == kW4A16) {
+    BReady<S> r;
     const float sc = __half2float(__ushort_as_half((unsigned short)b.sc));
-    const uint32_t w[4] = {b.q[0].x, b.q[0].y, b.q[0].z, b.q[0].w};
+    r.v[0] = dequant8_bf16(b.q[0].x, sc);
+    r.v[1] = dequant8_bf16(b.q[0].y, sc);
+    r.v[2] = dequant8_bf16(b.q[0].z, sc);
+    r.v[3] = dequant8_bf16(b.q[0].w, sc);
+    return r;
+  } else {
+    return BReady<S>{b};
+  }
+}
+
+template <int S>
+__device__ inline void mfma_step(typename Tr<S>::Acc& acc, const u32x4* a, const BReady<S>& br) {
+  if constexpr (S == kW4A16) {
 #pragma unroll
     for (int j = 0; j < 4; j++) {
       const bf16x8 av = __builtin_bit_cast(bf16x8, a[j]);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, dequant8_bf16(w[j], sc), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, br.v[j], acc, 0, 0, 0);
     }
   } else if constexpr (S == kW8A8) {
+    const BFrag<S>& b = br.f;
 #pragma unroll
     for (int j = 0; j < 2; j++) {
       acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, a[j]),
                                                  __builtin_bit_cast(i32x4, b.q[j]), acc, 0, 0, 0);
     }
   } else {
+    const BFrag<S>& b = br.f;
     // A fp8 (format 0) with unit scale 2^0 (e8m0 127); B fp4 (format 4) with
     // the e8m0 byte of its 32-wide block: byte 0 for MFMA 0, byte 1 for
     // MFMA 1.
@@ -189,9 +216,11 @@ __device__ inline float silu_mul(float g, float u) {
   return sg * u;
 }
 
-template <int S, int STAGE, int BM, bool PK>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void
-moe_gemm_kernel(GemmArgs g) {
+template <int S, int STAGE, int BM, bool PK, int NSUB, int WAVES>
+__global__ __launch_bounds__(WAVES * 64)
+    __attribute__((amdgpu_waves_per_eu(NSUB == 4 ? 1 : 2, NSUB == 4 ? 1 : 2))) void
+    moe_gemm_kernel(GemmArgs g) {
+  constexpr int kThreads = WAVES * 64;
   using T_ = Tr<S>;
   using Acc = typename T_::Acc;
   constexpr int MSUB = BM / 16;
@@ -199,11 +228,11 @@ moe_gemm_kernel(GemmArgs g) {
   constexpr int CPR = T_::A_STEP / 16;                       // 16-byte chunks per row per step
   constexpr int NCH = (BM * CPR + kThreads - 1) / kThreads;  // chunks per thread per step
   constexpr int NF = T_::A_FRAG / 16;                        // 16-byte LDS reads per fragment
-  constexpr int HALF = kNsub / 2;                            // stage 1: gate sub-tiles per wave
+  constexpr int HALF = NSUB / 2;                             // stage 1: gate sub-tiles per wave
 
   // Epilogue tile: the block's BM x COLS outputs, staged in LDS (over the
   // activation ring) so that global stores are 16 contiguous bytes per lane.
-  constexpr int COLS = STAGE == 1 ? kStage1Cols : kStage2Cols;
+  constexpr int COLS = stage_cols(STAGE, NSUB, WAVES);
   constexpr int OUT_ES = STAGE == 1 ? (S == kW4A16 ? 2 : 4) : (S == kW8A8 ? 4 : 2);
   constexpr int EPITCH = COLS * OUT_ES + 16;
   constexpr int RING = kStages * BM * PITCH;
@@ -265,14 +294,14 @@ moe_gemm_kernel(GemmArgs g) {
 
     // Weight rows of this wave's sub-tiles, as 32-bit offsets from the
     // expert's base (one expert's weights are far below 4 GiB).
-    int nrow[kNsub];
+    int nrow[NSUB];
 #pragma unroll
-    for (int s = 0; s < kNsub; s++) {
+    for (int s = 0; s < NSUB; s++) {
       if (STAGE == 1) {
-        const int base = nt * kStage1Cols + wave * HALF * 16 + lr;
+        const int base = nt * COLS + wave * HALF * 16 + lr;
         nrow[s] = s < HALF ? base + s * 16 : g.I + base + (s - HALF) * 16;
       } else {
-        nrow[s] = nt * kStage2Cols + wave * kNsub * 16 + s * 16 + lr;
+        nrow[s] = nt * COLS + wave * NSUB * 16 + s * 16 + lr;
       }
     }
     constexpr int SB = S == kW4A16 ? 2 : 1;  // scale bytes (w4a16 fp16, a8w4 e8m0)
@@ -284,9 +313,9 @@ moe_gemm_kernel(GemmArgs g) {
     // Streaming layout (qmoe_prepack): the 16 rows x step bytes of a sub-tile
     // are one contiguous block in which the same bytes sit at
     // i*1024 + lane*16, and the step's scales are 128 contiguous bytes.
-    uint32_t boff[kNsub], soff[kNsub];
+    uint32_t boff[NSUB], soff[NSUB];
 #pragma unroll
-    for (int s = 0; s < kNsub; s++) {
+    for (int s = 0; s < NSUB; s++) {
       if constexpr (PK) {
         const uint32_t g16 = (uint32_t)(nrow[s] - lr);  // first row of the 16-row group
         boff[s] = g16 * (uint32_t)kbytes + lane * 16;
@@ -302,9 +331,9 @@ moe_gemm_kernel(GemmArgs g) {
 
     // Every address below is a wave-uniform base plus one 32-bit per-lane
     // offset, so the loads use the scalar-base + 32-bit-offset form.
-    auto load_b = [&](BFrag<S>(&bf)[kNsub], int ks) __attribute__((always_inline)) {
+    auto load_b = [&](BFrag<S>(&bf)[NSUB], int ks) __attribute__((always_inline)) {
 #pragma unroll
-      for (int s = 0; s < kNsub; s++) {
+      for (int s = 0; s < NSUB; s++) {
         const uint32_t o = boff[s] + (uint32_t)ks * B_KS;
 #pragma unroll
         for (int i = 0; i < T_::B_FRAG / 16; i++)
@@ -345,11 +374,11 @@ moe_gemm_kernel(GemmArgs g) {
       }
     };
 
-    Acc acc[MSUB][kNsub];
+    Acc acc[MSUB][NSUB];
 #pragma unroll
     for (int m = 0; m < MSUB; m++)
 #pragma unroll
-      for (int s = 0; s < kNsub; s++) acc[m][s] = Acc{0, 0, 0, 0};
+      for (int s = 0; s < NSUB; s++) acc[m][s] = Acc{0, 0, 0, 0};
 
     // Activation fragments are read from LDS one 16-row group ahead of the
     // MFMAs that use them; the scheduling fences keep the compiler from
@@ -362,9 +391,13 @@ moe_gemm_kernel(GemmArgs g) {
     };
     // With FRAG2 the reads run one group ahead (two fragment buffers);
     // otherwise each group's reads directly precede its MFMAs and the other
-    // wave on the SIMD covers the LDS latency.
-    constexpr bool FRAG2 = !(S == kA8W4 && BM >= 128);
-    auto compute = [&](int stage, const BFrag<S>(&bc)[kNsub]) __attribute__((always_inline)) {
+    // wave on the SIMD covers the LDS latency (the 4-wave a8w4 128-row tile
+    // has no registers left for the second buffer).
+    constexpr bool FRAG2 = !(S == kA8W4 && BM >= 128 && (WAVES == 4 || STAGE == 2));
+    auto compute = [&](int stage, const BFrag<S>(&bcr)[NSUB]) __attribute__((always_inline)) {
+      BReady<S> bc[NSUB];
+#pragma unroll
+      for (int s = 0; s < NSUB; s++) bc[s] = prepare_b<S>(bcr[s]);
       u32x4 fa[NF], fb[NF];
       if constexpr (FRAG2) read_frag(fa, stage, 0);
 #pragma unroll
@@ -373,11 +406,11 @@ moe_gemm_kernel(GemmArgs g) {
           if constexpr (FRAG2) {
             if (m + 1 < MSUB && m + 1 < mvalid) read_frag((m & 1) ? fa : fb, stage, m + 1);
 #pragma unroll
-            for (int s = 0; s < kNsub; s++) mfma_step<S>(acc[m][s], (m & 1) ? fb : fa, bc[s]);
+            for (int s = 0; s < NSUB; s++) mfma_step<S>(acc[m][s], (m & 1) ? fb : fa, bc[s]);
           } else {
             read_frag(fa, stage, m);
 #pragma unroll
-            for (int s = 0; s < kNsub; s++) mfma_step<S>(acc[m][s], fa, bc[s]);
+            for (int s = 0; s < NSUB; s++) mfma_step<S>(acc[m][s], fa, bc[s]);
           }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -395,8 +428,8 @@ moe_gemm_kernel(GemmArgs g) {
     // and the compiler's counter waits stay exact.
     const int n = nsteps;
     u32x4 ar[NCH];
-    BFrag<S> b0[kNsub], b1[kNsub], b2[kNsub], b3[kNsub];
-    auto step = [&](int s, const BFrag<S>(&bc)[kNsub], BFrag<S>(&bl)[kNsub])
+    BFrag<S> b0[NSUB], b1[NSUB], b2[NSUB], b3[NSUB];
+    auto step = [&](int s, const BFrag<S>(&bc)[NSUB], BFrag<S>(&bl)[NSUB])
         __attribute__((always_inline)) {
       store_a(ar, (s + 1) & 1);
       load_a(ar, min(s + 2, n - 1));
@@ -470,8 +503,8 @@ moe_gemm_kernel(GemmArgs g) {
             float rs = 1.f;
             if constexpr (S != kW4A16) rs = sScale[row];
 #pragma unroll
-            for (int s = 0; s < kNsub; s++) {
-              const int cl = wave * kNsub * 16 + s * 16 + lr;  // output column inside the tile
+            for (int s = 0; s < NSUB; s++) {
+              const int cl = wave * NSUB * 16 + s * 16 + lr;  // output column inside the tile
               if constexpr (S == kW8A8) {
                 const float ws2 =
                     reinterpret_cast<const float*>(g.b_scale)[(size_t)e * g.N + nrow[s]];
@@ -524,51 +557,71 @@ moe_gemm_kernel(GemmArgs g) {
   }
 }
 
-template <int S, int STAGE, int BM, bool PK>
+template <int S, int STAGE, int BM, bool PK, int NSUB, int WAVES>
 hipError_t launch_one(const GemmArgs& g, hipStream_t s) {
   static int blocks_per_cu = 0;
   if (blocks_per_cu == 0) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, moe_gemm_kernel<S, STAGE, BM, PK>,
-                                                     kThreads, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &n, moe_gemm_kernel<S, STAGE, BM, PK, NSUB, WAVES>, WAVES * 64, 0) != hipSuccess ||
         n < 1)
       n = 1;
     blocks_per_cu = n;
   }
   int nblk = device_cu_count() * blocks_per_cu;
   nblk = nblk < 8 ? 8 : (nblk / 8) * 8;
-  hipLaunchKernelGGL((moe_gemm_kernel<S, STAGE, BM, PK>), dim3(nblk), dim3(kThreads), 0, s, g);
+  hipLaunchKernelGGL((moe_gemm_kernel<S, STAGE, BM, PK, NSUB, WAVES>), dim3(nblk),
+                     dim3(WAVES * 64), 0, s, g);
   return hipGetLastError();
 }
 
 template <int S, int STAGE, bool PK>
-hipError_t launch_bm(int block_m, const GemmArgs& g, hipStream_t s) {
+hipError_t launch_bm(int block_m, int nsub, int waves, const GemmArgs& g, hipStream_t s) {
+#ifdef QMOE_ENABLE_WIDE
+  if (nsub == 4 && waves == 4) {
+    switch (block_m) {
+      case 64: return launch_one<S, STAGE, 64, PK, 4, 4>(g, s);
+      case 128: return launch_one<S, STAGE, 128, PK, 4, 4>(g, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
+#endif
+  if (nsub != 2) return hipErrorInvalidValue;
+  if (waves == 8) {
+    switch (block_m) {
+      case 64: return launch_one<S, STAGE, 64, PK, 2, 8>(g, s);
+      case 128: return launch_one<S, STAGE, 128, PK, 2, 8>(g, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (waves != 4) return hipErrorInvalidValue;
   switch (block_m) {
-    case 16: return launch_one<S, STAGE, 16, PK>(g, s);
-    case 32: return launch_one<S, STAGE, 32, PK>(g, s);
-    case 64: return launch_one<S, STAGE, 64, PK>(g, s);
-    case 128: return launch_one<S, STAGE, 128, PK>(g, s);
+    case 16: return launch_one<S, STAGE, 16, PK, 2, 4>(g, s);
+    case 32: return launch_one<S, STAGE, 32, PK, 2, 4>(g, s);
+    case 64: return launch_one<S, STAGE, 64, PK, 2, 4>(g, s);
+    case 128: return launch_one<S, STAGE, 128, PK, 2, 4>(g, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <int S, int STAGE>
-hipError_t launch_layout(bool packed, int block_m, const GemmArgs& g, hipStream_t s) {
-  return packed ? launch_bm<S, STAGE, true>(block_m, g, s)
-                : launch_bm<S, STAGE, false>(block_m, g, s);
+hipError_t launch_layout(bool packed, int block_m, int nsub, int waves, const GemmArgs& g,
+                         hipStream_t s) {
+  return packed ? launch_bm<S, STAGE, true>(block_m, nsub, waves, g, s)
+                : launch_bm<S, STAGE, false>(block_m, nsub, waves, g, s);
 }
 
 }  // namespace
 
-hipError_t launch_gemm(int scheme, int stage, int block_m, bool packed, const GemmArgs& g,
-                       hipStream_t s) {
+hipError_t launch_gemm(int scheme, int stage, int block_m, bool packed, int nsub, int waves,
+                       const GemmArgs& g, hipStream_t s) {
   switch (scheme * 2 + (stage - 1)) {
-    case 0: return launch_layout<kW4A16, 1>(packed, block_m, g, s);
-    case 1: return launch_layout<kW4A16, 2>(packed, block_m, g, s);
-    case 2: return launch_layout<kW8A8, 1>(packed, block_m, g, s);
-    case 3: return launch_layout<kW8A8, 2>(packed, block_m, g, s);
-    case 4: return launch_layout<kA8W4, 1>(packed, block_m, g, s);
-    case 5: return launch_layout<kA8W4, 2>(packed, block_m, g, s);
+    case 0: return launch_layout<kW4A16, 1>(packed, block_m, nsub, waves, g, s);
+    case 1: return launch_layout<kW4A16, 2>(packed, block_m, nsub, waves, g, s);
+    case 2: return launch_layout<kW8A8, 1>(packed, block_m, nsub, waves, g, s);
+    case 3: return launch_layout<kW8A8, 2>(packed, block_m, nsub, waves, g, s);
+    case 4: return launch_layout<kA8W4, 1>(packed, block_m, nsub, waves, g, s);
+    case 5: return launch_layout<kA8W4, 2>(packed, block_m, nsub, waves, g, s);
     default: return hipErrorInvalidValue;
   }
 }

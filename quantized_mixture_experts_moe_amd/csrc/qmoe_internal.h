@@ -5,17 +5,23 @@
 
 namespace qmoe {
 
-// Tile geometry of the grouped GEMMs (both stages).  A block is 256
-// threads = 4 waves and two blocks share a CU (one wave of each per SIMD),
-// so one block's loads, epilogue and tile set-up overlap the other's MFMAs.
-// Every wave owns kNsub 16-column weight sub-tiles and all BM rows of the
-// tile, so a block covers 128 weight rows.
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
-constexpr int kNsub = 2;
-constexpr int kStages = 2;                            // LDS slots of the activation ring
-constexpr int kStage1Cols = kWaves * kNsub * 16 / 2;  // h columns per stage-1 tile (64)
-constexpr int kStage2Cols = kWaves * kNsub * 16;      // output columns per stage-2 tile (128)
+// Tile geometry of the grouped GEMMs (both stages).  A block is `waves`
+// waves of 64 threads; every wave owns `nsub` 16-column weight sub-tiles and
+// all BM rows of the tile, so a block covers waves*nsub*16 weight rows, and
+// the gathered activation rows it stages in LDS feed all of them.
+//  - 4 waves, nsub 2: two blocks share a CU (two waves per SIMD), so one
+//    block's loads, epilogue and tile set-up overlap the other's MFMAs;
+//  - 8 waves, nsub 2: one block per CU (two waves per SIMD); each staged
+//    activation row feeds twice the weight rows, which halves the
+//    activation traffic from L2 per weight byte;
+//  - 4 waves, nsub 4 (wide): one block per CU, accumulators in AGPRs.
+constexpr int kStages = 2;  // LDS slots of the activation ring
+// h columns per stage-1 tile (gate and up sub-tiles pair up), output
+// columns per stage-2 tile.
+constexpr int stage_cols(int stage, int nsub, int waves) {
+  return stage == 1 ? waves * nsub * 8 : waves * nsub * 16;
+}
+constexpr int kMinStage1Cols = stage_cols(1, 2, 4);  // sizes the per-row |h| max table
 
 struct GemmArgs {
   int T, H, I, E, k, P;  // P = T*k pairs
@@ -39,8 +45,8 @@ hipError_t launch_align(const int32_t* ids, int T, int k, int E, int block_m, in
                         int32_t* tile_expert, int32_t* offsets, int32_t* num_padded,
                         int32_t* chunk_counts, int32_t* chunk_flags, int32_t* flags, int cap,
                         hipStream_t s);
-hipError_t launch_gemm(int scheme, int stage, int block_m, bool packed, const GemmArgs& g,
-                       hipStream_t s);
+hipError_t launch_gemm(int scheme, int stage, int block_m, bool packed, int nsub, int waves,
+                       const GemmArgs& g, hipStream_t s);
 hipError_t launch_prepack(int scheme, int E, int N, int K, const void* codes, const void* scales,
                           void* codes_out, void* scales_out, hipStream_t s);
 hipError_t launch_requant(int scheme, const int32_t* sorted, const int32_t* num_padded,
