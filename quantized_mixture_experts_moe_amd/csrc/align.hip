@@ -9,13 +9,13 @@
 //  1. count: one block per 256-token chunk; each wave builds in LDS a 64-bit
 //     mask per expert of its 64 tokens routed to that expert, and the block
 //     writes the chunk's count per expert, counts[e][chunk].
-//  2. scan: one block.  A wave scans an expert's chunk counts into chunk
-//     bases (exclusive prefix), the expert totals are padded to block_m and
-//     scanned into expert offsets; the tile->expert map and the sentinels of
-//     the padding are written.
+//  2. scan: one block.  Each expert's chunk counts become chunk bases
+//     (exclusive prefix, staged through LDS), the expert totals are padded to
+//     block_m and scanned into expert offsets.
 //  3. scatter: the count blocks again; a pair's slot is the expert offset +
 //     the chunk base + the earlier waves' counts + popcount(mask & lanes
-//     below).
+//     below).  The same launch writes the padding sentinels, the
+//     tile->expert map and the tail, spread over at least 32 blocks.
 #include "qmoe_internal.h"
 
 namespace qmoe {
@@ -66,53 +66,78 @@ __global__ __launch_bounds__(kChunk) void align_count_kernel(const int32_t* __re
   }
 }
 
-__global__ __launch_bounds__(1024) void align_scan_kernel(int nchunks, int E, int block_m, int P,
-                                                          int cap, int32_t* __restrict__ counts,
-                                                          int32_t* __restrict__ sorted,
-                                                          int32_t* __restrict__ tile_expert,
+// Chunk counts staged in LDS per scan pass: the experts of a pass are those
+// whose nchunks counts fit (row pitch nchunks + 1 keeps the per-expert
+// walks free of bank conflicts).
+constexpr int kScanLdsInts = 16384;
+
+__global__ __launch_bounds__(1024) void align_scan_kernel(int nchunks, int E, int block_m,
+                                                          int32_t* __restrict__ counts,
+                                                          int32_t* __restrict__ totals,
                                                           int32_t* __restrict__ offsets,
                                                           int32_t* __restrict__ num_padded,
                                                           const int32_t* __restrict__ chunk_flags,
                                                           int32_t* __restrict__ flags) {
+  __shared__ int s_cnt[kScanLdsInts];
   __shared__ int s_total[kMaxExperts];
   __shared__ int s_part[1024];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  constexpr int kBatch = 8;  // experts whose loads a wave keeps in flight together
-  for (int eb = wave * kBatch; eb < E; eb += 16 * kBatch) {
-    int carry[kBatch];
-#pragma unroll
-    for (int i = 0; i < kBatch; i++) carry[i] = 0;
-    for (int cg = 0; cg < nchunks; cg += 64) {
-      const int c = cg + lane;
-      int v[kBatch];
-#pragma unroll
-      for (int i = 0; i < kBatch; i++) {
-        const int e = eb + i;
-        v[i] = (e < E && c < nchunks) ? counts[(size_t)e * nchunks + c] : 0;
-      }
-#pragma unroll
-      for (int i = 0; i < kBatch; i++) {
-        int x = v[i];
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const int y = __shfl_up(x, off, 64);
-          if (lane >= off) x += y;
+  // 1. counts[e][c] -> exclusive prefix over c (the chunk bases), in place,
+  //    and the expert totals.  Passes of experts whose counts fit in LDS:
+  //    one coalesced load, one thread per expert walks its row, one
+  //    coalesced store.
+  const int pitch = nchunks + 1;
+  const int per_pass = max(1, min(E, kScanLdsInts / pitch));
+  for (int e0 = 0; e0 < E; e0 += per_pass) {
+    const int ne = min(per_pass, E - e0);
+    const int n = ne * nchunks;
+    const int32_t* src = counts + (size_t)e0 * nchunks;
+    if (pitch * ne <= kScanLdsInts) {
+      for (int i = tid; i < n; i += 1024) s_cnt[(i / nchunks) * pitch + i % nchunks] = src[i];
+      __syncthreads();
+      for (int e = tid; e < ne; e += 1024) {
+        int run = 0;
+        int* row = s_cnt + e * pitch;
+        for (int c = 0; c < nchunks; c++) {
+          const int v = row[c];
+          row[c] = run;
+          run += v;
         }
-        const int e = eb + i;
-        if (e < E && c < nchunks) counts[(size_t)e * nchunks + c] = carry[i] + x - v[i];
-        carry[i] += __shfl(x, 63, 64);
+        s_total[e0 + e] = run;
       }
-    }
+      __syncthreads();
+      int32_t* dst = counts + (size_t)e0 * nchunks;
+      for (int i = tid; i < n; i += 1024) dst[i] = s_cnt[(i / nchunks) * pitch + i % nchunks];
+      __syncthreads();
+    } else {
+      // One expert's row exceeds LDS (more than kScanLdsInts chunks): a
+      // wave scans each row in pieces of 64 chunks.
+      for (int e = e0 + wave; e < e0 + ne; e += 16) {
+        int carry = 0;
+        int32_t* row = counts + (size_t)e * nchunks;
+        for (int cg = 0; cg < nchunks; cg += 64) {
+          const int c = cg + lane;
+          const int v = c < nchunks ? row[c] : 0;
+          int x = v;
 #pragma unroll
-    for (int i = 0; i < kBatch; i++)
-      if (lane == 0 && eb + i < E) s_total[eb + i] = carry[i];
+          for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(x, off, 64);
+            if (lane >= off) x += y;
+          }
+          if (c < nchunks) row[c] = carry + x - v;
+          carry += __shfl(x, 63, 64);
+        }
+        if (lane == 0) s_total[e] = carry;
+      }
+      __syncthreads();
+    }
   }
-  __syncthreads();
-  // Each thread owns a contiguous run of experts [e0, e1).
+  // 2. Expert offsets: exclusive scan of the block_m-padded totals.  Each
+  //    thread owns a contiguous run of experts.
   const int per = (E + 1023) / 1024;
-  const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
+  const int r0 = min(E, tid * per), r1 = min(E, r0 + per);
   int run_pad = 0;
-  for (int e = e0; e < e1; e++) run_pad += (s_total[e] + block_m - 1) / block_m * block_m;
+  for (int e = r0; e < r1; e++) run_pad += (s_total[e] + block_m - 1) / block_m * block_m;
   s_part[tid] = run_pad;
   __syncthreads();
   for (int off = 1; off < 1024; off <<= 1) {  // inclusive scan of the run totals
@@ -123,13 +148,10 @@ __global__ __launch_bounds__(1024) void align_scan_kernel(int nchunks, int E, in
   }
   const int npad = s_part[1023];
   int base = s_part[tid] - run_pad;
-  for (int e = e0; e < e1; e++) {
-    const int total = s_total[e];
-    const int padded = (total + block_m - 1) / block_m * block_m;
+  for (int e = r0; e < r1; e++) {
     offsets[e] = base;
-    for (int i = base / block_m; i < (base + padded) / block_m; i++) tile_expert[i] = e;
-    for (int i = base + total; i < base + padded; i++) sorted[i] = P;
-    base += padded;
+    totals[e] = s_total[e];
+    base += (s_total[e] + block_m - 1) / block_m * block_m;
   }
   int bad = 0;
   for (int c = tid; c < nchunks; c += 1024) bad |= chunk_flags[c];
@@ -140,35 +162,54 @@ __global__ __launch_bounds__(1024) void align_scan_kernel(int nchunks, int E, in
     *num_padded = npad;
     *flags = (b1 ? 1 : 0) | (b2 ? 2 : 0);
   }
-  for (int i = npad + tid; i < cap; i += 1024) sorted[i] = P;
-  for (int i = npad / block_m + tid; i < cap / block_m; i += 1024) tile_expert[i] = -1;
 }
 
+// Blocks below nchunks place their chunk's pairs; every block then takes a
+// share of the padding: the sentinels after each expert's pairs and its
+// tile->expert entries (one wave per expert, consecutive lanes on
+// consecutive slots), and the tail from num_padded to cap.
 __global__ __launch_bounds__(kChunk) void align_scatter_kernel(
-    const int32_t* __restrict__ ids, int T, int k, int E, int nchunks,
+    const int32_t* __restrict__ ids, int T, int k, int E, int nchunks, int block_m, int cap,
     const int32_t* __restrict__ chunk_base, const int32_t* __restrict__ offsets,
-    int32_t* __restrict__ sorted) {
+    const int32_t* __restrict__ totals, int32_t* __restrict__ sorted,
+    int32_t* __restrict__ tile_expert) {
   extern __shared__ unsigned long long mask[];  // [4][E]
-  build_masks(ids, T, k, E, mask);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int t = blockIdx.x * kChunk + tid;
-  if (t >= T) return;
-  const unsigned long long below = (1ull << lane) - 1ull;
-  for (int j = 0; j < k; j++) {
-    const int e = ids[(size_t)t * k + j];
-    if (e < 0 || e >= E) continue;
-    int rank = __popcll(mask[wave * E + e] & below);
-    for (int w = 0; w < wave; w++) rank += __popcll(mask[w * E + e]);
-    sorted[offsets[e] + chunk_base[(size_t)e * nchunks + blockIdx.x] + rank] = t * k + j;
+  const int P = T * k;
+  if ((int)blockIdx.x < nchunks) {
+    build_masks(ids, T, k, E, mask);
+    const int t = blockIdx.x * kChunk + tid;
+    if (t < T) {
+      const unsigned long long below = (1ull << lane) - 1ull;
+      for (int j = 0; j < k; j++) {
+        const int e = ids[(size_t)t * k + j];
+        if (e < 0 || e >= E) continue;
+        int rank = __popcll(mask[wave * E + e] & below);
+        for (int w = 0; w < wave; w++) rank += __popcll(mask[w * E + e]);
+        sorted[offsets[e] + chunk_base[(size_t)e * nchunks + blockIdx.x] + rank] = t * k + j;
+      }
+    }
   }
+  const int nwaves = gridDim.x * (kChunk / 64);
+  for (int e = blockIdx.x * (kChunk / 64) + wave; e < E; e += nwaves) {
+    const int off = offsets[e], total = totals[e];
+    const int padded = (total + block_m - 1) / block_m * block_m;
+    for (int i = off / block_m + lane; i < (off + padded) / block_m; i += 64) tile_expert[i] = e;
+    for (int i = off + total + lane; i < off + padded; i += 64) sorted[i] = P;
+  }
+  const int npad = offsets[E];
+  const int stride = gridDim.x * kChunk;
+  for (int i = npad + blockIdx.x * kChunk + tid; i < cap; i += stride) sorted[i] = P;
+  for (int i = npad / block_m + blockIdx.x * kChunk + tid; i < cap / block_m; i += stride)
+    tile_expert[i] = -1;
 }
 
 }  // namespace
 
 hipError_t launch_align(const int32_t* ids, int T, int k, int E, int block_m, int32_t* sorted,
                         int32_t* tile_expert, int32_t* offsets, int32_t* num_padded,
-                        int32_t* chunk_counts, int32_t* chunk_flags, int32_t* flags, int cap,
-                        hipStream_t s) {
+                        int32_t* chunk_counts, int32_t* chunk_flags, int32_t* totals,
+                        int32_t* flags, int cap, hipStream_t s) {
   if (E > kMaxExperts) return hipErrorInvalidValue;
   const int nchunks = (T + kChunk - 1) / kChunk;
   const size_t lds = (size_t)4 * E * sizeof(unsigned long long);
@@ -179,14 +220,14 @@ hipError_t launch_align(const int32_t* ids, int T, int k, int E, int block_m, in
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  hipLaunchKernelGGL(align_scan_kernel, dim3(1), dim3(1024), 0, s, nchunks, E, block_m, T * k,
-                     cap, chunk_counts, sorted, tile_expert, offsets, num_padded, chunk_flags,
-                     flags);
+  hipLaunchKernelGGL(align_scan_kernel, dim3(1), dim3(1024), 0, s, nchunks, E, block_m,
+                     chunk_counts, totals, offsets, num_padded, chunk_flags, flags);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  if (nchunks == 0) return hipSuccess;
-  hipLaunchKernelGGL(align_scatter_kernel, dim3(nchunks), dim3(kChunk), lds, s, ids, T, k, E,
-                     nchunks, chunk_counts, offsets, sorted);
+  // At least 32 blocks share the padding writes even when there are few chunks.
+  const int nblk = nchunks > 32 ? nchunks : 32;
+  hipLaunchKernelGGL(align_scatter_kernel, dim3(nblk), dim3(kChunk), lds, s, ids, T, k, E,
+                     nchunks, block_m, cap, chunk_counts, offsets, totals, sorted, tile_expert);
   return hipGetLastError();
 }
 

@@ -41,7 +41,7 @@ static bool valid_block_m(int bm) { return bm == 16 || bm == 32 || bm == 64 || b
 
 // Layout of qmoe_align's workspace: flag word, per-chunk flags, counts.
 struct AlignWs {
-  size_t flags, chunk_flags, counts, total;
+  size_t flags, chunk_flags, counts, totals, total;
 };
 static AlignWs align_ws_layout(int T, int E) {
   AlignWs w;
@@ -49,7 +49,8 @@ static AlignWs align_ws_layout(int T, int E) {
   w.flags = 0;
   w.chunk_flags = 256;
   w.counts = align_up(w.chunk_flags + nch * 4, 256);
-  w.total = align_up(w.counts + nch * (size_t)E * 4, 256);
+  w.totals = align_up(w.counts + nch * (size_t)E * 4, 256);
+  w.total = align_up(w.totals + (size_t)E * 4, 256);
   return w;
 }
 
@@ -175,6 +176,7 @@ qmoe_status qmoe_align(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
                                  expert_offsets, num_padded,
                                  reinterpret_cast<int32_t*>(w + lay.counts),
                                  reinterpret_cast<int32_t*>(w + lay.chunk_flags),
+                                 reinterpret_cast<int32_t*>(w + lay.totals),
                                  reinterpret_cast<int32_t*>(w + lay.flags), cap,
                                  (hipStream_t)stream));
 }

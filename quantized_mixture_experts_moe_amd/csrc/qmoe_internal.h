@@ -43,8 +43,8 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, 
                         hipStream_t s);
 hipError_t launch_align(const int32_t* ids, int T, int k, int E, int block_m, int32_t* sorted,
                         int32_t* tile_expert, int32_t* offsets, int32_t* num_padded,
-                        int32_t* chunk_counts, int32_t* chunk_flags, int32_t* flags, int cap,
-                        hipStream_t s);
+                        int32_t* chunk_counts, int32_t* chunk_flags, int32_t* totals,
+                        int32_t* flags, int cap, hipStream_t s);
 hipError_t launch_gemm(int scheme, int stage, int block_m, bool packed, int nsub, int waves,
                        const GemmArgs& g, hipStream_t s);
 hipError_t launch_prepack(int scheme, int E, int N, int K, const void* codes, const void* scales,

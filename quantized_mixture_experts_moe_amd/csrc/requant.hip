@@ -7,7 +7,8 @@
 //   w8a8: code = clamp(round_half_even(h / s), -127, 127)
 //   a8w4: code = e4m3 round-to-nearest-even of h / s, saturated to +-448.
 // The row absmax is the max of the per-column-tile maxima stage 1 wrote.
-// One wave per row; padding rows are skipped.
+// One wave per row; padding rows are skipped.  The division h / s is kept
+// (not a multiplication by 1/s) so the codes are the correctly rounded ones.
 #include "qmoe_internal.h"
 
 namespace qmoe {
@@ -34,6 +35,11 @@ __device__ inline uint32_t to_i8x4(float a, float b, float c, float d) {
          ((uint32_t)(qd & 0xff) << 24);
 }
 
+// A row is processed in passes of up to kVec*64 float4 (kVec*256 values);
+// within a pass every load is issued before the row max is reduced, so a
+// wave waits for memory about once per pass.
+constexpr int kVec = 8;
+
 template <bool FP8>
 __global__ __launch_bounds__(256) void requant_kernel(const int32_t* __restrict__ sorted,
                                                       const int32_t* __restrict__ num_padded,
@@ -46,18 +52,33 @@ __global__ __launch_bounds__(256) void requant_kernel(const int32_t* __restrict_
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= *num_padded) return;
   if (sorted[row] >= P) return;  // padding slot
+  const float4* src = reinterpret_cast<const float4*>(h32 + (size_t)row * I);
+  uint32_t* dst = reinterpret_cast<uint32_t*>(hq + (size_t)row * I);
+  const int n4 = I / 4;
+  float4 v[kVec];
+#pragma unroll
+  for (int i = 0; i < kVec; i++)
+    if (lane + 64 * i < n4) v[i] = src[lane + 64 * i];
   float a = 0.f;
   for (int i = lane; i < ntiles_n; i += 64) a = fmaxf(a, pmax[(size_t)row * ntiles_n + i]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
   const float s = a > 0.f ? a / (FP8 ? 448.0f : 127.0f) : 1.0f;
   if (lane == 0) hs[row] = s;
-  const float4* src = reinterpret_cast<const float4*>(h32 + (size_t)row * I);
-  uint32_t* dst = reinterpret_cast<uint32_t*>(hq + (size_t)row * I);
-  for (int i = lane; i < I / 4; i += 64) {
-    const float4 v = src[i];
-    const float x0 = v.x / s, x1 = v.y / s, x2 = v.z / s, x3 = v.w / s;
-    dst[i] = FP8 ? to_e4m3x4(x0, x1, x2, x3) : to_i8x4(x0, x1, x2, x3);
+  for (int base = 0; base < n4; base += 64 * kVec) {
+    if (base > 0) {
+#pragma unroll
+      for (int i = 0; i < kVec; i++)
+        if (base + lane + 64 * i < n4) v[i] = src[base + lane + 64 * i];
+    }
+#pragma unroll
+    for (int i = 0; i < kVec; i++) {
+      const int idx = base + lane + 64 * i;
+      if (idx < n4) {
+        const float x0 = v[i].x / s, x1 = v[i].y / s, x2 = v[i].z / s, x3 = v[i].w / s;
+        dst[idx] = FP8 ? to_e4m3x4(x0, x1, x2, x3) : to_i8x4(x0, x1, x2, x3);
+      }
+    }
   }
 }
 
