@@ -201,19 +201,25 @@ __device__ inline void mfma_step(typename Tr<S>::Acc& acc, const u32x4* a, const
   }
 }
 
-// fp32 epilogue recipe shared by w8a8 (bit-exact contract) and a8w4:
-// ex = f32(exp_f64(-g)); sg = g / (1 + ex); h = sg * u.  w4a16 uses expf.
+// SiLU(gate) * up in the stage-1 epilogue.
+// w8a8 follows the bit-exact fp32 recipe: ex = f32(exp_f64(-g));
+// sg = g / (1 + ex) (IEEE division); h = sg * u.
+// w4a16 and a8w4 use the hardware exp2 and reciprocal (a few ulp each; the
+// library expf and IEEE division cost ~25 more instructions per element, a
+// measured third of the tile epilogue):
+// ex = exp2(-g * log2(e)); sg = g * rcp(1 + ex); h = sg * u.
 template <int S>
 __device__ inline float silu_mul(float g, float u) {
-  float ex;
   if constexpr (S == kW8A8) {
-    ex = (float)exp(-(double)g);
+    const float ex = (float)exp(-(double)g);
+    const float den = 1.0f + ex;
+    const float sg = g / den;
+    return sg * u;
   } else {
-    ex = expf(-g);
+    const float ex = __builtin_amdgcn_exp2f(-g * 1.44269504088896341f);
+    const float sg = g * __builtin_amdgcn_rcpf(1.0f + ex);
+    return sg * u;
   }
-  const float den = 1.0f + ex;
-  const float sg = g / den;
-  return sg * u;
 }
 
 template <int S, int STAGE, int BM, bool PK, int NSUB, int WAVES>
@@ -238,8 +244,9 @@ __global__ __launch_bounds__(WAVES * 64)
   constexpr int RING = kStages * BM * PITCH;
   constexpr int SMEM = RING > BM * EPITCH ? RING : BM * EPITCH;
   __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
-  __shared__ int sRow[BM];
-  __shared__ float sScale[BM];
+  // Row ids of the tile being set up and of the tile in its epilogue.
+  __shared__ __attribute__((aligned(16))) int sRow[2][BM];
+  __shared__ __attribute__((aligned(16))) float sScale[BM];
   auto sA = [&](int stage) __attribute__((always_inline)) { return smem + stage * BM * PITCH; };
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -260,7 +267,7 @@ __global__ __launch_bounds__(WAVES * 64)
   const uint8_t* __restrict__ B = reinterpret_cast<const uint8_t*>(g.b);
 
   // Tile metadata (pair ids of the rows, the expert) is fetched one tile
-  // ahead, so a tile starts without waiting on those loads.
+  // ahead of the tile's set-up.
   int next_pair = g.P, next_expert = 0;
   auto fetch_meta = [&](int w) __attribute__((always_inline)) {
     if (w < w_end) {
@@ -269,51 +276,100 @@ __global__ __launch_bounds__(WAVES * 64)
       next_expert = g.tile_expert[m];
     }
   };
-  fetch_meta(w_begin + slot);
-  for (int wi = w_begin + slot; wi < w_end; wi += per_xcd) {
-    const int mt = wi / g.ntiles_n, nt = wi - mt * g.ntiles_n;
-    __syncthreads();  // previous tile is done with the LDS tiles and sRow / sScale
-    const int e = next_expert;
+
+  constexpr int SB = S == kW4A16 ? 2 : 1;  // scale bytes (w4a16 fp16, a8w4 e8m0)
+  constexpr uint32_t B_KS = PK ? 16 * T_::B_STEP : T_::B_STEP;  // code bytes per step
+  constexpr uint32_t B_PIECE = PK ? 1024 : 16;                   // between a lane's pieces
+  constexpr uint32_t S_KS = PK ? 128 : 8;                         // scale bytes per step
+  const int n = nsteps;
+
+  // State of the tile whose K loop runs next: its coordinates, the row
+  // count, the per-row scale (kept in a register until its epilogue) and the
+  // load addresses.  Every address is a wave-uniform base plus one 32-bit
+  // per-lane offset, so the loads use the scalar-base + 32-bit-offset form.
+  int t_mt = 0, t_nt = 0, t_e = 0, t_nvalid = 0, t_mvalid = 0;
+  float t_scale = 0.f;
+  int nrow[NSUB];
+  const uint8_t* __restrict__ Bexp = B;
+  const uint8_t* __restrict__ Sexp = reinterpret_cast<const uint8_t*>(g.b_scale);
+  uint32_t boff[NSUB], soff[NSUB], aoff[NCH];
+
+  auto load_b = [&](BFrag<S>(&bf)[NSUB], int ks) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < NSUB; s++) {
+      const uint32_t o = boff[s] + (uint32_t)ks * B_KS;
+#pragma unroll
+      for (int i = 0; i < T_::B_FRAG / 16; i++)
+        bf[s].q[i] = *reinterpret_cast<const u32x4*>(Bexp + (uint32_t)(o + B_PIECE * i));
+      if (S == kW4A16 || S == kA8W4)
+        bf[s].sc =
+            *reinterpret_cast<const unsigned short*>(Sexp + (uint32_t)(soff[s] + ks * S_KS));
+      else
+        bf[s].sc = 0;
+    }
+  };
+  auto load_a = [&](u32x4(&ar)[NCH], int ks) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NCH; i++)
+      ar[i] = *reinterpret_cast<const u32x4*>(A + (uint32_t)(aoff[i] + ks * T_::A_STEP));
+  };
+  // Chunk i of this thread lands at LDS row (tid/CPR + i*kThreads/CPR).
+  // (Skipping the rows of unused 16-row groups here was measured slower:
+  // the branches cost more registers than the LDS writes they save.)
+  auto store_a = [&](const u32x4(&ar)[NCH], int stage) __attribute__((always_inline)) {
+    uint8_t* dst = sA(stage) + lds_w;
+#pragma unroll
+    for (int i = 0; i < NCH; i++) {
+      if (NCH * kThreads == BM * CPR || tid + i * kThreads < BM * CPR)
+        *reinterpret_cast<u32x4*>(dst + i * (kThreads / CPR) * PITCH) = ar[i];
+    }
+  };
+
+  u32x4 ar[NCH];
+  BFrag<S> b0[NSUB], b1[NSUB], b2[NSUB], b3[NSUB];
+
+  // Set-up of tile w (row ids into sRow[bf]) and its first loads: the
+  // activation rows of step 0 and the weights of steps 0-2.  It runs right
+  // after the previous tile's K loop, before that tile's epilogue, so these
+  // loads are in flight while the epilogue computes and stores (issued after
+  // its stores they would queue behind them).
+  auto setup = [&](int w, int bf) __attribute__((always_inline)) {
+    t_mt = w / g.ntiles_n;
+    t_nt = w - t_mt * g.ntiles_n;
+    t_e = next_expert;
     int valid_here = 0;
-    float row_scale = 0.f;
     if (tid < BM) {
       const int p = next_pair;
       const bool ok = p < g.P;
       const int ri = ok ? (STAGE == 1 ? p / g.k : p) : -1;
-      sRow[tid] = ri;
+      sRow[bf][tid] = ri;
       valid_here = ok;
-      // Per-row scale used by the epilogue (token scale in stage 1, the
-      // requantized h scale in stage 2); written to LDS after the K loop, so
-      // the load's latency is covered by the loop.
+      // Per-row scale of the epilogue (token scale in stage 1, the
+      // requantized h scale in stage 2).
       if constexpr (S != kW4A16)
-        row_scale = ok ? g.a_scale[STAGE == 1 ? ri : (size_t)mt * BM + tid] : 0.f;
+        t_scale = ok ? g.a_scale[STAGE == 1 ? ri : (size_t)t_mt * BM + tid] : 0.f;
     }
-    const int nvalid = __syncthreads_count(valid_here);
-    const int mvalid = (nvalid + 15) >> 4;
-    fetch_meta(wi + per_xcd);
-
+    t_nvalid = __syncthreads_count(valid_here);
+    t_mvalid = (t_nvalid + 15) >> 4;
+    fetch_meta(w + per_xcd);
     // Weight rows of this wave's sub-tiles, as 32-bit offsets from the
     // expert's base (one expert's weights are far below 4 GiB).
-    int nrow[NSUB];
 #pragma unroll
     for (int s = 0; s < NSUB; s++) {
       if (STAGE == 1) {
-        const int base = nt * COLS + wave * HALF * 16 + lr;
+        const int base = t_nt * COLS + wave * HALF * 16 + lr;
         nrow[s] = s < HALF ? base + s * 16 : g.I + base + (s - HALF) * 16;
       } else {
-        nrow[s] = nt * COLS + wave * NSUB * 16 + s * 16 + lr;
+        nrow[s] = t_nt * COLS + wave * NSUB * 16 + s * 16 + lr;
       }
     }
-    constexpr int SB = S == kW4A16 ? 2 : 1;  // scale bytes (w4a16 fp16, a8w4 e8m0)
-    const uint8_t* __restrict__ Bexp = B + (size_t)e * g.N * kbytes;
-    const uint8_t* __restrict__ Sexp =
-        reinterpret_cast<const uint8_t*>(g.b_scale) + (size_t)e * g.N * (K / 32) * SB;
+    Bexp = B + (size_t)t_e * g.N * kbytes;
+    Sexp = reinterpret_cast<const uint8_t*>(g.b_scale) + (size_t)t_e * g.N * (K / 32) * SB;
     // Canonical layout: lane (lq, lr) reads row nrow's bytes [lq*B_FRAG,
     // (lq+1)*B_FRAG) of each step and the two scale bytes of that run.
-    // Streaming layout (qmoe_prepack): the 16 rows x step bytes of a sub-tile
-    // are one contiguous block in which the same bytes sit at
+    // Streaming layout (qmoe_prepack): the 16 rows x step bytes of a
+    // sub-tile are one contiguous block in which the same bytes sit at
     // i*1024 + lane*16, and the step's scales are 128 contiguous bytes.
-    uint32_t boff[NSUB], soff[NSUB];
 #pragma unroll
     for (int s = 0; s < NSUB; s++) {
       if constexpr (PK) {
@@ -325,60 +381,25 @@ __global__ __launch_bounds__(WAVES * 64)
         soff[s] = (uint32_t)nrow[s] * (uint32_t)(K / 32) * SB + lq * 2;
       }
     }
-    constexpr uint32_t B_KS = PK ? 16 * T_::B_STEP : T_::B_STEP;  // code bytes per step
-    constexpr uint32_t B_PIECE = PK ? 1024 : 16;                   // between a lane's pieces
-    constexpr uint32_t S_KS = PK ? 128 : 8;                         // scale bytes per step
-
-    // Every address below is a wave-uniform base plus one 32-bit per-lane
-    // offset, so the loads use the scalar-base + 32-bit-offset form.
-    auto load_b = [&](BFrag<S>(&bf)[NSUB], int ks) __attribute__((always_inline)) {
-#pragma unroll
-      for (int s = 0; s < NSUB; s++) {
-        const uint32_t o = boff[s] + (uint32_t)ks * B_KS;
-#pragma unroll
-        for (int i = 0; i < T_::B_FRAG / 16; i++)
-          bf[s].q[i] = *reinterpret_cast<const u32x4*>(Bexp + (uint32_t)(o + B_PIECE * i));
-        if (S == kW4A16 || S == kA8W4)
-          bf[s].sc =
-              *reinterpret_cast<const unsigned short*>(Sexp + (uint32_t)(soff[s] + ks * S_KS));
-        else
-          bf[s].sc = 0;
-      }
-    };
-
     // Activation chunks of this thread: fixed rows per tile.  Rows past the
     // tile's last real row read that row again (their results are dropped),
     // so every load is in bounds without a branch.
-    uint32_t aoff[NCH];
 #pragma unroll
     for (int i = 0; i < NCH; i++) {
-      const int row = min(tid / CPR + i * (kThreads / CPR), nvalid - 1), col = tid % CPR;
-      const uint32_t rbase = STAGE == 1 ? (uint32_t)sRow[row] * (uint32_t)(g.H * T_::A_ELEM)
-                                        : (uint32_t)(mt * BM + row) * (uint32_t)(g.I * T_::A_ELEM);
+      const int row = min(tid / CPR + i * (kThreads / CPR), t_nvalid - 1), col = tid % CPR;
+      const uint32_t rbase = STAGE == 1
+                                 ? (uint32_t)sRow[bf][row] * (uint32_t)(g.H * T_::A_ELEM)
+                                 : (uint32_t)(t_mt * BM + row) * (uint32_t)(g.I * T_::A_ELEM);
       aoff[i] = rbase + col * 16;
     }
-    auto load_a = [&](u32x4(&ar)[NCH], int ks) __attribute__((always_inline)) {
-#pragma unroll
-      for (int i = 0; i < NCH; i++)
-        ar[i] = *reinterpret_cast<const u32x4*>(A + (uint32_t)(aoff[i] + ks * T_::A_STEP));
-    };
-    // Chunk i of this thread lands at LDS row (tid/CPR + i*kThreads/CPR).
-    // (Skipping the rows of unused 16-row groups here was measured slower:
-    // the branches cost more registers than the LDS writes they save.)
-    auto store_a = [&](const u32x4(&ar)[NCH], int stage) __attribute__((always_inline)) {
-      uint8_t* dst = sA(stage) + lds_w;
-#pragma unroll
-      for (int i = 0; i < NCH; i++) {
-        if (NCH * kThreads == BM * CPR || tid + i * kThreads < BM * CPR)
-          *reinterpret_cast<u32x4*>(dst + i * (kThreads / CPR) * PITCH) = ar[i];
-      }
-    };
+    load_a(ar, 0);
+    load_b(b0, 0);
+    load_b(b1, min(1, n - 1));
+    load_b(b2, min(2, n - 1));
+  };
 
-    Acc acc[MSUB][NSUB];
-#pragma unroll
-    for (int m = 0; m < MSUB; m++)
-#pragma unroll
-      for (int s = 0; s < NSUB; s++) acc[m][s] = Acc{0, 0, 0, 0};
+  Acc acc[MSUB][NSUB];
+  int mvalid = 0;  // 16-row groups with a real row in the tile of the K loop
 
     // Activation fragments are read from LDS one 16-row group ahead of the
     // MFMAs that use them; the scheduling fences keep the compiler from
@@ -417,30 +438,30 @@ __global__ __launch_bounds__(WAVES * 64)
       }
     };
 
-    // K loop.  Step s computes from LDS slot s%2 and weight register set
-    // s%4.  A step first writes the activation rows of step s+1 (loaded one
-    // step earlier) to the other LDS slot, then issues the activation loads
-    // of step s+2 and the weight loads of step s+3, then runs the MFMAs of
-    // step s; one barrier ends the step.  Load counters complete in order,
-    // so this order lets the wait for the activations skip the younger
-    // weight loads, which keep three steps to arrive.  Loads past the last
-    // step re-read the last step (cache hits): every step has the same shape
-    // and the compiler's counter waits stay exact.
-    const int n = nsteps;
-    u32x4 ar[NCH];
-    BFrag<S> b0[NSUB], b1[NSUB], b2[NSUB], b3[NSUB];
-    auto step = [&](int s, const BFrag<S>(&bc)[NSUB], BFrag<S>(&bl)[NSUB])
-        __attribute__((always_inline)) {
-      store_a(ar, (s + 1) & 1);
-      load_a(ar, min(s + 2, n - 1));
-      load_b(bl, min(s + 3, n - 1));
-      if (s < n) compute(s & 1, bc);
-      __syncthreads();
-    };
-    load_a(ar, 0);
-    load_b(b0, 0);
-    load_b(b1, min(1, n - 1));
-    load_b(b2, min(2, n - 1));
+  // K loop.  Step s computes from LDS slot s%2 and weight register set s%4.
+  // A step first writes the activation rows of step s+1 (loaded one step
+  // earlier) to the other LDS slot, then issues the activation loads of
+  // step s+2 and the weight loads of step s+3, then runs the MFMAs of step
+  // s; one barrier ends the step.  Load counters complete in order, so this
+  // order lets the wait for the activations skip the younger weight loads,
+  // which keep three steps to arrive.  Loads past the last step re-read the
+  // last step (cache hits): every step has the same shape and the
+  // compiler's counter waits stay exact.
+  auto step = [&](int s, const BFrag<S>(&bc)[NSUB], BFrag<S>(&bl)[NSUB])
+      __attribute__((always_inline)) {
+    store_a(ar, (s + 1) & 1);
+    load_a(ar, min(s + 2, n - 1));
+    load_b(bl, min(s + 3, n - 1));
+    if (s < n) compute(s & 1, bc);
+    __syncthreads();
+  };
+
+  int wi = w_begin + slot;
+  if (wi >= w_end) return;
+  fetch_meta(wi);
+  int buf = 0;
+  setup(wi, buf);
+  while (true) {
     // The previous tile's output stores are still in flight.  On gfx9 stores
     // and loads share one counter, and pending stores would turn every wait
     // of the pipelined loop into a full drain; drain them here, where the
@@ -448,6 +469,11 @@ __global__ __launch_bounds__(WAVES * 64)
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     store_a(ar, 0);
     load_a(ar, min(1, n - 1));
+    mvalid = t_mvalid;
+#pragma unroll
+    for (int m = 0; m < MSUB; m++)
+#pragma unroll
+      for (int s = 0; s < NSUB; s++) acc[m][s] = Acc{0, 0, 0, 0};
     __syncthreads();
     for (int s = 0; s < n; s += 4) {
       step(s, b0, b3);
@@ -455,6 +481,17 @@ __global__ __launch_bounds__(WAVES * 64)
       step(s + 2, b2, b1);
       step(s + 3, b3, b2);
     }
+
+    // This tile's epilogue state; then the next tile's set-up and loads.
+    const int mt = t_mt, nt = t_nt, e = t_e, nvalid = t_nvalid;
+    const float row_scale = t_scale;
+    int enrow[NSUB];
+#pragma unroll
+    for (int s = 0; s < NSUB; s++) enrow[s] = nrow[s];
+    const int ebuf = buf;
+    const int wn = wi + per_xcd;
+    const bool more = wn < w_end;  // the same for the whole block
+    if (more) setup(wn, buf ^ 1);
 
     // ------------------------------------------------------------ epilogue
     // Phase 1: registers -> LDS tile (row = tile row, column = the block's
@@ -464,28 +501,35 @@ __global__ __launch_bounds__(WAVES * 64)
 #pragma unroll
     for (int m = 0; m < MSUB; m++) {
       if (m < mvalid) {
+        // This lane's four rows m*16 + lq*4 + r: their ids and scales in
+        // one 16-byte LDS read each.
+        const int4 rid = *reinterpret_cast<const int4*>(&sRow[ebuf][m * 16 + lq * 4]);
+        float4 rsc = make_float4(1.f, 1.f, 1.f, 1.f);
+        if constexpr (S != kW4A16) rsc = *reinterpret_cast<const float4*>(&sScale[m * 16 + lq * 4]);
+        const int rids[4] = {rid.x, rid.y, rid.z, rid.w};
+        const float rscs[4] = {rsc.x, rsc.y, rsc.z, rsc.w};
 #pragma unroll
         for (int r = 0; r < 4; r++) {
           const int row = m * 16 + lq * 4 + r;
           const size_t orow = (size_t)mt * BM + row;
           uint8_t* trow = smem + row * EPITCH;
           if constexpr (STAGE == 1) {
-            const int tok = sRow[row];
+            const int tok = rids[r];
 #pragma unroll
             for (int s = 0; s < HALF; s++) {
               const int cl = wave * HALF * 16 + s * 16 + lr;  // h column inside the tile
               float gf, uf;
               if constexpr (S == kW8A8) {
                 const float* ws = reinterpret_cast<const float*>(g.b_scale) + (size_t)e * g.N;
-                const float xs = sScale[row];
-                gf = ((float)acc[m][s][r] * xs) * ws[nrow[s]];
-                uf = ((float)acc[m][s + HALF][r] * xs) * ws[nrow[s + HALF]];
+                const float xs = rscs[r];
+                gf = ((float)acc[m][s][r] * xs) * ws[enrow[s]];
+                uf = ((float)acc[m][s + HALF][r] * xs) * ws[enrow[s + HALF]];
                 if (g.dump != nullptr && tok >= 0) {
-                  g.dump[orow * 2 * g.I + nrow[s]] = acc[m][s][r];
-                  g.dump[orow * 2 * g.I + nrow[s + HALF]] = acc[m][s + HALF][r];
+                  g.dump[orow * 2 * g.I + enrow[s]] = acc[m][s][r];
+                  g.dump[orow * 2 * g.I + enrow[s + HALF]] = acc[m][s + HALF][r];
                 }
               } else if constexpr (S == kA8W4) {
-                const float xs = sScale[row];
+                const float xs = rscs[r];
                 gf = acc[m][s][r] * xs;
                 uf = acc[m][s + HALF][r] * xs;
               } else {
@@ -499,17 +543,16 @@ __global__ __launch_bounds__(WAVES * 64)
                 *reinterpret_cast<float*>(trow + cl * 4) = h;
             }
           } else {
-            const int pair = sRow[row];
-            float rs = 1.f;
-            if constexpr (S != kW4A16) rs = sScale[row];
+            const int pair = rids[r];
+            const float rs = rscs[r];
 #pragma unroll
             for (int s = 0; s < NSUB; s++) {
               const int cl = wave * NSUB * 16 + s * 16 + lr;  // output column inside the tile
               if constexpr (S == kW8A8) {
                 const float ws2 =
-                    reinterpret_cast<const float*>(g.b_scale)[(size_t)e * g.N + nrow[s]];
+                    reinterpret_cast<const float*>(g.b_scale)[(size_t)e * g.N + enrow[s]];
                 *reinterpret_cast<float*>(trow + cl * 4) = ((float)acc[m][s][r] * rs) * ws2;
-                if (g.dump != nullptr && pair >= 0) g.dump[orow * g.H + nrow[s]] = acc[m][s][r];
+                if (g.dump != nullptr && pair >= 0) g.dump[orow * g.H + enrow[s]] = acc[m][s][r];
               } else if constexpr (S == kA8W4) {
                 *reinterpret_cast<__bf16*>(trow + cl * 2) = (__bf16)(acc[m][s][r] * rs);
               } else {
@@ -549,11 +592,15 @@ __global__ __launch_bounds__(WAVES * 64)
         } else {
           if (ok)
             __builtin_nontemporal_store(
-                v, reinterpret_cast<u32x4*>(O + (size_t)sRow[row] * g.H * OUT_ES +
+                v, reinterpret_cast<u32x4*>(O + (size_t)sRow[ebuf][row] * g.H * OUT_ES +
                                             (size_t)nt * COLS * OUT_ES + chunk * 16));
         }
       }
     }
+    if (!more) break;
+    wi = wn;
+    buf ^= 1;
+    __syncthreads();  // the epilogue is done with the LDS tile before the next store_a
   }
 }
 
