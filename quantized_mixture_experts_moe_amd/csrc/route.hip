@@ -7,16 +7,55 @@
 // softmax of the picked logits because the full denominator cancels.
 //
 // One wave per token.  Each lane keeps EPL logits in registers (expert
-// e = lane + 64*i); k rounds of a wave-wide arg-max with (value desc, index
-// asc) ordering pick the experts in slot order.  The weights use fp64 exp
-// so that they match a correctly rounded fp32 result.
+// e = lane + 64*i) as 64-bit sortable keys: the high word orders the fp32
+// values, the low word is ~e, so the largest key is the largest logit with
+// the lowest index among equal ones.  k rounds of a wave-wide maximum pick
+// the experts in slot order; the maximum runs on DPP row operations inside
+// each 16-lane row and four lane reads across the rows (no LDS traffic).
+// The weights use fp64 exp so that they match a correctly rounded fp32
+// result.
 #include "qmoe_internal.h"
 
 namespace qmoe {
 namespace {
 
-__device__ inline bool better(float va, int ia, float vb, int ib) {
-  return va > vb || (va == vb && ia < ib);
+typedef unsigned long long u64;
+
+__device__ inline u64 make_key(float v, int e) {
+  const uint32_t b = __float_as_uint(v);
+  const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((u64)ord << 32) | (uint32_t)~(uint32_t)e;
+}
+
+__device__ inline float key_value(u64 k) {
+  const uint32_t ord = (uint32_t)(k >> 32);
+  const uint32_t b = (ord & 0x80000000u) ? (ord & 0x7fffffffu) : ~ord;
+  return __uint_as_float(b);
+}
+
+template <int CTRL>
+__device__ inline u64 dpp_max(u64 x) {
+  const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)x, CTRL, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(x >> 32), CTRL, 0xf, 0xf, false);
+  const u64 y = ((u64)(uint32_t)hi << 32) | (uint32_t)lo;
+  return y > x ? y : x;
+}
+
+// Maximum of x over the 64 lanes, returned in every lane.
+__device__ inline u64 wave_max(u64 x) {
+  x = dpp_max<0xB1>(x);   // quad_perm [1,0,3,2]
+  x = dpp_max<0x4E>(x);   // quad_perm [2,3,0,1]
+  x = dpp_max<0x141>(x);  // row_half_mirror: the two quads of each half-row
+  x = dpp_max<0x140>(x);  // row_mirror: the two halves of each row
+  u64 best = 0;
+#pragma unroll
+  for (int r = 0; r < 4; r++) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, 16 * r);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), 16 * r);
+    const u64 y = ((u64)hi << 32) | lo;
+    best = y > best ? y : best;
+  }
+  return best;
 }
 
 template <int EPL>
@@ -27,36 +66,26 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;  // whole wave leaves together
   const float* row = logits + (size_t)t * E;
-  float v[EPL];
+  u64 key[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; i++) {
     const int e = lane + 64 * i;
-    v[i] = e < E ? row[e] : -__builtin_huge_valf();
+    key[i] = e < E ? make_key(row[e], e) : 0ull;  // 0 sorts below every real key
   }
-  uint64_t taken = 0;
   float top0 = 0.f, my_v = 0.f;
   int my_e = 0;
   for (int j = 0; j < k; j++) {
-    float bv = -__builtin_huge_valf();
-    int bi = 0x7fffffff;
+    u64 mine = key[0];
 #pragma unroll
-    for (int i = 0; i < EPL; i++) {
-      const int e = lane + 64 * i;
-      if (e < E && !((taken >> i) & 1) && better(v[i], e, bv, bi)) {
-        bv = v[i];
-        bi = e;
-      }
-    }
+    for (int i = 1; i < EPL; i++) mine = key[i] > mine ? key[i] : mine;
+    const u64 best = wave_max(mine);
+    const int bi = (int)~(uint32_t)best;
+    const float bv = key_value(best);
+    if ((bi & 63) == lane) {
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off, 64);
-      const int oi = __shfl_xor(bi, off, 64);
-      if (better(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
-      }
+      for (int i = 0; i < EPL; i++)
+        if (i == (bi >> 6)) key[i] = 0ull;  // taken
     }
-    if ((bi & 63) == lane) taken |= 1ull << (bi >> 6);
     if (j == 0) top0 = bv;
     if (lane == j) {
       my_v = bv;
