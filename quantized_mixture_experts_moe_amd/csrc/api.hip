@@ -278,7 +278,22 @@ static qmoe_status grouped_ffn_impl(const qmoe_ffn_desc* d, const void* x, const
 
   g2.N = d->H;
   g2.K = d->I;
-  g2.ntiles_n = d->H / stage_cols(2, gs2.nsub, gs2.waves);
+  const bool resident = stage2_resident_ok(d->scheme, d->I);
+  int passes = 1;
+  if (resident) {
+    // Column passes per work item: as many as keep at least four items per
+    // CU (by the capacity's tile count), so every item copies its rows to
+    // LDS once for as many passes as possible.
+    g2.ntiles_n = d->H / stage2_resident_cols();
+    const long tiles = (long)cap / d->block_m;
+    for (int p = g2.ntiles_n; p >= 1; p--) {
+      if (g2.ntiles_n % p != 0) continue;
+      passes = p;
+      if (tiles * (g2.ntiles_n / p) >= 4L * device_cu_count()) break;
+    }
+  } else {
+    g2.ntiles_n = d->H / stage_cols(2, gs2.nsub, gs2.waves);
+  }
   g2.a = quant_act ? (const void*)(wsb + lay.hq) : (const void*)(wsb + lay.h);
   g2.a_scale = quant_act ? reinterpret_cast<const float*>(wsb + lay.hs) : nullptr;
   g2.b = w->w2;
@@ -286,7 +301,8 @@ static qmoe_status grouped_ffn_impl(const qmoe_ffn_desc* d, const void* x, const
   g2.out = y_pairs;
   g2.row_pmax = nullptr;
   g2.dump = dump ? reinterpret_cast<int32_t*>(wsb + lay.acc2) : nullptr;
-  e = launch_gemm(d->scheme, 2, d->block_m, packed, gs2.nsub, gs2.waves, g2, s);
+  e = resident ? launch_stage2_resident(d->scheme, d->block_m, packed, g2, passes, s)
+               : launch_gemm(d->scheme, 2, d->block_m, packed, gs2.nsub, gs2.waves, g2, s);
   if (e == hipSuccess) e = mark(3);
   return hip_status(e);
 }

@@ -44,183 +44,13 @@
 // Schedule: a persistent grid (a multiple of 8 blocks, one slice of the work
 // list per XCD); work item = (row tile, column tile), row tile major, so the
 // blocks of one XCD share the same gathered activation rows in their L2.
-#include <hip/hip_fp16.h>
-
-#include "qmoe_internal.h"
+#include "gemm_common.h"
 
 namespace qmoe {
 namespace {
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-// Native 16-byte vector (HIP's uint4 is a struct, which keeps arrays of it
-// out of registers).
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+using namespace gk;
 
-enum { kW4A16 = 0, kW8A8 = 1, kA8W4 = 2 };
-
-// s_waitcnt immediate (gfx9 encoding) waiting for vmcnt == 0 only:
-// vmcnt bits [3:0] and [15:14] = 0, expcnt [6:4] = 7, lgkmcnt [11:8] = 15.
-constexpr int kWaitVmcnt0 = 0x0F70;
-
-template <int S>
-struct Tr;
-template <>
-struct Tr<kW4A16> {
-  static constexpr int BK = 128;      // K elements per pipeline step
-  static constexpr int A_ELEM = 2;    // bytes per activation element (bf16)
-  static constexpr int A_STEP = 256;  // activation bytes per row per step
-  static constexpr int A_FRAG = 64;   // activation bytes per lane per 16-row group per step
-  static constexpr int B_STEP = 64;   // weight bytes per row per step (int4)
-  static constexpr int B_FRAG = 16;   // weight bytes per lane per sub-tile per step
-  static constexpr int KB_NUM = 1, KB_DEN = 2;  // weight bytes per K element
-  typedef f32x4 Acc;
-};
-template <>
-struct Tr<kW8A8> {
-  static constexpr int BK = 128;
-  static constexpr int A_ELEM = 1;
-  static constexpr int A_STEP = 128;
-  static constexpr int A_FRAG = 32;
-  static constexpr int B_STEP = 128;
-  static constexpr int B_FRAG = 32;
-  static constexpr int KB_NUM = 1, KB_DEN = 1;
-  typedef i32x4 Acc;
-};
-template <>
-struct Tr<kA8W4> {
-  static constexpr int BK = 256;
-  static constexpr int A_ELEM = 1;
-  static constexpr int A_STEP = 256;
-  static constexpr int A_FRAG = 64;
-  static constexpr int B_STEP = 128;
-  static constexpr int B_FRAG = 32;
-  static constexpr int KB_NUM = 1, KB_DEN = 2;
-  typedef f32x4 Acc;
-};
-
-// Byte offset, inside a staged activation row of one step, of the f-th
-// 16-byte piece of lane group q's A fragment (a8w4: pieces 2j, 2j+1 feed
-// MFMA j; w8a8 and w4a16: piece j feeds MFMA j).  With the streaming weight
-// layout every MFMA of a step covers one contiguous K range, so the pieces
-// sit at 16q + 64f for the 8-bit schemes (a pattern free of LDS bank
-// conflicts on gfx950, measured); the canonical layout keeps each lane's
-// weight bytes contiguous and the A pieces follow it.
-template <int S, bool PK>
-__device__ inline int a_frag_offset(int q, int f) {
-  if constexpr (PK && S != kW4A16) {
-    return 16 * q + 64 * f;
-  } else if constexpr (S == kA8W4) {
-    // B lane group q holds the 32-K blocks 2q (MFMA 0) and 2q+1 (MFMA 1) of
-    // the 256-K step, so MFMA j's logical block b is step block 2b + j.  The
-    // fp8 halves of lane group q map to logical K 16q and 64 + 16q.
-    const int o = 64 * (q >> 1) + 16 * (q & 1);
-    const int j = f >> 1, half = f & 1;
-    return o + 32 * j + 128 * half;
-  } else {
-    return q * Tr<S>::A_FRAG + 16 * f;
-  }
-}
-
-// Weight fragment of one 16-column sub-tile for one step.
-template <int S>
-struct BFrag {
-  u32x4 q[Tr<S>::B_FRAG / 16];
-  uint32_t sc;  // w4a16: fp16 group scale bits; a8w4: two e8m0 bytes; w8a8: unused
-};
-
-__device__ inline bf16x8 dequant8_bf16(uint32_t v, float sc) {
-  bf16x8 r;
-#pragma unroll
-  for (int i = 0; i < 8; i++) {
-    const int q = __builtin_amdgcn_sbfe((int)v, 4 * i, 4);  // two's-complement nibble
-    r[i] = (__bf16)((float)q * sc);                          // exact product, one RNE rounding
-  }
-  return r;
-}
-
-// A step's weight fragment in the form the MFMAs take: w4a16 dequantizes
-// its int4 codes to bf16 once per step (the result is reused by every
-// 16-row group of the tile); the 8-bit schemes feed the codes as they are.
-template <int S>
-struct BReady {
-  BFrag<S> f;
-};
-template <>
-struct BReady<kW4A16> {
-  bf16x8 v[4];
-};
-
-template <int S>
-__device__ inline BReady<S> prepare_b(const BFrag<S>& b) {
-  if constexpr (S == kW4A16) {
-    BReady<S> r;
-    const float sc = __half2float(__ushort_as_half((unsigned short)b.sc));
-    r.v[0] = dequant8_bf16(b.q[0].x, sc);
-    r.v[1] = dequant8_bf16(b.q[0].y, sc);
-    r.v[2] = dequant8_bf16(b.q[0].z, sc);
-    r.v[3] = dequant8_bf16(b.q[0].w, sc);
-    return r;
-  } else {
-    return BReady<S>{b};
-  }
-}
-
-template <int S>
-__device__ inline void mfma_step(typename Tr<S>::Acc& acc, const u32x4* a, const BReady<S>& br) {
-  if constexpr (S == kW4A16) {
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const bf16x8 av = __builtin_bit_cast(bf16x8, a[j]);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, br.v[j], acc, 0, 0, 0);
-    }
-  } else if constexpr (S == kW8A8) {
-    const BFrag<S>& b = br.f;
-#pragma unroll
-    for (int j = 0; j < 2; j++) {
-      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, a[j]),
-                                                 __builtin_bit_cast(i32x4, b.q[j]), acc, 0, 0, 0);
-    }
-  } else {
-    const BFrag<S>& b = br.f;
-    // A fp8 (format 0) with unit scale 2^0 (e8m0 127); B fp4 (format 4) with
-    // the e8m0 byte of its 32-wide block: byte 0 for MFMA 0, byte 1 for
-    // MFMA 1.
-    const i32x8 a0 = {(int)a[0].x, (int)a[0].y, (int)a[0].z, (int)a[0].w,
-                      (int)a[1].x, (int)a[1].y, (int)a[1].z, (int)a[1].w};
-    const i32x8 a1 = {(int)a[2].x, (int)a[2].y, (int)a[2].z, (int)a[2].w,
-                      (int)a[3].x, (int)a[3].y, (int)a[3].z, (int)a[3].w};
-    const i32x8 b0 = {(int)b.q[0].x, (int)b.q[0].y, (int)b.q[0].z, (int)b.q[0].w, 0, 0, 0, 0};
-    const i32x8 b1 = {(int)b.q[1].x, (int)b.q[1].y, (int)b.q[1].z, (int)b.q[1].w, 0, 0, 0, 0};
-    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a0, b0, acc, 0, 4, 0, 127, 0,
-                                                           (int)b.sc);
-    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a1, b1, acc, 0, 4, 0, 127, 1,
-                                                           (int)b.sc);
-  }
-}
-
-// SiLU(gate) * up in the stage-1 epilogue.
-// w8a8 follows the bit-exact fp32 recipe: ex = f32(exp_f64(-g));
-// sg = g / (1 + ex) (IEEE division); h = sg * u.
-// w4a16 and a8w4 use the hardware exp2 and reciprocal (a few ulp each; the
-// library expf and IEEE division cost ~25 more instructions per element, a
-// measured third of the tile epilogue):
-// ex = exp2(-g * log2(e)); sg = g * rcp(1 + ex); h = sg * u.
-template <int S>
-__device__ inline float silu_mul(float g, float u) {
-  if constexpr (S == kW8A8) {
-    const float ex = (float)exp(-(double)g);
-    const float den = 1.0f + ex;
-    const float sg = g / den;
-    return sg * u;
-  } else {
-    const float ex = __builtin_amdgcn_exp2f(-g * 1.44269504088896341f);
-    const float sg = g * __builtin_amdgcn_rcpf(1.0f + ex);
-    return sg * u;
-  }
-}
 
 template <int S, int STAGE, int BM, bool PK, int NSUB, int WAVES>
 __global__ __launch_bounds__(WAVES * 64)
@@ -247,6 +77,7 @@ __global__ __launch_bounds__(WAVES * 64)
   // Row ids of the tile being set up and of the tile in its epilogue.
   __shared__ __attribute__((aligned(16))) int sRow[2][BM];
   __shared__ __attribute__((aligned(16))) float sScale[BM];
+  __shared__ int sExpert[2];
   auto sA = [&](int stage) __attribute__((always_inline)) { return smem + stage * BM * PITCH; };
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -259,6 +90,7 @@ __global__ __launch_bounds__(WAVES * 64)
   const int w_begin = xcd * chunk, w_end = min(total, w_begin + chunk);
 
   static_assert(kThreads % CPR == 0, "chunk rows must be thread-invariant");
+  static_assert(BM < kThreads, "the last thread loads the tile's expert id");
   const int lds_w = (tid / CPR) * PITCH + (tid % CPR) * 16;  // this thread's LDS store slot
   const size_t K = (size_t)g.K;
   const size_t kbytes = K * T_::KB_NUM / T_::KB_DEN;  // weight bytes per row
@@ -268,12 +100,16 @@ __global__ __launch_bounds__(WAVES * 64)
 
   // Tile metadata (pair ids of the rows, the expert) is fetched one tile
   // ahead of the tile's set-up.
+  // The tile's expert id is the same for the whole block, but it is loaded
+  // by one thread only (the last one, never a row thread) and passed on
+  // through LDS at the set-up barrier: a uniform load would be moved to a
+  // scalar register right away, waiting for every load in flight.
   int next_pair = g.P, next_expert = 0;
   auto fetch_meta = [&](int w) __attribute__((always_inline)) {
     if (w < w_end) {
       const int m = w / g.ntiles_n;
       if (tid < BM) next_pair = g.sorted_pair_ids[m * BM + tid];
-      next_expert = g.tile_expert[m];
+      if (tid == kThreads - 1) next_expert = g.tile_expert[m];
     }
   };
 
@@ -293,6 +129,10 @@ __global__ __launch_bounds__(WAVES * 64)
   const uint8_t* __restrict__ Bexp = B;
   const uint8_t* __restrict__ Sexp = reinterpret_cast<const uint8_t*>(g.b_scale);
   uint32_t boff[NSUB], soff[NSUB], aoff[NCH];
+  // Bit offset of this lane's scale field in its aligned 32-bit word: the
+  // field sits at byte 2*lane (streaming layout) or 2*lq (canonical) of a
+  // 4-byte aligned run.
+  const uint32_t sshift = ((PK ? lane : lq) & 1) * 16;
 
   auto load_b = [&](BFrag<S>(&bf)[NSUB], int ks) __attribute__((always_inline)) {
 #pragma unroll
@@ -301,9 +141,12 @@ __global__ __launch_bounds__(WAVES * 64)
 #pragma unroll
       for (int i = 0; i < T_::B_FRAG / 16; i++)
         bf[s].q[i] = *reinterpret_cast<const u32x4*>(Bexp + (uint32_t)(o + B_PIECE * i));
+      // The lane's two scale bytes as part of the aligned 32-bit word that
+      // holds them (a 16-bit load is zero-extended in the loop, which made
+      // every fourth step wait for all loads in flight).
       if (S == kW4A16 || S == kA8W4)
-        bf[s].sc =
-            *reinterpret_cast<const unsigned short*>(Sexp + (uint32_t)(soff[s] + ks * S_KS));
+        bf[s].sc = *reinterpret_cast<const uint32_t*>(
+            Sexp + ((uint32_t)(soff[s] + ks * S_KS) & ~3u));
       else
         bf[s].sc = 0;
     }
@@ -336,7 +179,7 @@ __global__ __launch_bounds__(WAVES * 64)
   auto setup = [&](int w, int bf) __attribute__((always_inline)) {
     t_mt = w / g.ntiles_n;
     t_nt = w - t_mt * g.ntiles_n;
-    t_e = next_expert;
+    if (tid == kThreads - 1) sExpert[bf] = next_expert;
     int valid_here = 0;
     if (tid < BM) {
       const int p = next_pair;
@@ -351,6 +194,7 @@ __global__ __launch_bounds__(WAVES * 64)
     }
     t_nvalid = __syncthreads_count(valid_here);
     t_mvalid = (t_nvalid + 15) >> 4;
+    t_e = sExpert[bf];
     fetch_meta(w + per_xcd);
     // Weight rows of this wave's sub-tiles, as 32-bit offsets from the
     // expert's base (one expert's weights are far below 4 GiB).
@@ -418,7 +262,7 @@ __global__ __launch_bounds__(WAVES * 64)
     auto compute = [&](int stage, const BFrag<S>(&bcr)[NSUB]) __attribute__((always_inline)) {
       BReady<S> bc[NSUB];
 #pragma unroll
-      for (int s = 0; s < NSUB; s++) bc[s] = prepare_b<S>(bcr[s]);
+      for (int s = 0; s < NSUB; s++) bc[s] = prepare_b<S>(bcr[s], sshift);
       u32x4 fa[NF], fb[NF];
       if constexpr (FRAG2) read_frag(fa, stage, 0);
 #pragma unroll

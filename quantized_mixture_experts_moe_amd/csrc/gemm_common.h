@@ -1,0 +1,188 @@
+// Building blocks shared by the grouped-GEMM kernels (not installed): the
+// per-scheme step geometry, weight fragments, the MFMA step of each scheme
+// and the SiLU epilogue recipe.
+#pragma once
+#include <hip/hip_fp16.h>
+
+#include "qmoe_internal.h"
+
+namespace qmoe {
+namespace gk {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+// Native 16-byte vector (HIP's uint4 is a struct, which keeps arrays of it
+// out of registers).
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+enum { kW4A16 = 0, kW8A8 = 1, kA8W4 = 2 };
+
+// s_waitcnt immediate (gfx9 encoding) waiting for vmcnt == 0 only:
+// vmcnt bits [3:0] and [15:14] = 0, expcnt [6:4] = 7, lgkmcnt [11:8] = 15.
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+template <int S>
+struct Tr;
+template <>
+struct Tr<kW4A16> {
+  static constexpr int BK = 128;      // K elements per pipeline step
+  static constexpr int A_ELEM = 2;    // bytes per activation element (bf16)
+  static constexpr int A_STEP = 256;  // activation bytes per row per step
+  static constexpr int A_FRAG = 64;   // activation bytes per lane per 16-row group per step
+  static constexpr int B_STEP = 64;   // weight bytes per row per step (int4)
+  static constexpr int B_FRAG = 16;   // weight bytes per lane per sub-tile per step
+  static constexpr int KB_NUM = 1, KB_DEN = 2;  // weight bytes per K element
+  typedef f32x4 Acc;
+};
+template <>
+struct Tr<kW8A8> {
+  static constexpr int BK = 128;
+  static constexpr int A_ELEM = 1;
+  static constexpr int A_STEP = 128;
+  static constexpr int A_FRAG = 32;
+  static constexpr int B_STEP = 128;
+  static constexpr int B_FRAG = 32;
+  static constexpr int KB_NUM = 1, KB_DEN = 1;
+  typedef i32x4 Acc;
+};
+template <>
+struct Tr<kA8W4> {
+  static constexpr int BK = 256;
+  static constexpr int A_ELEM = 1;
+  static constexpr int A_STEP = 256;
+  static constexpr int A_FRAG = 64;
+  static constexpr int B_STEP = 128;
+  static constexpr int B_FRAG = 32;
+  static constexpr int KB_NUM = 1, KB_DEN = 2;
+  typedef f32x4 Acc;
+};
+
+// Byte offset, inside a staged activation row of one step, of the f-th
+// 16-byte piece of lane group q's A fragment (a8w4: pieces 2j, 2j+1 feed
+// MFMA j; w8a8 and w4a16: piece j feeds MFMA j).  With the streaming weight
+// layout every MFMA of a step covers one contiguous K range, so the pieces
+// sit at 16q + 64f for the 8-bit schemes (a pattern free of LDS bank
+// conflicts on gfx950, measured); the canonical layout keeps each lane's
+// weight bytes contiguous and the A pieces follow it.
+template <int S, bool PK>
+__device__ inline int a_frag_offset(int q, int f) {
+  if constexpr (PK && S != kW4A16) {
+    return 16 * q + 64 * f;
+  } else if constexpr (S == kA8W4) {
+    // B lane group q holds the 32-K blocks 2q (MFMA 0) and 2q+1 (MFMA 1) of
+    // the 256-K step, so MFMA j's logical block b is step block 2b + j.  The
+    // fp8 halves of lane group q map to logical K 16q and 64 + 16q.
+    const int o = 64 * (q >> 1) + 16 * (q & 1);
+    const int j = f >> 1, half = f & 1;
+    return o + 32 * j + 128 * half;
+  } else {
+    return q * Tr<S>::A_FRAG + 16 * f;
+  }
+}
+
+// Weight fragment of one 16-column sub-tile for one step.
+template <int S>
+struct BFrag {
+  u32x4 q[Tr<S>::B_FRAG / 16];
+  uint32_t sc;  // w4a16: fp16 group scale bits; a8w4: two e8m0 bytes; w8a8: unused
+};
+
+__device__ inline bf16x8 dequant8_bf16(uint32_t v, float sc) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const int q = __builtin_amdgcn_sbfe((int)v, 4 * i, 4);  // two's-complement nibble
+    r[i] = (__bf16)((float)q * sc);                          // exact product, one RNE rounding
+  }
+  return r;
+}
+
+// A step's weight fragment in the form the MFMAs take: w4a16 dequantizes
+// its int4 codes to bf16 once per step (the result is reused by every
+// 16-row group of the tile); the 8-bit schemes feed the codes as they are.
+template <int S>
+struct BReady {
+  BFrag<S> f;
+};
+template <>
+struct BReady<kW4A16> {
+  bf16x8 v[4];
+};
+
+// `sshift` (0 or 16) picks this lane's 16-bit scale field out of the
+// aligned 32-bit word the weight loads fetch.
+template <int S>
+__device__ inline BReady<S> prepare_b(const BFrag<S>& b, uint32_t sshift) {
+  if constexpr (S == kW4A16) {
+    BReady<S> r;
+    const float sc = __half2float(__ushort_as_half((unsigned short)(b.sc >> sshift)));
+    r.v[0] = dequant8_bf16(b.q[0].x, sc);
+    r.v[1] = dequant8_bf16(b.q[0].y, sc);
+    r.v[2] = dequant8_bf16(b.q[0].z, sc);
+    r.v[3] = dequant8_bf16(b.q[0].w, sc);
+    return r;
+  } else {
+    BReady<S> r{b};
+    r.f.sc = b.sc >> sshift;
+    return r;
+  }
+}
+
+template <int S>
+__device__ inline void mfma_step(typename Tr<S>::Acc& acc, const u32x4* a, const BReady<S>& br) {
+  if constexpr (S == kW4A16) {
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const bf16x8 av = __builtin_bit_cast(bf16x8, a[j]);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, br.v[j], acc, 0, 0, 0);
+    }
+  } else if constexpr (S == kW8A8) {
+    const BFrag<S>& b = br.f;
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, a[j]),
+                                                 __builtin_bit_cast(i32x4, b.q[j]), acc, 0, 0, 0);
+    }
+  } else {
+    const BFrag<S>& b = br.f;
+    // A fp8 (format 0) with unit scale 2^0 (e8m0 127); B fp4 (format 4) with
+    // the e8m0 byte of its 32-wide block: byte 0 for MFMA 0, byte 1 for
+    // MFMA 1.
+    const i32x8 a0 = {(int)a[0].x, (int)a[0].y, (int)a[0].z, (int)a[0].w,
+                      (int)a[1].x, (int)a[1].y, (int)a[1].z, (int)a[1].w};
+    const i32x8 a1 = {(int)a[2].x, (int)a[2].y, (int)a[2].z, (int)a[2].w,
+                      (int)a[3].x, (int)a[3].y, (int)a[3].z, (int)a[3].w};
+    const i32x8 b0 = {(int)b.q[0].x, (int)b.q[0].y, (int)b.q[0].z, (int)b.q[0].w, 0, 0, 0, 0};
+    const i32x8 b1 = {(int)b.q[1].x, (int)b.q[1].y, (int)b.q[1].z, (int)b.q[1].w, 0, 0, 0, 0};
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a0, b0, acc, 0, 4, 0, 127, 0,
+                                                           (int)b.sc);
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a1, b1, acc, 0, 4, 0, 127, 1,
+                                                           (int)b.sc);
+  }
+}
+
+// SiLU(gate) * up in the stage-1 epilogue.
+// w8a8 follows the bit-exact fp32 recipe: ex = f32(exp_f64(-g));
+// sg = g / (1 + ex) (IEEE division); h = sg * u.
+// w4a16 and a8w4 use the hardware exp2 and reciprocal (a few ulp each; the
+// library expf and IEEE division cost ~25 more instructions per element, a
+// measured third of the tile epilogue):
+// ex = exp2(-g * log2(e)); sg = g * rcp(1 + ex); h = sg * u.
+template <int S>
+__device__ inline float silu_mul(float g, float u) {
+  if constexpr (S == kW8A8) {
+    const float ex = (float)exp(-(double)g);
+    const float den = 1.0f + ex;
+    const float sg = g / den;
+    return sg * u;
+  } else {
+    const float ex = __builtin_amdgcn_exp2f(-g * 1.44269504088896341f);
+    const float sg = g * __builtin_amdgcn_rcpf(1.0f + ex);
+    return sg * u;
+  }
+}
+
+}  // namespace gk
+}  // namespace qmoe

@@ -1,0 +1,295 @@
+// Stage 2 (down projection) of the grouped FFN with the tile's activation
+// rows resident in LDS (aiter PR 6090, Test Plan: stage2 tiles; hip-ep PR
+// "perf(qmoe): group prefill expert matmuls": one launch for every expert).
+//
+//   y_pairs[pair(row)] = h[row] . W2[e]^T,  rescaled by the row's h scale
+//
+// For the schemes whose stage-2 activations are one byte (a8w4 fp8, W8A8
+// int8), a row tile's h rows (BM x I bytes, I <= 1024) fit in LDS.  A work
+// item is (row tile, chunk of `passes` column passes of 256 outputs): the
+// block copies the rows into LDS once, then streams the expert's W2 rows for
+// every pass of the chunk through a register ring that runs three K steps
+// ahead across pass boundaries.  No barrier is needed between steps (the
+// activations are read-only), and no activation row is loaded again.
+//
+// One block = 8 waves (two per SIMD), one block per CU; each wave owns two
+// 16-column weight sub-tiles.  The MFMAs take the weight fragment as the A
+// operand and the activation fragment as the B operand, so a lane's four
+// accumulators are four consecutive output columns of one row, stored
+// straight from registers (8 bytes of bf16, 16 bytes of fp32).  Operand
+// layouts are the ones the row-major kernel uses (measured on gfx950: the
+// fp4/fp8 pairing and the per-lane e8m0 scale routing do not depend on which
+// operand slot holds which format).
+#include "gemm_common.h"
+
+namespace qmoe {
+namespace {
+
+using namespace gk;
+
+constexpr int kS2Waves = 8;
+constexpr int kS2Threads = kS2Waves * 64;
+constexpr int kS2Nsub = 2;
+constexpr int kS2Cols = kS2Waves * kS2Nsub * 16;  // output columns per pass
+constexpr int kS2RowBytes = 1024;                 // largest activation row held in LDS
+constexpr int kS2Pitch = kS2RowBytes + 16;        // LDS row pitch (bank spread)
+
+// One MFMA step with the weight fragment as the A operand.
+template <int S>
+__device__ inline void mfma_step_wa(typename Tr<S>::Acc& acc, const u32x4* a,
+                                    const BFrag<S>& b) {
+  if constexpr (S == kW8A8) {
+#pragma unroll
+    for (int j = 0; j < 2; j++)
+      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, b.q[j]),
+                                                 __builtin_bit_cast(i32x4, a[j]), acc, 0, 0, 0);
+  } else {
+    // A = weights, fp4 (format 4) with the e8m0 byte of its 32-wide block
+    // per lane (byte 0 for MFMA 0, byte 1 for MFMA 1); B = activations, fp8
+    // (format 0) with unit scale.
+    const i32x8 a0 = {(int)a[0].x, (int)a[0].y, (int)a[0].z, (int)a[0].w,
+                      (int)a[1].x, (int)a[1].y, (int)a[1].z, (int)a[1].w};
+    const i32x8 a1 = {(int)a[2].x, (int)a[2].y, (int)a[2].z, (int)a[2].w,
+                      (int)a[3].x, (int)a[3].y, (int)a[3].z, (int)a[3].w};
+    const i32x8 b0 = {(int)b.q[0].x, (int)b.q[0].y, (int)b.q[0].z, (int)b.q[0].w, 0, 0, 0, 0};
+    const i32x8 b1 = {(int)b.q[1].x, (int)b.q[1].y, (int)b.q[1].z, (int)b.q[1].w, 0, 0, 0, 0};
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b0, a0, acc, 4, 0, 0, (int)b.sc, 0,
+                                                           127);
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b1, a1, acc, 4, 0, 1, (int)b.sc, 0,
+                                                           127);
+  }
+}
+
+template <int S, int BM, bool PK>
+__global__ __launch_bounds__(kS2Threads) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+moe_stage2_resident(GemmArgs g, int passes) {
+  static_assert(S == kW8A8 || S == kA8W4, "one-byte activations only");
+  using T_ = Tr<S>;
+  using Acc = typename T_::Acc;
+  constexpr int MSUB = BM / 16;
+  constexpr int NF = T_::A_FRAG / 16;
+  __shared__ __attribute__((aligned(16))) uint8_t sA[BM * kS2Pitch];
+  __shared__ __attribute__((aligned(16))) int sRow[BM];
+  __shared__ __attribute__((aligned(16))) float sScale[BM];
+  __shared__ int sExpert;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lq = lane >> 4;
+  const int K = g.K;                     // = I; K bytes per activation row
+  const int nsteps = K / T_::BK;
+  const uint32_t kbytes = (uint32_t)(K * T_::KB_NUM / T_::KB_DEN);  // weight bytes per row
+  const int num_m = *g.num_padded / BM;
+  const int nchunk = g.ntiles_n / passes;
+  const int total = num_m * nchunk;
+  const int per_xcd = gridDim.x >> 3;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int chunk = (total + 7) >> 3;
+  const int w_begin = xcd * chunk, w_end = min(total, w_begin + chunk);
+  const uint8_t* __restrict__ Aglob = reinterpret_cast<const uint8_t*>(g.a);
+  const uint8_t* __restrict__ B = reinterpret_cast<const uint8_t*>(g.b);
+  const uint32_t sshift = ((PK ? lane : lq) & 1) * 16;
+  constexpr uint32_t B_KS = PK ? 16 * T_::B_STEP : T_::B_STEP;
+  constexpr uint32_t B_PIECE = PK ? 1024 : 16;
+  constexpr uint32_t S_KS = PK ? 128 : 8;
+  constexpr int SB = 1;  // e8m0 bytes (a8w4); W8A8 scales are per channel
+  const int G = passes * nsteps;  // weight steps of an item
+
+  Acc acc[MSUB][kS2Nsub];
+  BFrag<S> b0[kS2Nsub], b1[kS2Nsub], b2[kS2Nsub], b3[kS2Nsub];
+
+  for (int wi = w_begin + slot; wi < w_end; wi += per_xcd) {
+    const int mt = wi / nchunk, c = wi - mt * nchunk;
+    __syncthreads();  // the previous item is done with sA / sRow / sScale
+    int valid_here = 0;
+    if (tid < BM) {
+      const int p = g.sorted_pair_ids[mt * BM + tid];
+      const bool ok = p < g.P;
+      sRow[tid] = ok ? p : -1;
+      sScale[tid] = ok ? g.a_scale[(size_t)mt * BM + tid] : 0.f;
+      valid_here = ok;
+    }
+    if (tid == kS2Threads - 1) sExpert = g.tile_expert[mt];
+    const int nvalid = __syncthreads_count(valid_here);
+    const int mvalid = (nvalid + 15) >> 4;
+    const int e = sExpert;
+
+    // Weight cursor: the load for global step gs of this item reads column
+    // pass gs / nsteps, K step gs % nsteps; steps past the item re-read its
+    // last step (cache hits), so every step has the same shape.
+    const uint8_t* __restrict__ Bexp = B + (size_t)e * g.N * kbytes;
+    const uint8_t* __restrict__ Sexp =
+        reinterpret_cast<const uint8_t*>(g.b_scale) + (size_t)e * g.N * (K / 32) * SB;
+    auto load_b = [&](BFrag<S>(&bf)[kS2Nsub], int gs) __attribute__((always_inline)) {
+      gs = min(gs, G - 1);
+      const int p = gs / nsteps, ks = gs - p * nsteps;
+      const int col0 = (c * passes + p) * kS2Cols + wave * kS2Nsub * 16;  // first weight row
+#pragma unroll
+      for (int s = 0; s < kS2Nsub; s++) {
+        const uint32_t g16 = (uint32_t)(col0 + s * 16);
+        uint32_t o, so;
+        if constexpr (PK) {
+          o = g16 * kbytes + lane * 16 + (uint32_t)ks * B_KS;
+          so = g16 * (uint32_t)(K / 32) * SB + lane * 2 + (uint32_t)ks * S_KS;
+        } else {
+          o = (g16 + lr) * kbytes + lq * T_::B_FRAG + (uint32_t)ks * B_KS;
+          so = (g16 + lr) * (uint32_t)(K / 32) * SB + lq * 2 + (uint32_t)ks * S_KS;
+        }
+#pragma unroll
+        for (int i = 0; i < T_::B_FRAG / 16; i++)
+          bf[s].q[i] = *reinterpret_cast<const u32x4*>(Bexp + (uint32_t)(o + B_PIECE * i));
+        if constexpr (S == kA8W4)
+          bf[s].sc = *reinterpret_cast<const uint32_t*>(Sexp + (so & ~3u));
+        else
+          bf[s].sc = 0;
+      }
+    };
+    load_b(b0, 0);
+    load_b(b1, 1);
+    load_b(b2, 2);
+
+    // The tile's activation rows (real rows and the rest of their 16-row
+    // group; those extra rows only feed discarded outputs) into LDS.
+    {
+      const int cpr = K * T_::A_ELEM / 16;  // 16-byte chunks per row
+      const int n = mvalid * 16 * cpr;
+      for (int i = tid; i < n; i += kS2Threads) {
+        const int r = i / cpr, cc = i - r * cpr;
+        *reinterpret_cast<u32x4*>(sA + r * kS2Pitch + cc * 16) = *reinterpret_cast<const u32x4*>(
+            Aglob + ((size_t)mt * BM + r) * (size_t)(K * T_::A_ELEM) + cc * 16);
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < MSUB; m++)
+#pragma unroll
+      for (int s = 0; s < kS2Nsub; s++) acc[m][s] = Acc{0, 0, 0, 0};
+    __syncthreads();
+
+    auto read_frag = [&](u32x4(&af)[NF], int ks, int m) __attribute__((always_inline)) {
+      const uint8_t* src = sA + (m * 16 + lr) * kS2Pitch + ks * T_::A_STEP;
+#pragma unroll
+      for (int f = 0; f < NF; f++)
+        af[f] = *reinterpret_cast<const u32x4*>(src + a_frag_offset<S, PK>(lq, f));
+    };
+    auto compute = [&](int ks, const BFrag<S>(&bcr)[kS2Nsub]) __attribute__((always_inline)) {
+      BFrag<S> bc[kS2Nsub];
+#pragma unroll
+      for (int s = 0; s < kS2Nsub; s++) {
+        bc[s] = bcr[s];
+        bc[s].sc = bcr[s].sc >> sshift;
+      }
+      u32x4 fa[NF], fb[NF];
+      read_frag(fa, ks, 0);
+#pragma unroll
+      for (int m = 0; m < MSUB; m++) {
+        if (m < mvalid) {
+          if (m + 1 < MSUB && m + 1 < mvalid) read_frag((m & 1) ? fa : fb, ks, m + 1);
+#pragma unroll
+          for (int s = 0; s < kS2Nsub; s++) mfma_step_wa<S>(acc[m][s], (m & 1) ? fb : fa, bc[s]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    // Outputs of column pass p: lane (lq, lr) holds, for row m*16 + lr,
+    // the four columns 4*lq .. 4*lq+3 of each sub-tile.
+    auto epilogue = [&](int p) __attribute__((always_inline)) {
+      const int colw = (c * passes + p) * kS2Cols + wave * kS2Nsub * 16 + 4 * lq;
+#pragma unroll
+      for (int m = 0; m < MSUB; m++) {
+        if (m < mvalid) {
+          const int row = m * 16 + lr;
+          const int pair = sRow[row];
+          const float rs = sScale[row];
+#pragma unroll
+          for (int s = 0; s < kS2Nsub; s++) {
+            const int col = colw + s * 16;
+            if constexpr (S == kA8W4) {
+              const __bf16 v0 = (__bf16)(acc[m][s][0] * rs), v1 = (__bf16)(acc[m][s][1] * rs);
+              const __bf16 v2 = (__bf16)(acc[m][s][2] * rs), v3 = (__bf16)(acc[m][s][3] * rs);
+              const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, v0) |
+                                  ((uint32_t)__builtin_bit_cast(uint16_t, v1) << 16);
+              const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, v2) |
+                                  ((uint32_t)__builtin_bit_cast(uint16_t, v3) << 16);
+              if (pair >= 0)
+                *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(g.out) +
+                                          (size_t)pair * g.H + col) = make_uint2(lo, hi);
+            } else {
+              const float4 ws = *reinterpret_cast<const float4*>(
+                  reinterpret_cast<const float*>(g.b_scale) + (size_t)e * g.N + col);
+              const float4 y = make_float4(((float)acc[m][s][0] * rs) * ws.x,
+                                           ((float)acc[m][s][1] * rs) * ws.y,
+                                           ((float)acc[m][s][2] * rs) * ws.z,
+                                           ((float)acc[m][s][3] * rs) * ws.w);
+              if (pair >= 0) {
+                *reinterpret_cast<float4*>(reinterpret_cast<float*>(g.out) + (size_t)pair * g.H +
+                                           col) = y;
+                if (g.dump != nullptr)
+                  *reinterpret_cast<int4*>(g.dump + ((size_t)mt * BM + row) * g.H + col) =
+                      make_int4(acc[m][s][0], acc[m][s][1], acc[m][s][2], acc[m][s][3]);
+              }
+            }
+            acc[m][s] = Acc{0, 0, 0, 0};
+          }
+        }
+      }
+    };
+
+    // Step gs computes with weight register set gs % 4 and loads step gs+3
+    // into the set that step gs-1 used.
+    auto step = [&](int gs, const BFrag<S>(&bc)[kS2Nsub], BFrag<S>(&bl)[kS2Nsub])
+        __attribute__((always_inline)) {
+      load_b(bl, gs + 3);
+      if (gs < G) {
+        const int p = gs / nsteps, ks = gs - p * nsteps;
+        compute(ks, bc);
+        if (ks == nsteps - 1) epilogue(p);
+      }
+    };
+    for (int gs = 0; gs < G; gs += 4) {
+      step(gs, b0, b3);
+      step(gs + 1, b1, b0);
+      step(gs + 2, b2, b1);
+      step(gs + 3, b3, b2);
+    }
+  }
+}
+
+template <int S, int BM, bool PK>
+hipError_t launch_s2r(const GemmArgs& g, int passes, hipStream_t s) {
+  int nblk = device_cu_count();
+  nblk = nblk < 8 ? 8 : (nblk / 8) * 8;
+  hipLaunchKernelGGL((moe_stage2_resident<S, BM, PK>), dim3(nblk), dim3(kS2Threads), 0, s, g,
+                     passes);
+  return hipGetLastError();
+}
+
+template <int S, bool PK>
+hipError_t launch_s2r_bm(int block_m, const GemmArgs& g, int passes, hipStream_t s) {
+  switch (block_m) {
+    case 16: return launch_s2r<S, 16, PK>(g, passes, s);
+    case 32: return launch_s2r<S, 32, PK>(g, passes, s);
+    case 64: return launch_s2r<S, 64, PK>(g, passes, s);
+    case 128: return launch_s2r<S, 128, PK>(g, passes, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+bool stage2_resident_ok(int scheme, int I) {
+  return (scheme == 1 || scheme == 2) && I <= kS2RowBytes;
+}
+
+int stage2_resident_cols() { return kS2Cols; }
+
+hipError_t launch_stage2_resident(int scheme, int block_m, bool packed, const GemmArgs& g,
+                                  int passes, hipStream_t s) {
+  if (scheme == 2)
+    return packed ? launch_s2r_bm<kA8W4, true>(block_m, g, passes, s)
+                  : launch_s2r_bm<kA8W4, false>(block_m, g, passes, s);
+  if (scheme == 1)
+    return packed ? launch_s2r_bm<kW8A8, true>(block_m, g, passes, s)
+                  : launch_s2r_bm<kW8A8, false>(block_m, g, passes, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace qmoe

@@ -47,6 +47,14 @@ hipError_t launch_align(const int32_t* ids, int T, int k, int E, int block_m, in
                         int32_t* flags, int cap, hipStream_t s);
 hipError_t launch_gemm(int scheme, int stage, int block_m, bool packed, int nsub, int waves,
                        const GemmArgs& g, hipStream_t s);
+// Stage 2 with the tile's activation rows resident in LDS (gemm_s2.hip):
+// available for the one-byte-activation schemes with I <= 1024; its column
+// passes are stage2_resident_cols() wide and a work item covers `passes`
+// of them (ntiles_n must be a multiple of passes).
+bool stage2_resident_ok(int scheme, int I);
+int stage2_resident_cols();
+hipError_t launch_stage2_resident(int scheme, int block_m, bool packed, const GemmArgs& g,
+                                  int passes, hipStream_t s);
 hipError_t launch_prepack(int scheme, int E, int N, int K, const void* codes, const void* scales,
                           void* codes_out, void* scales_out, hipStream_t s);
 hipError_t launch_requant(int scheme, const int32_t* sorted, const int32_t* num_padded,
