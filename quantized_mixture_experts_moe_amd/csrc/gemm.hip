@@ -44,6 +44,10 @@
 // Schedule: a persistent grid (a multiple of 8 blocks, one slice of the work
 // list per XCD); work item = (row tile, column tile), row tile major, so the
 // blocks of one XCD share the same gathered activation rows in their L2.
+// Between the tiles of a block the stream of loads does not stop: in stage 1
+// (K steps a multiple of four) the K loop's last three steps issue the next
+// tile's first activation and weight loads, and the epilogue runs while they
+// are in flight.
 #include "gemm_common.h"
 
 namespace qmoe {
@@ -52,7 +56,7 @@ namespace {
 using namespace gk;
 
 
-template <int S, int STAGE, int BM, bool PK, int NSUB, int WAVES>
+template <int S, int STAGE, int BM, bool PK, int NSUB, int WAVES, bool XT>
 __global__ __launch_bounds__(WAVES * 64)
     __attribute__((amdgpu_waves_per_eu(NSUB == 4 ? 1 : 2, NSUB == 4 ? 1 : 2))) void
     moe_gemm_kernel(GemmArgs g) {
@@ -66,14 +70,22 @@ __global__ __launch_bounds__(WAVES * 64)
   constexpr int NF = T_::A_FRAG / 16;                        // 16-byte LDS reads per fragment
   constexpr int HALF = NSUB / 2;                             // stage 1: gate sub-tiles per wave
 
-  // Epilogue tile: the block's BM x COLS outputs, staged in LDS (over the
-  // activation ring) so that global stores are 16 contiguous bytes per lane.
+  // Epilogue tile: the block's BM x COLS outputs, staged in LDS so that
+  // global stores are 16 contiguous bytes per lane.  It lies over the
+  // activation ring; with XT (next tile's first loads issued from the K
+  // loop's last steps) it starts at ring slot 1, since slot 0 then already
+  // holds the next tile's first activation step.
   constexpr int COLS = stage_cols(STAGE, NSUB, WAVES);
   constexpr int OUT_ES = STAGE == 1 ? (S == kW4A16 ? 2 : 4) : (S == kW8A8 ? 4 : 2);
   constexpr int EPITCH = COLS * OUT_ES + 16;
-  constexpr int RING = kStages * BM * PITCH;
-  constexpr int SMEM = RING > BM * EPITCH ? RING : BM * EPITCH;
+  constexpr int SLOT = BM * PITCH;
+  constexpr int RING = kStages * SLOT;
+  constexpr int EPI = BM * EPITCH;
+  constexpr int EPI_OFF = XT ? SLOT : 0;
+  constexpr int SMEM = XT ? SLOT + (EPI > SLOT ? EPI : SLOT) : (RING > EPI ? RING : EPI);
+  static_assert(kStages == 2, "two activation slots");
   __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
+  uint8_t* const etile = smem + EPI_OFF;
   // Row ids of the tile being set up and of the tile in its epilogue.
   __shared__ __attribute__((aligned(16))) int sRow[2][BM];
   __shared__ __attribute__((aligned(16))) float sScale[BM];
@@ -104,13 +116,19 @@ __global__ __launch_bounds__(WAVES * 64)
   // by one thread only (the last one, never a row thread) and passed on
   // through LDS at the set-up barrier: a uniform load would be moved to a
   // scalar register right away, waiting for every load in flight.
-  int next_pair = g.P, next_expert = 0;
+  int next_pair = g.P, next_expert = 0, next_ri = -1;
   auto fetch_meta = [&](int w) __attribute__((always_inline)) {
     if (w < w_end) {
       const int m = w / g.ntiles_n;
       if (tid < BM) next_pair = g.sorted_pair_ids[m * BM + tid];
       if (tid == kThreads - 1) next_expert = g.tile_expert[m];
     }
+  };
+  // Row id of a fetched pair slot (stage 1: its token), -1 for padding.  Run
+  // right after a full wait for loads, so that the division (and a register
+  // reload, if any) never waits inside the pipelined loop.
+  auto decode_meta = [&]() __attribute__((always_inline)) {
+    if (tid < BM) next_ri = next_pair < g.P ? (STAGE == 1 ? next_pair / g.k : next_pair) : -1;
   };
 
   constexpr int SB = S == kW4A16 ? 2 : 1;  // scale bytes (w4a16 fp16, a8w4 e8m0)
@@ -124,6 +142,7 @@ __global__ __launch_bounds__(WAVES * 64)
   // load addresses.  Every address is a wave-uniform base plus one 32-bit
   // per-lane offset, so the loads use the scalar-base + 32-bit-offset form.
   int t_mt = 0, t_nt = 0, t_e = 0, t_nvalid = 0, t_mvalid = 0;
+  int t_ri = -1;  // row thread's id (stage 1 token, stage 2 pair), -1 past the real rows
   float t_scale = 0.f;
   int nrow[NSUB];
   const uint8_t* __restrict__ Bexp = B;
@@ -171,31 +190,24 @@ __global__ __launch_bounds__(WAVES * 64)
   u32x4 ar[NCH];
   BFrag<S> b0[NSUB], b1[NSUB], b2[NSUB], b3[NSUB];
 
-  // Set-up of tile w (row ids into sRow[bf]) and its first loads: the
-  // activation rows of step 0 and the weights of steps 0-2.  It runs right
-  // after the previous tile's K loop, before that tile's epilogue, so these
-  // loads are in flight while the epilogue computes and stores (issued after
-  // its stores they would queue behind them).
-  auto setup = [&](int w, int bf) __attribute__((always_inline)) {
+  // Set-up of tile w, in three parts.  setup_rows: row ids into sRow[bf],
+  // the row count, the load offsets (no global loads).  meta_loads: the
+  // per-row scale of tile w and the metadata of the tile after it.
+  // setup_loads: the activation rows of step 0 and the weights of steps 0-2.
+  auto setup_rows = [&](int w, int bf) __attribute__((always_inline)) {
     t_mt = w / g.ntiles_n;
     t_nt = w - t_mt * g.ntiles_n;
     if (tid == kThreads - 1) sExpert[bf] = next_expert;
     int valid_here = 0;
     if (tid < BM) {
-      const int p = next_pair;
-      const bool ok = p < g.P;
-      const int ri = ok ? (STAGE == 1 ? p / g.k : p) : -1;
+      const int ri = next_ri;
       sRow[bf][tid] = ri;
-      valid_here = ok;
-      // Per-row scale of the epilogue (token scale in stage 1, the
-      // requantized h scale in stage 2).
-      if constexpr (S != kW4A16)
-        t_scale = ok ? g.a_scale[STAGE == 1 ? ri : (size_t)t_mt * BM + tid] : 0.f;
+      t_ri = ri;
+      valid_here = ri >= 0;
     }
     t_nvalid = __syncthreads_count(valid_here);
     t_mvalid = (t_nvalid + 15) >> 4;
     t_e = sExpert[bf];
-    fetch_meta(w + per_xcd);
     // Weight rows of this wave's sub-tiles, as 32-bit offsets from the
     // expert's base (one expert's weights are far below 4 GiB).
 #pragma unroll
@@ -236,6 +248,17 @@ __global__ __launch_bounds__(WAVES * 64)
                                  : (uint32_t)(t_mt * BM + row) * (uint32_t)(g.I * T_::A_ELEM);
       aoff[i] = rbase + col * 16;
     }
+  };
+  auto meta_loads = [&](int w) __attribute__((always_inline)) {
+    // Per-row scale of the epilogue (token scale in stage 1, the
+    // requantized h scale in stage 2).
+    if constexpr (S != kW4A16) {
+      if (tid < BM)
+        t_scale = t_ri >= 0 ? g.a_scale[STAGE == 1 ? t_ri : (size_t)t_mt * BM + tid] : 0.f;
+    }
+    fetch_meta(w + per_xcd);
+  };
+  auto setup_loads = [&]() __attribute__((always_inline)) {
     load_a(ar, 0);
     load_b(b0, 0);
     load_b(b1, min(1, n - 1));
@@ -303,39 +326,94 @@ __global__ __launch_bounds__(WAVES * 64)
   int wi = w_begin + slot;
   if (wi >= w_end) return;
   fetch_meta(wi);
+  decode_meta();
   int buf = 0;
-  setup(wi, buf);
+  setup_rows(wi, buf);
+  meta_loads(wi);
+  setup_loads();
+  bool first = true;
   while (true) {
     // The previous tile's output stores are still in flight.  On gfx9 stores
     // and loads share one counter, and pending stores would turn every wait
     // of the pipelined loop into a full drain; drain them here, where the
     // wait for this tile's first loads has to happen anyway.
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    store_a(ar, 0);
-    load_a(ar, min(1, n - 1));
+    decode_meta();
     mvalid = t_mvalid;
 #pragma unroll
     for (int m = 0; m < MSUB; m++)
 #pragma unroll
       for (int s = 0; s < NSUB; s++) acc[m][s] = Acc{0, 0, 0, 0};
-    __syncthreads();
-    for (int s = 0; s < n; s += 4) {
-      step(s, b0, b3);
-      step(s + 1, b1, b0);
-      step(s + 2, b2, b1);
-      step(s + 3, b3, b2);
+    if (!XT || first) {
+      store_a(ar, 0);
+      load_a(ar, min(1, n - 1));
+      __syncthreads();
     }
-
-    // This tile's epilogue state; then the next tile's set-up and loads.
-    const int mt = t_mt, nt = t_nt, e = t_e, nvalid = t_nvalid;
-    const float row_scale = t_scale;
-    int enrow[NSUB];
-#pragma unroll
-    for (int s = 0; s < NSUB; s++) enrow[s] = nrow[s];
-    const int ebuf = buf;
+    first = false;
     const int wn = wi + per_xcd;
     const bool more = wn < w_end;  // the same for the whole block
-    if (more) setup(wn, buf ^ 1);
+
+    // This tile's epilogue state (taken before the next tile's set-up).
+    int mt, nt, e, nvalid, enrow[NSUB];
+    float row_scale;
+    const int ebuf = buf;
+    auto keep_epilogue_state = [&]() __attribute__((always_inline)) {
+      mt = t_mt, nt = t_nt, e = t_e, nvalid = t_nvalid;
+      row_scale = t_scale;
+#pragma unroll
+      for (int s = 0; s < NSUB; s++) enrow[s] = nrow[s];
+    };
+    if constexpr (XT) {
+      // n % 4 == 0.  The last four steps are written out: the loads that
+      // would run past step n-1 fetch the next tile's activations of steps
+      // 0-1 and weights of steps 0-2 instead (the current tile's last step
+      // again when there is no next tile), into the slots and registers that
+      // tile's step 0 expects.  Its row set-up runs between the last loads
+      // of this tile and the first of the next, and has no global loads of
+      // its own: a load issued on only some paths would make every later
+      // counter wait of the loop a conservative one.
+      for (int s = 0; s < n - 4; s += 4) {
+        step(s, b0, b3);
+        step(s + 1, b1, b0);
+        step(s + 2, b2, b1);
+        step(s + 3, b3, b2);
+      }
+      step(n - 4, b0, b3);
+      store_a(ar, 0);  // step n-2
+      load_a(ar, n - 1);
+      keep_epilogue_state();
+      if (more) setup_rows(wn, buf ^ 1);
+      load_b(b0, more ? 0 : n - 1);
+      compute(1, b1);  // step n-3
+      __syncthreads();
+      store_a(ar, 1);  // step n-1
+      load_a(ar, more ? 0 : n - 1);
+      load_b(b1, more ? 1 : n - 1);
+      compute(0, b2);  // step n-2
+      __syncthreads();
+      store_a(ar, 0);  // the next tile's step 0
+      load_a(ar, more ? 1 : n - 1);
+      load_b(b2, more ? 2 : n - 1);
+      compute(1, b3);  // step n-1
+      __syncthreads();
+    } else {
+      for (int s = 0; s < n; s += 4) {
+        step(s, b0, b3);
+        step(s + 1, b1, b0);
+        step(s + 2, b2, b1);
+        step(s + 3, b3, b2);
+      }
+      // The next tile's set-up and first loads run before this tile's
+      // epilogue, so that those loads are in flight while the epilogue
+      // computes and stores (issued after its stores they would queue
+      // behind them).
+      keep_epilogue_state();
+      if (more) {
+        setup_rows(wn, buf ^ 1);
+        meta_loads(wn);
+        setup_loads();
+      }
+    }
 
     // ------------------------------------------------------------ epilogue
     // Phase 1: registers -> LDS tile (row = tile row, column = the block's
@@ -356,7 +434,7 @@ __global__ __launch_bounds__(WAVES * 64)
         for (int r = 0; r < 4; r++) {
           const int row = m * 16 + lq * 4 + r;
           const size_t orow = (size_t)mt * BM + row;
-          uint8_t* trow = smem + row * EPITCH;
+          uint8_t* trow = etile + row * EPITCH;
           if constexpr (STAGE == 1) {
             const int tok = rids[r];
 #pragma unroll
@@ -419,8 +497,8 @@ __global__ __launch_bounds__(WAVES * 64)
       for (int row0 = 0; row0 < mvalid * 16; row0 += RPP) {
         const int row = row0 + prow;
         const bool ok = row < nvalid;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(smem + (row < BM ? row : 0) * EPITCH +
-                                                         chunk * 16);
+        const u32x4 v = *reinterpret_cast<const u32x4*>(etile + (row < BM ? row : 0) * EPITCH +
+                                                          chunk * 16);
         if constexpr (STAGE == 1) {
           if (ok)
             __builtin_nontemporal_store(
@@ -429,9 +507,8 @@ __global__ __launch_bounds__(WAVES * 64)
           if constexpr (S != kW4A16) {
             float a = fmaxf(fmaxf(fabsf(__uint_as_float(v.x)), fabsf(__uint_as_float(v.y))),
                             fmaxf(fabsf(__uint_as_float(v.z)), fabsf(__uint_as_float(v.w))));
-#pragma unroll
-            for (int off = 1; off < CPRO; off <<= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
-            if (ok && chunk == 0) g.row_pmax[((size_t)mt * BM + row) * g.ntiles_n + nt] = a;
+            a = group_max<CPRO>(a);
+            if (ok && chunk == CPRO - 1) g.row_pmax[((size_t)mt * BM + row) * g.ntiles_n + nt] = a;
           }
         } else {
           if (ok)
@@ -442,28 +519,41 @@ __global__ __launch_bounds__(WAVES * 64)
       }
     }
     if (!more) break;
+    if constexpr (XT) meta_loads(wn);
     wi = wn;
     buf ^= 1;
     __syncthreads();  // the epilogue is done with the LDS tile before the next store_a
   }
 }
 
-template <int S, int STAGE, int BM, bool PK, int NSUB, int WAVES>
-hipError_t launch_one(const GemmArgs& g, hipStream_t s) {
+template <int S, int STAGE, int BM, bool PK, int NSUB, int WAVES, bool XT>
+hipError_t launch_xt(const GemmArgs& g, hipStream_t s) {
   static int blocks_per_cu = 0;
   if (blocks_per_cu == 0) {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, moe_gemm_kernel<S, STAGE, BM, PK, NSUB, WAVES>, WAVES * 64, 0) != hipSuccess ||
+            &n, moe_gemm_kernel<S, STAGE, BM, PK, NSUB, WAVES, XT>, WAVES * 64, 0) != hipSuccess ||
         n < 1)
       n = 1;
     blocks_per_cu = n;
   }
   int nblk = device_cu_count() * blocks_per_cu;
   nblk = nblk < 8 ? 8 : (nblk / 8) * 8;
-  hipLaunchKernelGGL((moe_gemm_kernel<S, STAGE, BM, PK, NSUB, WAVES>), dim3(nblk),
+  hipLaunchKernelGGL((moe_gemm_kernel<S, STAGE, BM, PK, NSUB, WAVES, XT>), dim3(nblk),
                      dim3(WAVES * 64), 0, s, g);
   return hipGetLastError();
+}
+
+// Stage 1 runs the cross-tile pipeline whenever its K loop has a multiple of
+// four steps (the register ring's length).
+template <int S, int STAGE, int BM, bool PK, int NSUB, int WAVES>
+hipError_t launch_one(const GemmArgs& g, hipStream_t s) {
+  if constexpr (STAGE == 1) {
+    const int nsteps = g.K / Tr<S>::BK;
+    if (nsteps >= 4 && nsteps % 4 == 0)
+      return launch_xt<S, STAGE, BM, PK, NSUB, WAVES, true>(g, s);
+  }
+  return launch_xt<S, STAGE, BM, PK, NSUB, WAVES, false>(g, s);
 }
 
 template <int S, int STAGE, bool PK>

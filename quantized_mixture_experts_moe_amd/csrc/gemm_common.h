@@ -163,6 +163,30 @@ __device__ inline void mfma_step(typename Tr<S>::Acc& acc, const u32x4* a, const
   }
 }
 
+// max(x, x of the lane that DPP control CTRL names); lanes of rows outside
+// ROW_MASK keep x.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ inline float dpp_fmax(float x) {
+  const int y = __builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL, ROW_MASK,
+                                            0xf, false);
+  return fmaxf(x, __int_as_float(y));
+}
+
+// Maximum of x over each aligned group of G lanes (G = 16 or 32), exact in
+// the group's last lane.  Four DPP steps reduce each 16-lane row (quad
+// swaps, then the half-row and row mirrors); for G = 32 the last lane of
+// the group's first row is then broadcast into its second row.
+template <int G>
+__device__ inline float group_max(float x) {
+  static_assert(G == 16 || G == 32, "groups of 16 or 32 lanes");
+  x = dpp_fmax<0xB1>(x);   // quad_perm [1,0,3,2]
+  x = dpp_fmax<0x4E>(x);   // quad_perm [2,3,0,1]
+  x = dpp_fmax<0x141>(x);  // row_half_mirror
+  x = dpp_fmax<0x140>(x);  // row_mirror
+  if constexpr (G == 32) x = dpp_fmax<0x142, 0xA>(x);  // row_bcast15 into rows 1 and 3
+  return x;
+}
+
 // SiLU(gate) * up in the stage-1 epilogue.
 // w8a8 follows the bit-exact fp32 recipe: ex = f32(exp_f64(-g));
 // sg = g / (1 + ex) (IEEE division); h = sg * u.

@@ -148,14 +148,31 @@ moe_stage2_resident(GemmArgs g, int passes) {
     load_b(b2, 2);
 
     // The tile's activation rows (real rows and the rest of their 16-row
-    // group; those extra rows only feed discarded outputs) into LDS.
+    // group; those extra rows only feed discarded outputs) into LDS, eight
+    // 16-byte loads per thread in flight at a time.
     {
+      constexpr int kBatch = 8;
       const int cpr = K * T_::A_ELEM / 16;  // 16-byte chunks per row
       const int n = mvalid * 16 * cpr;
-      for (int i = tid; i < n; i += kS2Threads) {
-        const int r = i / cpr, cc = i - r * cpr;
-        *reinterpret_cast<u32x4*>(sA + r * kS2Pitch + cc * 16) = *reinterpret_cast<const u32x4*>(
-            Aglob + ((size_t)mt * BM + r) * (size_t)(K * T_::A_ELEM) + cc * 16);
+      for (int i0 = tid; i0 < n; i0 += kBatch * kS2Threads) {
+        u32x4 v[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; j++) {
+          const int i = i0 + j * kS2Threads;
+          if (i < n) {
+            const int r = i / cpr, cc = i - r * cpr;
+            v[j] = *reinterpret_cast<const u32x4*>(
+                Aglob + ((size_t)mt * BM + r) * (size_t)(K * T_::A_ELEM) + cc * 16);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; j++) {
+          const int i = i0 + j * kS2Threads;
+          if (i < n) {
+            const int r = i / cpr, cc = i - r * cpr;
+            *reinterpret_cast<u32x4*>(sA + r * kS2Pitch + cc * 16) = v[j];
+          }
+        }
       }
     }
 #pragma unroll
