@@ -9,9 +9,11 @@ inter 1024, 4096 tokens (40960 (token, expert) rows).
 
 Weights are rewritten once into the library's streaming layout
 (qmoe_prepack) at set-up.  Before every timed step a 512 MiB buffer is
-written to flush the 256 MB memory-side cache; each step is timed with HIP
-events on the launch stream (the flush sits outside them) and ms_per_step
-is their mean over the timed steps.
+read (a max reduction) to flush the 256 MB memory-side cache: the step then
+finds none of its inputs in that cache, and no dirty lines of the flush
+itself are left to be written back inside the step, as a write-based flush
+would leave.  Each step is timed with HIP events on the launch stream (the
+flush sits outside them) and ms_per_step is their mean over the timed steps.
 
 Prints one JSON line on stdout (one per workload with --sweep); progress
 goes to stderr.
@@ -183,8 +185,8 @@ def run_workload(name: str, args, torch, with_cpu: bool) -> dict:
     torch.cuda.synchronize()
     touched = int(torch.unique(ids).numel())
     # The memory-side cache (256 MB) is flushed before every timed step by
-    # writing a 512 MiB buffer; the flush sits between the step's events.
-    flush = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    # reading a 512 MiB buffer; the flush sits between the step's events.
+    flush = None if args.no_flush else torch.ones(64 << 20, dtype=torch.int64, device=dev)
 
     n_ev = 7
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
@@ -195,7 +197,7 @@ def run_workload(name: str, args, torch, with_cpu: bool) -> dict:
 
     def step(i, ev=None):
         if flush is not None:
-            flush.fill_(i & 255)
+            torch.amax(flush)
         if ev is not None:
             ev[0].record()
         ops.route(g["logits"], k, ids, tw)

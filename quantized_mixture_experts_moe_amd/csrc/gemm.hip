@@ -64,7 +64,12 @@ __global__ __launch_bounds__(WAVES * 64)
   using T_ = Tr<S>;
   using Acc = typename T_::Acc;
   constexpr int MSUB = BM / 16;
-  constexpr int PITCH = T_::A_STEP + 16;                     // LDS row pitch (bytes), padded
+  // LDS row pitch (bytes).  With a 32-byte pad the fragment reads of the
+  // 8-bit schemes (16 rows x 16 bytes at 16q + 64f) reach 64 distinct banks
+  // per 16 lanes: 4 LDS cycles per read instead of 8 with a 16-byte pad
+  // (measured on gfx950).  w4a16's 64q + 16f pattern takes 8 cycles with
+  // either pad.
+  constexpr int PITCH = T_::A_STEP + (S == kW4A16 ? 16 : 32);
   constexpr int CPR = T_::A_STEP / 16;                       // 16-byte chunks per row per step
   constexpr int NCH = (BM * CPR + kThreads - 1) / kThreads;  // chunks per thread per step
   constexpr int NF = T_::A_FRAG / 16;                        // 16-byte LDS reads per fragment

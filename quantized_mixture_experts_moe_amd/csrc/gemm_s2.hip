@@ -32,7 +32,9 @@ constexpr int kS2Threads = kS2Waves * 64;
 constexpr int kS2Nsub = 2;
 constexpr int kS2Cols = kS2Waves * kS2Nsub * 16;  // output columns per pass
 constexpr int kS2RowBytes = 1024;                 // largest activation row held in LDS
-constexpr int kS2Pitch = kS2RowBytes + 16;        // LDS row pitch (bank spread)
+// LDS row pitch: the 32-byte pad makes the 16-byte fragment reads (16 rows
+// at 16q + 64f) free of bank conflicts on gfx950, measured.
+constexpr int kS2Pitch = kS2RowBytes + 32;
 
 // One MFMA step with the weight fragment as the A operand.
 template <int S>
