@@ -12,8 +12,13 @@ Weights are rewritten once into the library's streaming layout
 read (a max reduction) to flush the 256 MB memory-side cache: the step then
 finds none of its inputs in that cache, and no dirty lines of the flush
 itself are left to be written back inside the step, as a write-based flush
-would leave.  Each step is timed with HIP events on the launch stream (the
-flush sits outside them) and ms_per_step is their mean over the timed steps.
+would leave.  The step's four launches are captured once into a HIP graph
+and replayed (no host launch gaps between the kernels); each replay is
+timed with HIP events on the launch stream (the flush sits outside them)
+and ms_per_step is their mean over the timed steps.  The last replay's
+output must equal an eager step's bit for bit.  A separate eager pass with
+events between the kernels gives the per-kernel breakdown (kernel_ms; its
+route, align and combine intervals also hold host launch gaps).
 
 Prints one JSON line on stdout (one per workload with --sweep); progress
 goes to stderr.
@@ -150,6 +155,64 @@ def stage_flops(shape) -> dict:
             "stage2": 2.0 * shape.hidden * shape.inter * P, "combine": 0.0}
 
 
+def graph_step_ms(torch, ops, args, flush, b: dict, eager_step):
+    """Mean and median GPU time of one step run as a HIP graph: the four
+    launches (route, align, grouped FFN, combine) captured once and replayed,
+    so that no host launch gap sits between them.  The cache flush stays
+    outside the graph and outside the events.  The last replay's outputs
+    must equal a following eager step's bit for bit."""
+    sh, g, E, k = b["shape"], b["g"], b["shape"].experts, b["shape"].topk
+
+    def body():
+        ops.route(g["logits"], k, b["ids"], b["tw"])
+        ops.align(b["ids"], E, b["bm"], out=b["al"])
+        ops.grouped_ffn(sh.scheme, g["x"], g["x_scale"], b["W"], b["al"], E, k, ws=b["ws"],
+                        y_pairs=b["y"])
+        ops.combine(b["y"], b["tw"], out_bf16=b["out_bf16"], out_f32=b["out_f32"],
+                    want_f32=b["out_f32"] is not None)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        body()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        body()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for i in range(args.warmup):
+        if flush is not None:
+            torch.amax(flush)
+        graph.replay()
+    torch.cuda.synchronize()
+    if flush is not None:
+        for i in range(args.steps):
+            torch.amax(flush)
+            ev[i][0].record()
+            graph.replay()
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        ms = np.array([e0.elapsed_time(e1) for e0, e1 in ev])
+    else:
+        ev[0][0].record()
+        for i in range(args.steps):
+            graph.replay()
+        ev[0][1].record()
+        torch.cuda.synchronize()
+        ms = np.array([ev[0][0].elapsed_time(ev[0][1]) / args.steps])
+    got = [t.clone() for t in (b["out_bf16"], b["out_f32"]) if t is not None]
+    eager_step()
+    torch.cuda.synchronize()
+    want = [t for t in (b["out_bf16"], b["out_f32"]) if t is not None]
+    if not all(torch.equal(x, y) for x, y in zip(got, want)):
+        raise SystemExit("bench: graph replay output differs from the eager step")
+    del graph
+    log(f"{sh.name}: graph step {float(ms.mean()):.4f} ms")
+    return float(ms.mean()), float(np.median(ms))
+
+
 def run_workload(name: str, args, torch, with_cpu: bool) -> dict:
     from quantized_mixture_experts_moe_amd import ops, synth
     from quantized_mixture_experts_moe_amd.shapes import default_block_m, shape_by_name
@@ -223,10 +286,17 @@ def run_workload(name: str, args, torch, with_cpu: bool) -> dict:
         return np.array([evs[i][a].elapsed_time(evs[i][b]) for i in range(args.steps)])
 
     step_ms = per_step(0, 6)
-    # Whole-step time: the mean of the timed steps' GPU time (event 0 -> 6),
+    # Eager step time: the mean of the timed steps' GPU time (event 0 -> 6),
     # which leaves out the cache flush between steps; without the flush the
-    # steps run back to back and the host clock is used.
-    ms_per_step = float(step_ms.mean()) if flush is not None else wall_ms
+    # steps run back to back and the host clock is used.  At small sizes it
+    # also holds the host's launch gaps between the kernels.
+    eager_ms = float(step_ms.mean()) if flush is not None else wall_ms
+    ms_per_step, graph_ms, graph_median = eager_ms, None, None
+    if not args.eager:
+        graph_ms, graph_median = graph_step_ms(torch, ops, args, flush, dict(
+            shape=shape, g=g, W=W, ids=ids, tw=tw, al=al, y=y, ws=ws, bm=bm,
+            out_bf16=out_bf16, out_f32=out_f32), lambda: step(0))
+        ms_per_step = graph_ms
     kern = {"route": per_step(0, 1).mean(), "align": per_step(1, 2).mean(),
             "stage1": per_step(2, 3).mean(), "requant": per_step(3, 4).mean(),
             "stage2": per_step(4, 5).mean(), "combine": per_step(5, 6).mean(),
@@ -272,7 +342,10 @@ def run_workload(name: str, args, torch, with_cpu: bool) -> dict:
                    "touched_experts": touched, "weight_layout": layout,
                    "cache_flush_between_steps": flush is not None,
                    "parallelism": "none (1 GPU)"},
-        "ms_per_step_median": round(float(np.median(step_ms)), 4),
+        "ms_per_step_median": round(float(np.median(step_ms) if graph_median is None
+                                          else graph_median), 4),
+        "timing": "hip graph of the step, replayed" if graph_ms is not None else "eager launches",
+        "ms_per_step_eager": round(eager_ms, 4),
         "wall_ms_per_step": round(wall_ms, 4),
         "tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
         "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
@@ -296,6 +369,8 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="run every workload of the sweep, one JSON line each (no CPU baseline)")
     ap.add_argument("--block-m", type=int, default=0)
+    ap.add_argument("--eager", action="store_true",
+                    help="time the eager launches only (no HIP graph of the step)")
     ap.add_argument("--canonical", action="store_true",
                     help="feed the weights in their canonical layout (default: the streaming "
                          "layout qmoe_prepack writes once at set-up, outside the timed steps)")

@@ -16,6 +16,8 @@
 //     the chunk base + the earlier waves' counts + popcount(mask & lanes
 //     below).  The same launch writes the padding sentinels, the
 //     tile->expert map and the tail, spread over at least 32 blocks.
+// Up to 256 tokens (one chunk) all three steps run in one block of one
+// launch (align_small_kernel): short prefills pay one launch, not three.
 #include "qmoe_internal.h"
 
 namespace qmoe {
@@ -204,6 +206,78 @@ __global__ __launch_bounds__(kChunk) void align_scatter_kernel(
     tile_expert[i] = -1;
 }
 
+// The whole of moe_align for T <= kChunk in one block: masks, expert totals,
+// the padded offsets (block scan), the scatter, the padding sentinels, the
+// tile->expert map and the tail.
+__global__ __launch_bounds__(kChunk) void align_small_kernel(
+    const int32_t* __restrict__ ids, int T, int k, int E, int block_m, int cap,
+    int32_t* __restrict__ sorted, int32_t* __restrict__ tile_expert,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ num_padded,
+    int32_t* __restrict__ flags) {
+  extern __shared__ unsigned long long mask[];  // [4][E]
+  __shared__ int s_tot[kMaxExperts];
+  __shared__ int s_off[kMaxExperts + 1];
+  __shared__ int s_part[kChunk];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int P = T * k;
+  const int bad = build_masks(ids, T, k, E, mask);
+  auto padded = [&](int n) { return (n + block_m - 1) / block_m * block_m; };
+  // Expert totals and the exclusive scan of their padded sizes; each thread
+  // owns a contiguous run of experts.
+  const int per = (E + kChunk - 1) / kChunk;
+  const int r0 = min(E, tid * per), r1 = min(E, r0 + per);
+  int run = 0;
+  for (int e = r0; e < r1; e++) {
+    const int c = __popcll(mask[e]) + __popcll(mask[E + e]) + __popcll(mask[2 * E + e]) +
+                  __popcll(mask[3 * E + e]);
+    s_tot[e] = c;
+    run += padded(c);
+  }
+  s_part[tid] = run;
+  __syncthreads();
+  for (int off = 1; off < kChunk; off <<= 1) {  // inclusive scan of the run totals
+    const int v = tid >= off ? s_part[tid - off] : 0;
+    __syncthreads();
+    s_part[tid] += v;
+    __syncthreads();
+  }
+  int base = s_part[tid] - run;
+  for (int e = r0; e < r1; e++) {
+    s_off[e] = base;
+    offsets[e] = base;
+    base += padded(s_tot[e]);
+  }
+  if (tid == kChunk - 1) {
+    const int npad = s_part[kChunk - 1];
+    s_off[E] = npad;
+    offsets[E] = npad;
+    *num_padded = npad;
+    *flags = bad;
+  }
+  __syncthreads();
+  // Scatter: rank inside the expert = pairs of earlier tokens of this block.
+  if (tid < T) {
+    const unsigned long long below = (1ull << lane) - 1ull;
+    for (int j = 0; j < k; j++) {
+      const int e = ids[(size_t)tid * k + j];
+      if (e < 0 || e >= E) continue;
+      int rank = __popcll(mask[wave * E + e] & below);
+      for (int w = 0; w < wave; w++) rank += __popcll(mask[w * E + e]);
+      sorted[s_off[e] + rank] = tid * k + j;
+    }
+  }
+  // Sentinels and tile->expert entries, one wave per expert.
+  for (int e = wave; e < E; e += kChunk / 64) {
+    const int off = s_off[e], total = s_tot[e];
+    const int pe = padded(total);
+    for (int i = off / block_m + lane; i < (off + pe) / block_m; i += 64) tile_expert[i] = e;
+    for (int i = off + total + lane; i < off + pe; i += 64) sorted[i] = P;
+  }
+  const int npad = s_off[E];
+  for (int i = npad + tid; i < cap; i += kChunk) sorted[i] = P;
+  for (int i = npad / block_m + tid; i < cap / block_m; i += kChunk) tile_expert[i] = -1;
+}
+
 }  // namespace
 
 hipError_t launch_align(const int32_t* ids, int T, int k, int E, int block_m, int32_t* sorted,
@@ -214,6 +288,11 @@ hipError_t launch_align(const int32_t* ids, int T, int k, int E, int block_m, in
   const int nchunks = (T + kChunk - 1) / kChunk;
   const size_t lds = (size_t)4 * E * sizeof(unsigned long long);
   hipError_t err;
+  if (nchunks <= 1) {
+    hipLaunchKernelGGL(align_small_kernel, dim3(1), dim3(kChunk), lds, s, ids, T, k, E, block_m,
+                       cap, sorted, tile_expert, offsets, num_padded, flags);
+    return hipGetLastError();
+  }
   if (nchunks > 0) {
     hipLaunchKernelGGL(align_count_kernel, dim3(nchunks), dim3(kChunk), lds, s, ids, T, k, E,
                        nchunks, chunk_counts, chunk_flags);

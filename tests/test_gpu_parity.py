@@ -59,7 +59,8 @@ def _check_align(al, ids_np, E, bm):
     np.testing.assert_array_equal(al["expert_offsets"].cpu().numpy(), ref["expert_offsets"])
 
 
-@pytest.mark.parametrize("T,k,E,bm", [(64, 2, 8, 16), (128, 8, 128, 16), (2048, 8, 128, 128),
+@pytest.mark.parametrize("T,k,E,bm", [(64, 2, 8, 16), (128, 8, 128, 16), (256, 10, 512, 16),
+                                      (2048, 8, 128, 128),
                                       (4096, 10, 512, 128), (1, 1, 1, 16), (257, 3, 7, 32),
                                       (1000, 4, 1024, 64), (8192, 10, 512, 16)])
 def test_align_matches_oracle(T, k, E, bm):
