@@ -16,8 +16,8 @@
 //     the chunk base + the earlier waves' counts + popcount(mask & lanes
 //     below).  The same launch writes the padding sentinels, the
 //     tile->expert map and the tail, spread over at least 32 blocks.
-// Up to 256 tokens (one chunk) all three steps run in one block of one
-// launch (align_small_kernel): short prefills pay one launch, not three.
+// Up to 1024 tokens all three steps run in one block of one launch
+// (align_small_kernel): short prefills pay one launch, not three.
 #include "qmoe_internal.h"
 
 namespace qmoe {
@@ -206,56 +206,77 @@ __global__ __launch_bounds__(kChunk) void align_scatter_kernel(
     tile_expert[i] = -1;
 }
 
-// The whole of moe_align for T <= kChunk in one block: masks, expert totals,
-// the padded offsets (block scan), the scatter, the padding sentinels, the
-// tile->expert map and the tail.
-__global__ __launch_bounds__(kChunk) void align_small_kernel(
-    const int32_t* __restrict__ ids, int T, int k, int E, int block_m, int cap,
+// The whole of moe_align for T <= kSmallT in one block of 16 waves (64
+// tokens each): masks, expert totals (one expert per thread), the padded
+// offsets (block scan), the scatter, the padding sentinels, the
+// tile->expert map and the tail.  block_m is a power of two.
+constexpr int kSmallT = 1024;
+constexpr int kSmallWaves = kSmallT / 64;
+
+__device__ inline int block_excl_scan_1024(int v, int* s_wave) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) s_wave[wave] = x;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; w++) before += s_wave[w];
+  return before + x - v;
+}
+
+__global__ __launch_bounds__(kSmallT) void align_small_kernel(
+    const int32_t* __restrict__ ids, int T, int k, int E, int bm_shift, int cap,
     int32_t* __restrict__ sorted, int32_t* __restrict__ tile_expert,
     int32_t* __restrict__ offsets, int32_t* __restrict__ num_padded,
     int32_t* __restrict__ flags) {
-  extern __shared__ unsigned long long mask[];  // [4][E]
+  extern __shared__ unsigned long long mask[];  // [kSmallWaves][E]
   __shared__ int s_tot[kMaxExperts];
   __shared__ int s_off[kMaxExperts + 1];
-  __shared__ int s_part[kChunk];
+  __shared__ int s_wave[kSmallWaves];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int P = T * k;
-  const int bad = build_masks(ids, T, k, E, mask);
-  auto padded = [&](int n) { return (n + block_m - 1) / block_m * block_m; };
-  // Expert totals and the exclusive scan of their padded sizes; each thread
-  // owns a contiguous run of experts.
-  const int per = (E + kChunk - 1) / kChunk;
-  const int r0 = min(E, tid * per), r1 = min(E, r0 + per);
-  int run = 0;
-  for (int e = r0; e < r1; e++) {
-    const int c = __popcll(mask[e]) + __popcll(mask[E + e]) + __popcll(mask[2 * E + e]) +
-                  __popcll(mask[3 * E + e]);
-    s_tot[e] = c;
-    run += padded(c);
-  }
-  s_part[tid] = run;
+  const int bm = 1 << bm_shift;
+  for (int i = tid; i < kSmallWaves * E; i += kSmallT) mask[i] = 0ull;
   __syncthreads();
-  for (int off = 1; off < kChunk; off <<= 1) {  // inclusive scan of the run totals
-    const int v = tid >= off ? s_part[tid - off] : 0;
-    __syncthreads();
-    s_part[tid] += v;
-    __syncthreads();
+  int bad = 0;
+  if (tid < T) {
+    for (int j = 0; j < k; j++) {
+      const int e = ids[(size_t)tid * k + j];
+      if (e >= 0 && e < E) {
+        const unsigned long long old = atomicOr(&mask[wave * E + e], 1ull << lane);
+        if (old & (1ull << lane)) bad |= 2;
+      } else {
+        bad |= 1;
+      }
+    }
   }
-  int base = s_part[tid] - run;
-  for (int e = r0; e < r1; e++) {
-    s_off[e] = base;
-    offsets[e] = base;
-    base += padded(s_tot[e]);
+  const int b1 = __syncthreads_or(bad & 1);
+  const int b2 = __syncthreads_or(bad & 2);
+  // Totals, one expert per thread (E <= 1024), and their padded prefix.
+  int tot = 0;
+  if (tid < E) {
+#pragma unroll 4
+    for (int w = 0; w < kSmallWaves; w++) tot += __popcll(mask[w * E + tid]);
   }
-  if (tid == kChunk - 1) {
-    const int npad = s_part[kChunk - 1];
-    s_off[E] = npad;
-    offsets[E] = npad;
-    *num_padded = npad;
-    *flags = bad;
+  const int pe = ((tot + bm - 1) >> bm_shift) << bm_shift;
+  const int off = block_excl_scan_1024(tid < E ? pe : 0, s_wave);
+  if (tid < E) {
+    s_tot[tid] = tot;
+    s_off[tid] = off;
+    offsets[tid] = off;
+  }
+  if (tid == E - 1) {
+    s_off[E] = off + pe;
+    offsets[E] = off + pe;
+    *num_padded = off + pe;
+    *flags = (b1 ? 1 : 0) | (b2 ? 2 : 0);
   }
   __syncthreads();
-  // Scatter: rank inside the expert = pairs of earlier tokens of this block.
+  // Scatter: rank inside the expert = pairs of earlier tokens.
   if (tid < T) {
     const unsigned long long below = (1ull << lane) - 1ull;
     for (int j = 0; j < k; j++) {
@@ -267,15 +288,14 @@ __global__ __launch_bounds__(kChunk) void align_small_kernel(
     }
   }
   // Sentinels and tile->expert entries, one wave per expert.
-  for (int e = wave; e < E; e += kChunk / 64) {
-    const int off = s_off[e], total = s_tot[e];
-    const int pe = padded(total);
-    for (int i = off / block_m + lane; i < (off + pe) / block_m; i += 64) tile_expert[i] = e;
-    for (int i = off + total + lane; i < off + pe; i += 64) sorted[i] = P;
+  for (int e = wave; e < E; e += kSmallWaves) {
+    const int o = s_off[e], t = s_tot[e], end = s_off[e + 1];
+    for (int i = (o >> bm_shift) + lane; i < (end >> bm_shift); i += 64) tile_expert[i] = e;
+    for (int i = o + t + lane; i < end; i += 64) sorted[i] = P;
   }
   const int npad = s_off[E];
-  for (int i = npad + tid; i < cap; i += kChunk) sorted[i] = P;
-  for (int i = npad / block_m + tid; i < cap / block_m; i += kChunk) tile_expert[i] = -1;
+  for (int i = npad + tid; i < cap; i += kSmallT) sorted[i] = P;
+  for (int i = (npad >> bm_shift) + tid; i < (cap >> bm_shift); i += kSmallT) tile_expert[i] = -1;
 }
 
 }  // namespace
@@ -288,9 +308,11 @@ hipError_t launch_align(const int32_t* ids, int T, int k, int E, int block_m, in
   const int nchunks = (T + kChunk - 1) / kChunk;
   const size_t lds = (size_t)4 * E * sizeof(unsigned long long);
   hipError_t err;
-  if (nchunks <= 1) {
-    hipLaunchKernelGGL(align_small_kernel, dim3(1), dim3(kChunk), lds, s, ids, T, k, E, block_m,
-                       cap, sorted, tile_expert, offsets, num_padded, flags);
+  if (T <= kSmallT) {
+    const int bm_shift = __builtin_ctz((unsigned)block_m);
+    const size_t lds_small = (size_t)kSmallWaves * E * sizeof(unsigned long long);
+    hipLaunchKernelGGL(align_small_kernel, dim3(1), dim3(kSmallT), lds_small, s, ids, T, k, E,
+                       bm_shift, cap, sorted, tile_expert, offsets, num_padded, flags);
     return hipGetLastError();
   }
   if (nchunks > 0) {

@@ -12,8 +12,9 @@
 // CU); each wave owns two 16-column weight sub-tiles (stage 1: the gate
 // column and the up column of the same h column, so silu(gate)*up is formed
 // in registers) and all BM rows.  Weight fragments stream from HBM straight
-// into VGPRs, each weight byte read by exactly one wave, three K steps ahead
-// of the MFMAs (a ring of four register sets); the gathered activation rows
+// into VGPRs, each weight byte read by exactly one wave, RING-1 K steps
+// ahead of the MFMAs (a ring of RING register sets: 8 for tiles of up to 32
+// rows, 4 for taller ones); the gathered activation rows
 // go global -> VGPR -> a two-slot LDS ring, loaded two steps ahead and
 // shared by the block's waves.  One barrier per K step.  16-row groups past
 // the tile's last real row are skipped.
@@ -56,7 +57,7 @@ namespace {
 using namespace gk;
 
 
-template <int S, int STAGE, int BM, bool PK, int NSUB, int WAVES, bool XT>
+template <int S, int STAGE, int BM, bool PK, int NSUB, int WAVES, bool XT, int RING>
 __global__ __launch_bounds__(WAVES * 64)
     __attribute__((amdgpu_waves_per_eu(NSUB == 4 ? 1 : 2, NSUB == 4 ? 1 : 2))) void
     moe_gemm_kernel(GemmArgs g) {
@@ -84,10 +85,10 @@ __global__ __launch_bounds__(WAVES * 64)
   constexpr int OUT_ES = STAGE == 1 ? (S == kW4A16 ? 2 : 4) : (S == kW8A8 ? 4 : 2);
   constexpr int EPITCH = COLS * OUT_ES + 16;
   constexpr int SLOT = BM * PITCH;
-  constexpr int RING = kStages * SLOT;
+  constexpr int A_RING = kStages * SLOT;  // activation ring bytes
   constexpr int EPI = BM * EPITCH;
   constexpr int EPI_OFF = XT ? SLOT : 0;
-  constexpr int SMEM = XT ? SLOT + (EPI > SLOT ? EPI : SLOT) : (RING > EPI ? RING : EPI);
+  constexpr int SMEM = XT ? SLOT + (EPI > SLOT ? EPI : SLOT) : (A_RING > EPI ? A_RING : EPI);
   static_assert(kStages == 2, "two activation slots");
   __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
   uint8_t* const etile = smem + EPI_OFF;
@@ -147,7 +148,6 @@ __global__ __launch_bounds__(WAVES * 64)
   // load addresses.  Every address is a wave-uniform base plus one 32-bit
   // per-lane offset, so the loads use the scalar-base + 32-bit-offset form.
   int t_mt = 0, t_nt = 0, t_e = 0, t_nvalid = 0, t_mvalid = 0;
-  int t_ri = -1;  // row thread's id (stage 1 token, stage 2 pair), -1 past the real rows
   float t_scale = 0.f;
   int nrow[NSUB];
   const uint8_t* __restrict__ Bexp = B;
@@ -193,12 +193,15 @@ __global__ __launch_bounds__(WAVES * 64)
   };
 
   u32x4 ar[NCH];
-  BFrag<S> b0[NSUB], b1[NSUB], b2[NSUB], b3[NSUB];
+  // The weight ring: RING register sets, loads RING-1 steps ahead.
+  static_assert(RING == 4 || RING == 8, "ring of 4 or 8 steps");
+  BFrag<S> bq[RING][NSUB];
 
-  // Set-up of tile w, in three parts.  setup_rows: row ids into sRow[bf],
-  // the row count, the load offsets (no global loads).  meta_loads: the
-  // per-row scale of tile w and the metadata of the tile after it.
-  // setup_loads: the activation rows of step 0 and the weights of steps 0-2.
+  // Set-up of tile w, in four parts.  setup_rows: row ids into sRow[bf],
+  // the row count, the weight offsets (no global loads).  setup_aoff: the
+  // activation offsets.  meta_loads: the per-row scale of tile w and the
+  // metadata of the tile after it.  setup_loads: the activation rows of
+  // step 0 and the weights of steps 0 to RING-2.
   auto setup_rows = [&](int w, int bf) __attribute__((always_inline)) {
     t_mt = w / g.ntiles_n;
     t_nt = w - t_mt * g.ntiles_n;
@@ -207,7 +210,6 @@ __global__ __launch_bounds__(WAVES * 64)
     if (tid < BM) {
       const int ri = next_ri;
       sRow[bf][tid] = ri;
-      t_ri = ri;
       valid_here = ri >= 0;
     }
     t_nvalid = __syncthreads_count(valid_here);
@@ -242,9 +244,11 @@ __global__ __launch_bounds__(WAVES * 64)
         soff[s] = (uint32_t)nrow[s] * (uint32_t)(K / 32) * SB + lq * 2;
       }
     }
-    // Activation chunks of this thread: fixed rows per tile.  Rows past the
-    // tile's last real row read that row again (their results are dropped),
-    // so every load is in bounds without a branch.
+  };
+  // Activation chunks of this thread: fixed rows per tile.  Rows past the
+  // tile's last real row read that row again (their results are dropped), so
+  // every load is in bounds without a branch.
+  auto setup_aoff = [&](int bf) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < NCH; i++) {
       const int row = min(tid / CPR + i * (kThreads / CPR), t_nvalid - 1), col = tid % CPR;
@@ -254,20 +258,21 @@ __global__ __launch_bounds__(WAVES * 64)
       aoff[i] = rbase + col * 16;
     }
   };
-  auto meta_loads = [&](int w) __attribute__((always_inline)) {
+  auto meta_loads = [&](int w, int bf) __attribute__((always_inline)) {
     // Per-row scale of the epilogue (token scale in stage 1, the
-    // requantized h scale in stage 2).
+    // requantized h scale in stage 2); the row id is read back from sRow.
     if constexpr (S != kW4A16) {
-      if (tid < BM)
-        t_scale = t_ri >= 0 ? g.a_scale[STAGE == 1 ? t_ri : (size_t)t_mt * BM + tid] : 0.f;
+      if (tid < BM) {
+        const int ri = sRow[bf][tid];
+        t_scale = ri >= 0 ? g.a_scale[STAGE == 1 ? ri : (size_t)t_mt * BM + tid] : 0.f;
+      }
     }
     fetch_meta(w + per_xcd);
   };
   auto setup_loads = [&]() __attribute__((always_inline)) {
     load_a(ar, 0);
-    load_b(b0, 0);
-    load_b(b1, min(1, n - 1));
-    load_b(b2, min(2, n - 1));
+#pragma unroll
+    for (int u = 0; u < RING - 1; u++) load_b(bq[u], min(u, n - 1));
   };
 
   Acc acc[MSUB][NSUB];
@@ -310,22 +315,28 @@ __global__ __launch_bounds__(WAVES * 64)
       }
     };
 
-  // K loop.  Step s computes from LDS slot s%2 and weight register set s%4.
-  // A step first writes the activation rows of step s+1 (loaded one step
-  // earlier) to the other LDS slot, then issues the activation loads of
-  // step s+2 and the weight loads of step s+3, then runs the MFMAs of step
-  // s; one barrier ends the step.  Load counters complete in order, so this
-  // order lets the wait for the activations skip the younger weight loads,
-  // which keep three steps to arrive.  Loads past the last step re-read the
+  // K loop.  Step s computes from LDS slot s%2 and weight register set
+  // s%RING.  A step first writes the activation rows of step s+1 (loaded one
+  // step earlier) to the other LDS slot, then issues the activation loads of
+  // step s+2 and the weight loads of step s+RING-1, then runs the MFMAs of
+  // step s; one barrier ends the step.  Load counters complete in order, so
+  // this order lets the wait for the activations skip the younger weight
+  // loads, which keep RING-1 steps to arrive.  Loads past the last step re-read the
   // last step (cache hits): every step has the same shape and the
   // compiler's counter waits stay exact.
   auto step = [&](int s, const BFrag<S>(&bc)[NSUB], BFrag<S>(&bl)[NSUB])
       __attribute__((always_inline)) {
     store_a(ar, (s + 1) & 1);
     load_a(ar, min(s + 2, n - 1));
-    load_b(bl, min(s + 3, n - 1));
+    load_b(bl, min(s + RING - 1, n - 1));
     if (s < n) compute(s & 1, bc);
     __syncthreads();
+  };
+  // RING steps from s0 (a multiple of RING): step s0+u computes from ring
+  // slot u and loads into the slot freed by the step before.
+  auto group = [&](int s0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < RING; u++) step(s0 + u, bq[u], bq[(u + RING - 1) % RING]);
   };
 
   int wi = w_begin + slot;
@@ -334,7 +345,8 @@ __global__ __launch_bounds__(WAVES * 64)
   decode_meta();
   int buf = 0;
   setup_rows(wi, buf);
-  meta_loads(wi);
+  setup_aoff(buf);
+  meta_loads(wi, buf);
   setup_loads();
   bool first = true;
   while (true) {
@@ -369,45 +381,33 @@ __global__ __launch_bounds__(WAVES * 64)
       for (int s = 0; s < NSUB; s++) enrow[s] = nrow[s];
     };
     if constexpr (XT) {
-      // n % 4 == 0.  The last four steps are written out: the loads that
+      // n % RING == 0.  The last RING steps are written out: the loads that
       // would run past step n-1 fetch the next tile's activations of steps
-      // 0-1 and weights of steps 0-2 instead (the current tile's last step
-      // again when there is no next tile), into the slots and registers that
-      // tile's step 0 expects.  Its row set-up runs between the last loads
-      // of this tile and the first of the next, and has no global loads of
-      // its own: a load issued on only some paths would make every later
-      // counter wait of the loop a conservative one.
-      for (int s = 0; s < n - 4; s += 4) {
-        step(s, b0, b3);
-        step(s + 1, b1, b0);
-        step(s + 2, b2, b1);
-        step(s + 3, b3, b2);
+      // 0-1 and weights of steps 0 to RING-2 instead (the current tile's last
+      // step again when there is no next tile), into the slots and registers
+      // that tile's step 0 expects.  Its row set-up runs before the first of
+      // those weight loads, its activation offsets before the first of those
+      // activation loads; neither has global loads of its own: a load issued
+      // on only some paths would make every later counter wait of the loop a
+      // conservative one.
+      for (int s = 0; s < n - RING; s += RING) group(s);
+      step(n - RING, bq[0], bq[RING - 1]);
+#pragma unroll
+      for (int u = 1; u < RING; u++) {
+        const int s = n - RING + u;
+        store_a(ar, (s + 1) & 1);
+        if (u == RING - 2 && more) setup_aoff(buf ^ 1);
+        load_a(ar, s + 2 < n ? s + 2 : (more ? s + 2 - n : n - 1));
+        if (u == 1) {
+          keep_epilogue_state();
+          if (more) setup_rows(wn, buf ^ 1);
+        }
+        load_b(bq[u - 1], more ? u - 1 : n - 1);
+        compute(s & 1, bq[u]);
+        __syncthreads();
       }
-      step(n - 4, b0, b3);
-      store_a(ar, 0);  // step n-2
-      load_a(ar, n - 1);
-      keep_epilogue_state();
-      if (more) setup_rows(wn, buf ^ 1);
-      load_b(b0, more ? 0 : n - 1);
-      compute(1, b1);  // step n-3
-      __syncthreads();
-      store_a(ar, 1);  // step n-1
-      load_a(ar, more ? 0 : n - 1);
-      load_b(b1, more ? 1 : n - 1);
-      compute(0, b2);  // step n-2
-      __syncthreads();
-      store_a(ar, 0);  // the next tile's step 0
-      load_a(ar, more ? 1 : n - 1);
-      load_b(b2, more ? 2 : n - 1);
-      compute(1, b3);  // step n-1
-      __syncthreads();
     } else {
-      for (int s = 0; s < n; s += 4) {
-        step(s, b0, b3);
-        step(s + 1, b1, b0);
-        step(s + 2, b2, b1);
-        step(s + 3, b3, b2);
-      }
+      for (int s = 0; s < n; s += RING) group(s);
       // The next tile's set-up and first loads run before this tile's
       // epilogue, so that those loads are in flight while the epilogue
       // computes and stores (issued after its stores they would queue
@@ -415,7 +415,8 @@ __global__ __launch_bounds__(WAVES * 64)
       keep_epilogue_state();
       if (more) {
         setup_rows(wn, buf ^ 1);
-        meta_loads(wn);
+        setup_aoff(buf ^ 1);
+        meta_loads(wn, buf ^ 1);
         setup_loads();
       }
     }
@@ -524,41 +525,52 @@ __global__ __launch_bounds__(WAVES * 64)
       }
     }
     if (!more) break;
-    if constexpr (XT) meta_loads(wn);
+    if constexpr (XT) meta_loads(wn, buf ^ 1);
     wi = wn;
     buf ^= 1;
     __syncthreads();  // the epilogue is done with the LDS tile before the next store_a
   }
 }
 
-template <int S, int STAGE, int BM, bool PK, int NSUB, int WAVES, bool XT>
+template <int S, int STAGE, int BM, bool PK, int NSUB, int WAVES, bool XT, int RING>
 hipError_t launch_xt(const GemmArgs& g, hipStream_t s) {
   static int blocks_per_cu = 0;
   if (blocks_per_cu == 0) {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, moe_gemm_kernel<S, STAGE, BM, PK, NSUB, WAVES, XT>, WAVES * 64, 0) != hipSuccess ||
+            &n, moe_gemm_kernel<S, STAGE, BM, PK, NSUB, WAVES, XT, RING>, WAVES * 64, 0) !=
+            hipSuccess ||
         n < 1)
       n = 1;
     blocks_per_cu = n;
   }
   int nblk = device_cu_count() * blocks_per_cu;
   nblk = nblk < 8 ? 8 : (nblk / 8) * 8;
-  hipLaunchKernelGGL((moe_gemm_kernel<S, STAGE, BM, PK, NSUB, WAVES, XT>), dim3(nblk),
+  hipLaunchKernelGGL((moe_gemm_kernel<S, STAGE, BM, PK, NSUB, WAVES, XT, RING>), dim3(nblk),
                      dim3(WAVES * 64), 0, s, g);
   return hipGetLastError();
 }
 
-// Stage 1 runs the cross-tile pipeline whenever its K loop has a multiple of
-// four steps (the register ring's length).
+// Tiles of up to 32 rows (16 for a8w4, whose larger steps leave no
+// registers for it at 32) stream few weight bytes per step, so their weight
+// ring is eight steps long (seven steps of loads in flight) when the K loop
+// has a multiple of eight steps; four otherwise.  Stage 1 runs the
+// cross-tile pipeline whenever its K loop has a multiple of the ring's
+// steps.
 template <int S, int STAGE, int BM, bool PK, int NSUB, int WAVES>
 hipError_t launch_one(const GemmArgs& g, hipStream_t s) {
-  if constexpr (STAGE == 1) {
-    const int nsteps = g.K / Tr<S>::BK;
-    if (nsteps >= 4 && nsteps % 4 == 0)
-      return launch_xt<S, STAGE, BM, PK, NSUB, WAVES, true>(g, s);
+  const int nsteps = g.K / Tr<S>::BK;
+  if constexpr (BM <= (S == kA8W4 ? 16 : 32)) {
+    if (nsteps % 8 == 0) {
+      if (STAGE == 1) return launch_xt<S, STAGE, BM, PK, NSUB, WAVES, STAGE == 1, 8>(g, s);
+      return launch_xt<S, STAGE, BM, PK, NSUB, WAVES, false, 8>(g, s);
+    }
   }
-  return launch_xt<S, STAGE, BM, PK, NSUB, WAVES, false>(g, s);
+  if constexpr (STAGE == 1) {
+    if (nsteps >= 4 && nsteps % 4 == 0)
+      return launch_xt<S, STAGE, BM, PK, NSUB, WAVES, true, 4>(g, s);
+  }
+  return launch_xt<S, STAGE, BM, PK, NSUB, WAVES, false, 4>(g, s);
 }
 
 template <int S, int STAGE, bool PK>
