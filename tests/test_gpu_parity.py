@@ -210,6 +210,15 @@ def test_small_shapes_other_schemes(scheme, prepacked):
         _parity_full(sh, bm, prepacked)
 
 
+@pytest.mark.parametrize("scheme", ["w8a8", "a8w4"])
+def test_long_intermediate_rows(scheme):
+    """I = 2304: h rows longer than one requantization pass (2048 columns),
+    and a stage 2 beyond the LDS-resident activation size."""
+    sh = MoEShape(f"long_inter_{scheme}", scheme, tokens=48, hidden=256, inter=2304, experts=8,
+                  topk=2, seed=78)
+    _parity_full(sh, 16)
+
+
 def _parity_sampled(shape, n_sample=24, prepacked=False):
     _flush(f"ffn sampled {shape.name} prepacked={prepacked}")
     inp = synth.make_inputs(shape)
