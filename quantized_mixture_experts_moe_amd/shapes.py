@@ -94,14 +94,22 @@ def shape_by_name(name: str) -> MoEShape:
 
 
 def default_block_m(shape: MoEShape) -> int:
-    """Tile height for a shape: about the mean rows per expert, 16..128.
+    """Tile height for a shape, from the mean rows per expert (measured on
+    one MI355X for the workloads of the sweep).
 
-    Row tiles never straddle experts, so a tile much taller than an expert's
-    row count is mostly padding (skipped in 16-row groups by the kernels);
-    at >= 128 rows per expert the tallest tile is used.
+    Row tiles never straddle experts and each row tile streams its expert's
+    weights once, so taller tiles read the weights fewer times but carry
+    more padding (skipped in 16-row groups).  Up to 12 rows per expert: 16.
+    Up to 40: 64 (one or two tiles per expert; 32 measured slower).  Up to
+    96: 128 (one tile per expert, weights read once).  Above 96 with an even
+    routing, 64: a second 128-row tile would be mostly padding.  Skewed
+    routing keeps 128 for its heavy experts.
     """
     mean_rows = shape.pairs / shape.experts
-    for bm in (16, 32, 64):
-        if mean_rows <= bm:
-            return bm
-    return 128
+    if mean_rows <= 12:
+        return 16
+    if mean_rows <= 40:
+        return 64
+    if mean_rows <= 96 or shape.zipf_s:
+        return 128
+    return 64

@@ -191,8 +191,9 @@ def test_qwen3moe_w4a16_full(prepacked):
 
 
 @LAYOUTS
-def test_w8a8_full_bitexact_accumulators(prepacked):
-    _parity_full(W8A8_T2048, prepacked=prepacked)
+@pytest.mark.parametrize("bm", [64, 128])
+def test_w8a8_full_bitexact_accumulators(bm, prepacked):
+    _parity_full(W8A8_T2048, bm, prepacked)
 
 
 @LAYOUTS
