@@ -89,14 +89,32 @@ struct BFrag {
   uint32_t sc;  // w4a16: fp16 group scale bits; a8w4: two e8m0 bytes; w8a8: unused
 };
 
+// Eight int4 codes (two's complement, element i in bits 4i..4i+3) times the
+// group scale, each rounded once to bf16 (RNE).  The nibbles are spread
+// into bytes and offset by 8 (q + 8 = nibble ^ 8, in 0..15), so each one
+// converts to float in one instruction; q*s = fma(q + 8, s, -8s) is exact
+// (q*s needs at most 15 significant bits), so the only rounding is the
+// final one to bf16: the same values as converting q and multiplying.
 __device__ inline bf16x8 dequant8_bf16(uint32_t v, float sc) {
-  bf16x8 r;
+  uint32_t even = (v & 0x0F0F0F0Fu) ^ 0x08080808u;         // elements 0, 2, 4, 6
+  uint32_t odd = ((v >> 4) & 0x0F0F0F0Fu) ^ 0x08080808u;   // elements 1, 3, 5, 7
+  // An empty asm hides the known-zero high nibbles from the compiler, which
+  // otherwise re-extracts each byte with a shift and a mask instead of
+  // converting it in place (v_cvt_f32_ubyte1..3).
+  asm("" : "+v"(even), "+v"(odd));
+  const float off = -8.0f * sc;
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  u32x4 w;
 #pragma unroll
-  for (int i = 0; i < 8; i++) {
-    const int q = __builtin_amdgcn_sbfe((int)v, 4 * i, 4);  // two's-complement nibble
-    r[i] = (__bf16)((float)q * sc);                          // exact product, one RNE rounding
+  for (int j = 0; j < 4; j++) {
+    const float e = (float)((even >> (8 * j)) & 0xFFu);
+    const float o = (float)((odd >> (8 * j)) & 0xFFu);
+    const bf16x2 pr = __builtin_convertvector(
+        (f32x2){__builtin_fmaf(e, sc, off), __builtin_fmaf(o, sc, off)}, bf16x2);
+    w[j] = __builtin_bit_cast(uint32_t, pr);
   }
-  return r;
+  return __builtin_bit_cast(bf16x8, w);
 }
 
 // A step's weight fragment in the form the MFMAs take: w4a16 dequantizes
