@@ -20,6 +20,9 @@ QMOE_OK, QMOE_ERR_INVALID_ARG, QMOE_ERR_UNSUPPORTED, QMOE_ERR_HIP = 0, 1, 2, 3
 QMOE_DT_BF16, QMOE_DT_F32 = 0, 1
 QMOE_FLAG_DUMP_ACC = 1
 QMOE_FLAG_PREPACKED = 2
+# QMOE_ABI_VERSION of the include/qmoe.h this binding follows; loading a
+# library that reports another version fails.
+ABI_VERSION = 2
 
 # Every symbol include/qmoe.h declares.
 EXPORTS = (
@@ -60,6 +63,9 @@ def _lib() -> ctypes.CDLL:
     L = ctypes.CDLL(LIB_PATH)
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     L.qmoe_abi_version.restype = ctypes.c_int
+    if L.qmoe_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{LIB_PATH} reports ABI version {L.qmoe_abi_version()}, this "
+                           f"binding expects {ABI_VERSION}; rebuild the library")
     L.qmoe_status_str.restype = ctypes.c_char_p
     L.qmoe_status_str.argtypes = [ctypes.c_int]
     L.qmoe_last_hip_error.restype = ctypes.c_int

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = ops.lib()
-    assert L.qmoe_abi_version() == 2
+    assert L.qmoe_abi_version() == 2 == ops.ABI_VERSION
     for s in range(4):
         assert L.qmoe_status_str(s)
     assert L.qmoe_status_str(99) == b"unknown status"
