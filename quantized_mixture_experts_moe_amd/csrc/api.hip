@@ -287,7 +287,7 @@ static qmoe_status grouped_ffn_impl(const qmoe_ffn_desc* d, const void* x, const
     g2.ntiles_n = d->H / stage2_resident_cols();
     const long tiles = (long)cap / d->block_m;
     for (int p = g2.ntiles_n; p >= 1; p--) {
-      if (g2.ntiles_n % p != 0) continue;
+      if (g2.ntiles_n % p != 0 || p > stage2_resident_max_passes(d->scheme)) continue;
       passes = p;
       if (tiles * (g2.ntiles_n / p) >= 4L * device_cu_count()) break;
     }

@@ -149,6 +149,7 @@ __global__ __launch_bounds__(WAVES * 64)
   // per-lane offset, so the loads use the scalar-base + 32-bit-offset form.
   int t_mt = 0, t_nt = 0, t_e = 0, t_nvalid = 0, t_mvalid = 0;
   float t_scale = 0.f;
+  float t_ws[S == kW8A8 ? NSUB : 1];  // W8A8 weight scales of the K loop's tile
   int nrow[NSUB];
   const uint8_t* __restrict__ Bexp = B;
   const uint8_t* __restrict__ Sexp = reinterpret_cast<const uint8_t*>(g.b_scale);
@@ -356,6 +357,14 @@ __global__ __launch_bounds__(WAVES * 64)
     // wait for this tile's first loads has to happen anyway.
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     decode_meta();
+    // W8A8: the per-channel weight scales of this tile's columns, loaded
+    // before any of its K loop's loads, so that the epilogue's wait for them
+    // does not wait for the next tile's loads already in flight.
+    if constexpr (S == kW8A8) {
+#pragma unroll
+      for (int s = 0; s < NSUB; s++)
+        t_ws[s] = reinterpret_cast<const float*>(g.b_scale)[(size_t)t_e * g.N + nrow[s]];
+    }
     mvalid = t_mvalid;
 #pragma unroll
     for (int m = 0; m < MSUB; m++)
@@ -448,10 +457,9 @@ __global__ __launch_bounds__(WAVES * 64)
               const int cl = wave * HALF * 16 + s * 16 + lr;  // h column inside the tile
               float gf, uf;
               if constexpr (S == kW8A8) {
-                const float* ws = reinterpret_cast<const float*>(g.b_scale) + (size_t)e * g.N;
                 const float xs = rscs[r];
-                gf = ((float)acc[m][s][r] * xs) * ws[enrow[s]];
-                uf = ((float)acc[m][s + HALF][r] * xs) * ws[enrow[s + HALF]];
+                gf = ((float)acc[m][s][r] * xs) * t_ws[s];
+                uf = ((float)acc[m][s + HALF][r] * xs) * t_ws[s + HALF];
                 if (g.dump != nullptr && tok >= 0) {
                   g.dump[orow * 2 * g.I + enrow[s]] = acc[m][s][r];
                   g.dump[orow * 2 * g.I + enrow[s + HALF]] = acc[m][s + HALF][r];
@@ -477,8 +485,7 @@ __global__ __launch_bounds__(WAVES * 64)
             for (int s = 0; s < NSUB; s++) {
               const int cl = wave * NSUB * 16 + s * 16 + lr;  // output column inside the tile
               if constexpr (S == kW8A8) {
-                const float ws2 =
-                    reinterpret_cast<const float*>(g.b_scale)[(size_t)e * g.N + enrow[s]];
+                const float ws2 = t_ws[s];
                 *reinterpret_cast<float*>(trow + cl * 4) = ((float)acc[m][s][r] * rs) * ws2;
                 if (g.dump != nullptr && pair >= 0) g.dump[orow * g.H + enrow[s]] = acc[m][s][r];
               } else if constexpr (S == kA8W4) {

@@ -35,6 +35,7 @@ constexpr int kS2RowBytes = 1024;                 // largest activation row held
 // LDS row pitch: the 32-byte pad makes the 16-byte fragment reads (16 rows
 // at 16q + 64f) free of bank conflicts on gfx950, measured.
 constexpr int kS2Pitch = kS2RowBytes + 32;
+constexpr int kS2MaxPasses = 16;  // W8A8: column passes whose weight scales sit in LDS
 
 // One MFMA step with the weight fragment as the A operand.
 template <int S>
@@ -74,6 +75,10 @@ moe_stage2_resident(GemmArgs g, int passes) {
   __shared__ __attribute__((aligned(16))) int sRow[BM];
   __shared__ __attribute__((aligned(16))) float sScale[BM];
   __shared__ int sExpert;
+  // W8A8: the item's per-channel weight scales (its columns are one
+  // contiguous range of passes * kS2Cols), copied at the item's start so
+  // that no pass epilogue waits on a global load behind the weight stream.
+  __shared__ __attribute__((aligned(16))) float sWs[S == kW8A8 ? kS2MaxPasses * kS2Cols : 4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lq = lane >> 4;
@@ -114,6 +119,11 @@ moe_stage2_resident(GemmArgs g, int passes) {
     const int nvalid = __syncthreads_count(valid_here);
     const int mvalid = (nvalid + 15) >> 4;
     const int e = sExpert;
+    if constexpr (S == kW8A8) {
+      const float* ws = reinterpret_cast<const float*>(g.b_scale) + (size_t)e * g.N +
+                        (size_t)c * passes * kS2Cols;
+      for (int i = tid; i < passes * kS2Cols; i += kS2Threads) sWs[i] = ws[i];
+    }
 
     // Weight cursor: the load for global step gs of this item reads column
     // pass gs / nsteps, K step gs % nsteps; steps past the item re-read its
@@ -233,7 +243,7 @@ moe_stage2_resident(GemmArgs g, int passes) {
                                           (size_t)pair * g.H + col) = make_uint2(lo, hi);
             } else {
               const float4 ws = *reinterpret_cast<const float4*>(
-                  reinterpret_cast<const float*>(g.b_scale) + (size_t)e * g.N + col);
+                  &sWs[p * kS2Cols + wave * kS2Nsub * 16 + 4 * lq + s * 16]);
               const float4 y = make_float4(((float)acc[m][s][0] * rs) * ws.x,
                                            ((float)acc[m][s][1] * rs) * ws.y,
                                            ((float)acc[m][s][2] * rs) * ws.z,
@@ -300,8 +310,11 @@ bool stage2_resident_ok(int scheme, int I) {
 
 int stage2_resident_cols() { return kS2Cols; }
 
+int stage2_resident_max_passes(int scheme) { return scheme == 1 ? kS2MaxPasses : 1 << 30; }
+
 hipError_t launch_stage2_resident(int scheme, int block_m, bool packed, const GemmArgs& g,
                                   int passes, hipStream_t s) {
+  if (scheme == 1 && passes > kS2MaxPasses) return hipErrorInvalidValue;
   if (scheme == 2)
     return packed ? launch_s2r_bm<kA8W4, true>(block_m, g, passes, s)
                   : launch_s2r_bm<kA8W4, false>(block_m, g, passes, s);

@@ -53,6 +53,7 @@ hipError_t launch_gemm(int scheme, int stage, int block_m, bool packed, int nsub
 // of them (ntiles_n must be a multiple of passes).
 bool stage2_resident_ok(int scheme, int I);
 int stage2_resident_cols();
+int stage2_resident_max_passes(int scheme);  // bound on passes per work item
 hipError_t launch_stage2_resident(int scheme, int block_m, bool packed, const GemmArgs& g,
                                   int passes, hipStream_t s);
 hipError_t launch_prepack(int scheme, int E, int N, int K, const void* codes, const void* scales,
