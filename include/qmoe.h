@@ -213,7 +213,7 @@ qmoe_status qmoe_grouped_ffn_profiled(const qmoe_ffn_desc* d, const void* x,
  * result is bitwise reproducible (hip-ep PR, description: deterministic
  * scatter order).  y_pairs dtype: QMOE_DT_BF16 or QMOE_DT_F32.
  * out_bf16 [T,H] (round to nearest even) and/or out_f32 [T,H]; at least
- * one must be non-NULL.  Requires H % 8 == 0.                            */
+ * one must be non-NULL when T > 0.  Requires H % 8 == 0.                 */
 qmoe_status qmoe_combine(const void* y_pairs, int32_t y_dtype, const float* topk_w,
                          int32_t T, int32_t k, int32_t H, uint16_t* out_bf16,
                          float* out_f32, void* stream);

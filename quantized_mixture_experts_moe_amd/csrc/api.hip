@@ -361,8 +361,8 @@ qmoe_status qmoe_combine(const void* y_pairs, int32_t y_dtype, const float* topk
                          int32_t k, int32_t H, uint16_t* out_bf16, float* out_f32, void* stream) {
   if (T < 0 || k < 1 || H <= 0 || H % 8 != 0) return QMOE_ERR_INVALID_ARG;
   if (y_dtype != QMOE_DT_BF16 && y_dtype != QMOE_DT_F32) return QMOE_ERR_INVALID_ARG;
+  if (T == 0) return QMOE_OK;  // nothing to write (the outputs may be empty, null buffers)
   if (!out_bf16 && !out_f32) return QMOE_ERR_INVALID_ARG;
-  if (T == 0) return QMOE_OK;
   if (!y_pairs || !topk_w) return QMOE_ERR_INVALID_ARG;
   if (!aligned(y_pairs, 16) || (out_bf16 && !aligned(out_bf16, 16)) ||
       (out_f32 && !aligned(out_f32, 16)))

@@ -124,6 +124,8 @@ def test_combine_validation():
     assert L.qmoe_combine(p, 7, p, 4, 2, 16, p, None, None) == ops.QMOE_ERR_INVALID_ARG  # dtype
     assert L.qmoe_combine(p, 0, p, 4, 2, 16, None, None, None) == ops.QMOE_ERR_INVALID_ARG
     assert L.qmoe_combine(None, 0, None, 0, 2, 16, p, None, None) == ops.QMOE_OK  # T = 0
+    # T = 0 with empty (null) outputs as well: still a no-op, not an error.
+    assert L.qmoe_combine(None, 0, None, 0, 2, 16, None, None, None) == ops.QMOE_OK
 
 
 def test_prepack_validation():

@@ -211,6 +211,35 @@ def test_small_shapes_other_schemes(scheme, prepacked):
         _parity_full(sh, bm, prepacked)
 
 
+@pytest.mark.parametrize("scheme", ["w4a16", "w8a8", "a8w4"])
+@pytest.mark.parametrize("T,E,k", [(1, 4, 1), (3, 1, 1), (40, 4, 4), (17, 6, 3)])
+def test_degenerate_routing(scheme, T, E, k):
+    """One token; one expert (the dense FFN); every expert per token; an odd
+    token count: each through the whole path against the oracle."""
+    I = 256 if scheme == "a8w4" else 128
+    sh = MoEShape(f"edge_{scheme}_T{T}_E{E}_k{k}", scheme, tokens=T, hidden=256, inter=I,
+                  experts=E, topk=k, seed=90 + T + E + k)
+    _parity_full(sh, 16)
+
+
+@pytest.mark.parametrize("scheme", ["w4a16", "w8a8", "a8w4"])
+def test_empty_batch_is_a_no_op(scheme):
+    """T = 0: every entry point returns OK and launches nothing that writes."""
+    _flush(f"empty batch {scheme}")
+    sh = MoEShape(f"empty_{scheme}", scheme, tokens=8, hidden=256, inter=256, experts=4, topk=2,
+                  seed=95)
+    inp = synth.make_inputs(sh)
+    g = gpu_inputs(inp)
+    W = {k: g[k] for k in WEIGHT_KEYS}
+    x0 = g["x"][:0]
+    xs0 = None if g["x_scale"] is None else g["x_scale"][:0]
+    r = ops.moe_forward(sh.scheme, g["logits"][:0], x0, xs0, W, sh.topk, 16,
+                        want_f32=sh.scheme == "w8a8")
+    torch.cuda.synchronize()
+    assert r["out"].shape == (0, sh.hidden)
+    assert int(r["align"]["num_padded"].item()) == 0
+
+
 @pytest.mark.parametrize("scheme", ["w8a8", "a8w4"])
 def test_long_intermediate_rows(scheme):
     """I = 2304: h rows longer than one requantization pass (2048 columns),
