@@ -17,7 +17,10 @@
 //     below).  The same launch writes the padding sentinels, the
 //     tile->expert map and the tail, spread over at least 32 blocks.
 // Up to 1024 tokens all three steps run in one block of one launch
-// (align_small_kernel): short prefills pay one launch, not three.
+// (align_small_kernel): short prefills pay one launch, not three.  Up to
+// 64 chunks (16384 tokens) the scan runs inside the scatter launch
+// (align_place_kernel): every block reads the whole count matrix and scans
+// it itself, so two launches remain.
 #include "qmoe_internal.h"
 
 namespace qmoe {
@@ -213,7 +216,9 @@ __global__ __launch_bounds__(kChunk) void align_scatter_kernel(
 constexpr int kSmallT = 1024;
 constexpr int kSmallWaves = kSmallT / 64;
 
-__device__ inline int block_excl_scan_1024(int v, int* s_wave) {
+// Exclusive prefix sum of v over the block (any size up to 1024 threads);
+// s_wave holds one int per wave.
+__device__ inline int block_excl_scan(int v, int* s_wave) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   int x = v;
 #pragma unroll
@@ -263,7 +268,7 @@ __global__ __launch_bounds__(kSmallT) void align_small_kernel(
     for (int w = 0; w < kSmallWaves; w++) tot += __popcll(mask[w * E + tid]);
   }
   const int pe = ((tot + bm - 1) >> bm_shift) << bm_shift;
-  const int off = block_excl_scan_1024(tid < E ? pe : 0, s_wave);
+  const int off = block_excl_scan(tid < E ? pe : 0, s_wave);
   if (tid < E) {
     s_tot[tid] = tot;
     s_off[tid] = off;
@@ -298,6 +303,114 @@ __global__ __launch_bounds__(kSmallT) void align_small_kernel(
   for (int i = (npad >> bm_shift) + tid; i < (cap >> bm_shift); i += kSmallT) tile_expert[i] = -1;
 }
 
+// count + scan + scatter in two launches for nchunks <= kPlaceMaxChunks:
+// after align_count_kernel, every block of this launch reads the whole
+// count matrix (E x nchunks ints, from L2), takes each expert's total and
+// the pairs of the chunks before its own, and scans the padded totals
+// itself; block 0 writes the expert offsets, num_padded and the flag word
+// (the OR of the chunks' flags).  Blocks below nchunks then place their
+// chunk's pairs (as align_scatter_kernel), and every block takes a share of
+// the padding.
+constexpr int kPlaceMaxChunks = 64;
+
+__global__ __launch_bounds__(kChunk) void align_place_kernel(
+    const int32_t* __restrict__ ids, int T, int k, int E, int nchunks, int bm_shift, int cap,
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ chunk_flags,
+    int32_t* __restrict__ sorted, int32_t* __restrict__ tile_expert,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ num_padded,
+    int32_t* __restrict__ flags) {
+  extern __shared__ unsigned long long mask[];  // [4][E]
+  __shared__ int s_before[kMaxExperts];
+  __shared__ int s_tot[kMaxExperts];
+  __shared__ int s_off[kMaxExperts + 1];
+  __shared__ int s_wave[kChunk / 64];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int P = T * k;
+  const int own = blockIdx.x;  // the chunk this block places, if below nchunks
+  const int t = own * kChunk + tid;
+  const bool placing = own < nchunks;  // the same for the whole block
+  const bool mine = placing && t < T;
+  // This thread's token ids (up to kRegK of them kept in registers), loaded
+  // before the count matrix so that both round trips overlap.
+  constexpr int kRegK = 16;
+  int te[kRegK];
+#pragma unroll
+  for (int j = 0; j < kRegK; j++) te[j] = mine && j < k ? ids[(size_t)t * k + j] : -1;
+  if (placing)
+    for (int i = tid; i < 4 * E; i += kChunk) mask[i] = 0ull;
+  for (int e = tid; e < E; e += kChunk) {
+    const int32_t* row = counts + (size_t)e * nchunks;
+    int tot = 0, before = 0;
+#pragma unroll 8
+    for (int c = 0; c < nchunks; c++) {
+      const int v = row[c];
+      tot += v;
+      before += c < own ? v : 0;
+    }
+    s_tot[e] = tot;
+    s_before[e] = before;
+  }
+  __syncthreads();
+  auto set_bit = [&](int e) __attribute__((always_inline)) {
+    if (e >= 0 && e < E) atomicOr(&mask[wave * E + e], 1ull << lane);
+  };
+#pragma unroll
+  for (int j = 0; j < kRegK; j++)
+    if (mine && j < k) set_bit(te[j]);
+  for (int j = kRegK; j < k; j++)
+    if (mine) set_bit(ids[(size_t)t * k + j]);
+  // Padded offsets: thread tid owns a contiguous run of experts.
+  const int per = (E + kChunk - 1) / kChunk;
+  const int r0 = min(E, tid * per), r1 = min(E, r0 + per);
+  int run = 0;
+  for (int e = r0; e < r1; e++) run += ((s_tot[e] + (1 << bm_shift) - 1) >> bm_shift) << bm_shift;
+  int base = block_excl_scan(run, s_wave);
+  for (int e = r0; e < r1; e++) {
+    s_off[e] = base;
+    base += ((s_tot[e] + (1 << bm_shift) - 1) >> bm_shift) << bm_shift;
+  }
+  if (tid == kChunk - 1) s_off[E] = base;
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    for (int e = tid; e <= E; e += kChunk) offsets[e] = s_off[e];
+    int bad = 0;
+    for (int c = tid; c < nchunks; c += kChunk) bad |= chunk_flags[c];
+    const int b1 = __syncthreads_or(bad & 1);
+    const int b2 = __syncthreads_or(bad & 2);
+    if (tid == 0) {
+      *num_padded = s_off[E];
+      *flags = (b1 ? 1 : 0) | (b2 ? 2 : 0);
+    }
+  }
+  // Pair (t, j) goes to its expert's offset + the pairs of earlier chunks,
+  // earlier waves and earlier lanes; j ascending, so a repeated id keeps the
+  // later pair, as in the other paths.
+  const unsigned long long below = (1ull << lane) - 1ull;
+  auto place = [&](int e, int j) __attribute__((always_inline)) {
+    if (e < 0 || e >= E) return;
+    int rank = s_before[e] + __popcll(mask[wave * E + e] & below);
+    for (int w = 0; w < wave; w++) rank += __popcll(mask[w * E + e]);
+    sorted[s_off[e] + rank] = t * k + j;
+  };
+#pragma unroll
+  for (int j = 0; j < kRegK; j++)
+    if (mine && j < k) place(te[j], j);
+  for (int j = kRegK; j < k; j++)
+    if (mine) place(ids[(size_t)t * k + j], j);
+  const int nwaves = gridDim.x * (kChunk / 64);
+  for (int e = blockIdx.x * (kChunk / 64) + wave; e < E; e += nwaves) {
+    const int o = s_off[e], n = s_tot[e], end = s_off[e + 1];
+    for (int i = (o >> bm_shift) + lane; i < (end >> bm_shift); i += 64) tile_expert[i] = e;
+    for (int i = o + n + lane; i < end; i += 64) sorted[i] = P;
+  }
+  const int npad = s_off[E];
+  const int stride = gridDim.x * kChunk;
+  for (int i = npad + blockIdx.x * kChunk + tid; i < cap; i += stride) sorted[i] = P;
+  for (int i = (npad >> bm_shift) + blockIdx.x * kChunk + tid; i < (cap >> bm_shift);
+       i += stride)
+    tile_expert[i] = -1;
+}
+
 }  // namespace
 
 hipError_t launch_align(const int32_t* ids, int T, int k, int E, int block_m, int32_t* sorted,
@@ -321,12 +434,18 @@ hipError_t launch_align(const int32_t* ids, int T, int k, int E, int block_m, in
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
+  // At least 32 blocks share the padding writes even when there are few chunks.
+  const int nblk = nchunks > 32 ? nchunks : 32;
+  if (nchunks <= kPlaceMaxChunks) {
+    hipLaunchKernelGGL(align_place_kernel, dim3(nblk), dim3(kChunk), lds, s, ids, T, k, E,
+                       nchunks, __builtin_ctz((unsigned)block_m), cap, chunk_counts,
+                       chunk_flags, sorted, tile_expert, offsets, num_padded, flags);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(align_scan_kernel, dim3(1), dim3(1024), 0, s, nchunks, E, block_m,
                      chunk_counts, totals, offsets, num_padded, chunk_flags, flags);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  // At least 32 blocks share the padding writes even when there are few chunks.
-  const int nblk = nchunks > 32 ? nchunks : 32;
   hipLaunchKernelGGL(align_scatter_kernel, dim3(nblk), dim3(kChunk), lds, s, ids, T, k, E,
                      nchunks, block_m, cap, chunk_counts, offsets, totals, sorted, tile_expert);
   return hipGetLastError();

@@ -7,8 +7,14 @@
 //   w8a8: code = clamp(round_half_even(h / s), -127, 127)
 //   a8w4: code = e4m3 round-to-nearest-even of h / s, saturated to +-448.
 // The row absmax is the max of the per-column-tile maxima stage 1 wrote.
-// One wave per row; padding rows are skipped.  The division h / s is kept
-// (not a multiplication by 1/s) so the codes are the correctly rounded ones.
+// One wave per row; padding rows are skipped.  h / s is the correctly
+// rounded fp32 quotient, as a plain division gives, but from one reciprocal
+// per row and two fused multiply-adds per value: with r = RN(1/s) and
+// q = RN(h*r), the remainder h - q*s is exact in an fma and RN(q + rem*r)
+// is the correctly rounded quotient (Markstein's theorem on division by
+// reciprocal refinement; it needs no overflow or underflow in the steps,
+// which s >= 2^-60 and |h| <= 448 s guarantee; rows with a smaller s use
+// the plain division).
 #include "qmoe_internal.h"
 
 namespace qmoe {
@@ -50,8 +56,12 @@ __global__ __launch_bounds__(256) void requant_kernel(const int32_t* __restrict_
                                                       float* __restrict__ hs) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= *num_padded) return;
-  if (sorted[row] >= P) return;  // padding slot
+  // Both loads in one round trip: row < cap always (the grid is cap / 4
+  // blocks and cap is a multiple of block_m), so sorted[row] is in bounds
+  // even past num_padded.
+  const int npad = *num_padded;
+  const int pair = sorted[row];
+  if (row >= npad || pair >= P) return;  // past the tiles, or a padding slot
   const float4* src = reinterpret_cast<const float4*>(h32 + (size_t)row * I);
   uint32_t* dst = reinterpret_cast<uint32_t*>(hq + (size_t)row * I);
   const int n4 = I / 4;
@@ -65,6 +75,13 @@ __global__ __launch_bounds__(256) void requant_kernel(const int32_t* __restrict_
   for (int off = 32; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
   const float s = a > 0.f ? a / (FP8 ? 448.0f : 127.0f) : 1.0f;
   if (lane == 0) hs[row] = s;
+  const bool refine = s >= 0x1p-60f;  // the same for the whole wave
+  const float r = 1.0f / s;
+  auto quot = [&](float x) __attribute__((always_inline)) {
+    if (!refine) return x / s;
+    const float q = x * r;
+    return __builtin_fmaf(__builtin_fmaf(-q, s, x), r, q);
+  };
   for (int base = 0; base < n4; base += 64 * kVec) {
     if (base > 0) {
 #pragma unroll
@@ -75,7 +92,7 @@ __global__ __launch_bounds__(256) void requant_kernel(const int32_t* __restrict_
     for (int i = 0; i < kVec; i++) {
       const int idx = base + lane + 64 * i;
       if (idx < n4) {
-        const float x0 = v[i].x / s, x1 = v[i].y / s, x2 = v[i].z / s, x3 = v[i].w / s;
+        const float x0 = quot(v[i].x), x1 = quot(v[i].y), x2 = quot(v[i].z), x3 = quot(v[i].w);
         dst[idx] = FP8 ? to_e4m3x4(x0, x1, x2, x3) : to_i8x4(x0, x1, x2, x3);
       }
     }
@@ -87,7 +104,8 @@ __global__ __launch_bounds__(256) void requant_kernel(const int32_t* __restrict_
 hipError_t launch_requant(int scheme, const int32_t* sorted, const int32_t* num_padded, int P,
                           int I, int ntiles_n, int cap, const float* h32, const float* pmax,
                           uint8_t* hq, float* hs, hipStream_t s) {
-  const dim3 grid((cap + 3) / 4), block(256);
+  if (cap % 4 != 0) return hipErrorInvalidValue;  // every row of the grid must be below cap
+  const dim3 grid(cap / 4), block(256);
   if (scheme == 2)
     hipLaunchKernelGGL(requant_kernel<true>, grid, block, 0, s, sorted, num_padded, P, I,
                        ntiles_n, h32, pmax, hq, hs);

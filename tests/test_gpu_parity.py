@@ -62,8 +62,13 @@ def _check_align(al, ids_np, E, bm):
 @pytest.mark.parametrize("T,k,E,bm", [(64, 2, 8, 16), (128, 8, 128, 16), (256, 10, 512, 16),
                                       (2048, 8, 128, 128),
                                       (4096, 10, 512, 128), (1, 1, 1, 16), (257, 3, 7, 32),
-                                      (1000, 4, 1024, 64), (8192, 10, 512, 16)])
+                                      (1000, 4, 1024, 64), (8192, 10, 512, 16),
+                                      (1025, 3, 7, 32), (2100, 16, 200, 64),
+                                      (1500, 20, 64, 32), (17000, 2, 64, 64)])
 def test_align_matches_oracle(T, k, E, bm):
+    """One launch up to 1024 tokens, one launch of one block per 1024-token
+    chunk up to 16384 tokens with k <= 16, three launches beyond (the last
+    two cases)."""
     _flush(f"align T={T} k={k} E={E} bm={bm}")
     rng = np.random.default_rng(T + E + bm)
     L = rng.standard_normal((T, E)).astype(np.float32)
@@ -98,6 +103,20 @@ def test_align_empty_and_out_of_range():
     dup = np.array([[3, 3], [1, 2]], np.int32)
     al = ops.align(to_gpu(dup), 8, 16)
     assert ops.check_flags(al["ws"]) & 2
+    # The same cases past 1024 tokens (the chunked single-launch path): every
+    # block sees the bad ids of every chunk.
+    rng = np.random.default_rng(5)
+    ids_np, _ = O.route(rng.standard_normal((3000, 64)).astype(np.float32), 4)
+    ids_np[2500, 1] = -3
+    ids_np[10, 3] = 64
+    al = ops.align(to_gpu(ids_np), 64, 32)
+    torch.cuda.synchronize()
+    _check_align(al, ids_np, 64, 32)
+    assert ops.check_flags(al["ws"]) == 1
+    ids_np, _ = O.route(rng.standard_normal((3000, 64)).astype(np.float32), 4)
+    ids_np[2999, 2] = ids_np[2999, 0]
+    al = ops.align(to_gpu(ids_np), 64, 32)
+    assert ops.check_flags(al["ws"]) == 2
 
 
 # ------------------------------------------------------------------ combine
