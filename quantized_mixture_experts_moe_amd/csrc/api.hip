@@ -256,6 +256,14 @@ static qmoe_status grouped_ffn_impl(const qmoe_ffn_desc* d, const void* x, const
   g1.out = wsb + lay.h;
   g1.row_pmax = quant_act ? reinterpret_cast<float*>(wsb + lay.pmax) : nullptr;
   g1.dump = dump ? reinterpret_cast<int32_t*>(wsb + lay.acc1) : nullptr;
+  // a8w4 with 128-row tiles and more pairs than one tile per expert: the
+  // stage-1 blocks take runs of consecutive row tiles (an expert's second
+  // tile then reads its weights from the memory-side cache); measured
+  // neutral or slower for the other schemes and tile heights.
+  g1.schedule = (d->scheme == QMOE_A8W4_MXFP4 && d->block_m == 128 &&
+                 (long)d->T * d->k > (long)d->E * d->block_m)
+                    ? 1
+                    : 0;
   auto mark = [&](int i) -> hipError_t {
     return events ? hipEventRecord((hipEvent_t)events[i], s) : hipSuccess;
   };
@@ -276,6 +284,7 @@ static qmoe_status grouped_ffn_impl(const qmoe_ffn_desc* d, const void* x, const
   e = mark(2);
   if (e != hipSuccess) return hip_status(e);
 
+  g2.schedule = 0;
   g2.N = d->H;
   g2.K = d->I;
   const bool resident = stage2_resident_ok(d->scheme, d->I);

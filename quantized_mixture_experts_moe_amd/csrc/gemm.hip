@@ -101,11 +101,43 @@ __global__ __launch_bounds__(WAVES * 64)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lq = lane >> 4;
   const int num_m = *g.num_padded / BM;
-  const int total = num_m * g.ntiles_n;
   const int per_xcd = gridDim.x >> 3;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int chunk = (total + 7) >> 3;
-  const int w_begin = xcd * chunk, w_end = min(total, w_begin + chunk);
+  // Work items of this XCD and the order in which this block takes them
+  // (valid(u): the block has a u-th item; decode(u): its row and column
+  // tile):
+  //  - schedule 0: an even share of the row-tile-major item list, the
+  //    blocks of the XCD strided over it;
+  //  - schedule 1 (runs): an even share of the row tiles; the blocks of the
+  //    XCD are split into groups of ntiles_n, block j of a group keeps
+  //    column tile j, and the groups take contiguous runs of row tiles, so
+  //    a block's consecutive items are consecutive row tiles of one column
+  //    tile: when they belong to the same expert the second one reads the
+  //    weights the first has just read (memory-side cache hits).  Taken
+  //    only when per_xcd is a multiple of ntiles_n (schedule 0 otherwise).
+  const int total = num_m * g.ntiles_n;
+  const int ichunk = (total + 7) >> 3;
+  const int w_begin = min(total, xcd * ichunk), w_end = min(total, w_begin + ichunk);
+  const int mchunk = (num_m + 7) >> 3;
+  const int m_begin = min(num_m, xcd * mchunk), nm = min(num_m, m_begin + mchunk) - m_begin;
+  const bool runs = g.schedule == 1 && per_xcd % g.ntiles_n == 0;  // else schedule 0
+  const int groups = per_xcd / g.ntiles_n, grp = slot / g.ntiles_n;
+  const int run_nt = slot - grp * g.ntiles_n;
+  const int run_begin = grp < groups ? (int)((long)grp * nm / groups) : nm;
+  const int run_end = grp < groups ? (int)((long)(grp + 1) * nm / groups) : nm;
+  auto valid = [&](int u) __attribute__((always_inline)) {
+    return runs ? run_begin + u < run_end : w_begin + slot + u * per_xcd < w_end;
+  };
+  auto decode = [&](int u, int& mt_out, int& nt_out) __attribute__((always_inline)) {
+    if (runs) {
+      mt_out = m_begin + run_begin + u;
+      nt_out = run_nt;
+    } else {
+      const int w = w_begin + slot + u * per_xcd;
+      mt_out = w / g.ntiles_n;
+      nt_out = w - mt_out * g.ntiles_n;
+    }
+  };
 
   static_assert(kThreads % CPR == 0, "chunk rows must be thread-invariant");
   static_assert(BM < kThreads, "the last thread loads the tile's expert id");
@@ -123,9 +155,10 @@ __global__ __launch_bounds__(WAVES * 64)
   // through LDS at the set-up barrier: a uniform load would be moved to a
   // scalar register right away, waiting for every load in flight.
   int next_pair = g.P, next_expert = 0, next_ri = -1;
-  auto fetch_meta = [&](int w) __attribute__((always_inline)) {
-    if (w < w_end) {
-      const int m = w / g.ntiles_n;
+  auto fetch_meta = [&](int u) __attribute__((always_inline)) {
+    if (valid(u)) {
+      int m, nt_unused;
+      decode(u, m, nt_unused);
       if (tid < BM) next_pair = g.sorted_pair_ids[m * BM + tid];
       if (tid == kThreads - 1) next_expert = g.tile_expert[m];
     }
@@ -203,9 +236,8 @@ __global__ __launch_bounds__(WAVES * 64)
   // activation offsets.  meta_loads: the per-row scale of tile w and the
   // metadata of the tile after it.  setup_loads: the activation rows of
   // step 0 and the weights of steps 0 to RING-2.
-  auto setup_rows = [&](int w, int bf) __attribute__((always_inline)) {
-    t_mt = w / g.ntiles_n;
-    t_nt = w - t_mt * g.ntiles_n;
+  auto setup_rows = [&](int u, int bf) __attribute__((always_inline)) {
+    decode(u, t_mt, t_nt);
     if (tid == kThreads - 1) sExpert[bf] = next_expert;
     int valid_here = 0;
     if (tid < BM) {
@@ -259,7 +291,7 @@ __global__ __launch_bounds__(WAVES * 64)
       aoff[i] = rbase + col * 16;
     }
   };
-  auto meta_loads = [&](int w, int bf) __attribute__((always_inline)) {
+  auto meta_loads = [&](int u, int bf) __attribute__((always_inline)) {
     // Per-row scale of the epilogue (token scale in stage 1, the
     // requantized h scale in stage 2); the row id is read back from sRow.
     if constexpr (S != kW4A16) {
@@ -268,7 +300,7 @@ __global__ __launch_bounds__(WAVES * 64)
         t_scale = ri >= 0 ? g.a_scale[STAGE == 1 ? ri : (size_t)t_mt * BM + tid] : 0.f;
       }
     }
-    fetch_meta(w + per_xcd);
+    fetch_meta(u + 1);
   };
   auto setup_loads = [&]() __attribute__((always_inline)) {
     load_a(ar, 0);
@@ -340,8 +372,8 @@ __global__ __launch_bounds__(WAVES * 64)
     for (int u = 0; u < RING; u++) step(s0 + u, bq[u], bq[(u + RING - 1) % RING]);
   };
 
-  int wi = w_begin + slot;
-  if (wi >= w_end) return;
+  int wi = 0;  // the block's item counter
+  if (!valid(0)) return;
   fetch_meta(wi);
   decode_meta();
   int buf = 0;
@@ -376,8 +408,8 @@ __global__ __launch_bounds__(WAVES * 64)
       __syncthreads();
     }
     first = false;
-    const int wn = wi + per_xcd;
-    const bool more = wn < w_end;  // the same for the whole block
+    const int wn = wi + 1;
+    const bool more = valid(wn);  // the same for the whole block
 
     // This tile's epilogue state (taken before the next tile's set-up).
     int mt, nt, e, nvalid, enrow[NSUB];

@@ -37,6 +37,7 @@ struct GemmArgs {
   void* out;             // stage 1: h (bf16 or f32) [cap, I]; stage 2: y_pairs [P, H]
   float* row_pmax;       // stage 1 (w8a8/a8w4): |h| max per row and column tile
   int32_t* dump;         // w8a8 debug accumulators or nullptr
+  int schedule;          // stage-1 work order: 0 strided items, 1 runs of row tiles
 };
 
 hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w,

@@ -102,8 +102,11 @@ def default_block_m(shape: MoEShape) -> int:
     more padding (skipped in 16-row groups).  Up to 12 rows per expert: 16.
     Up to 40: 64 (one or two tiles per expert; 32 measured slower).  Up to
     96: 128 (one tile per expert, weights read once).  Above 96 with an even
-    routing, 64: a second 128-row tile would be mostly padding.  Skewed
-    routing keeps 128 for its heavy experts.
+    routing, 64: a second 128-row tile would be mostly padding; except for
+    a8w4 above 128 rows, where 128-row tiles taken in runs of consecutive
+    row tiles (an expert's second tile reads its weights from the
+    memory-side cache) measured faster.  Skewed routing keeps 128 for its
+    heavy experts.
     """
     mean_rows = shape.pairs / shape.experts
     if mean_rows <= 12:
@@ -111,5 +114,7 @@ def default_block_m(shape: MoEShape) -> int:
     if mean_rows <= 40:
         return 64
     if mean_rows <= 96 or shape.zipf_s:
+        return 128
+    if shape.scheme == "a8w4" and mean_rows > 128:
         return 128
     return 64

@@ -230,6 +230,17 @@ def test_small_shapes_other_schemes(scheme, prepacked):
         _parity_full(sh, bm, prepacked)
 
 
+@LAYOUTS
+@pytest.mark.parametrize("T", [1000, 1500])
+def test_a8w4_runs_of_row_tiles(T, prepacked):
+    """a8w4 with 128-row tiles and more pairs than one tile per expert: the
+    stage-1 blocks take runs of consecutive row tiles (the 8192-token
+    workload's schedule); experts of two and three tiles, ragged last tiles."""
+    sh = MoEShape(f"runs_a8w4_T{T}", "a8w4", tokens=T, hidden=512, inter=256, experts=8,
+                  topk=2, seed=300 + T)
+    _parity_full(sh, 128, prepacked)
+
+
 @pytest.mark.parametrize("scheme", ["w4a16", "w8a8", "a8w4"])
 @pytest.mark.parametrize("T,E,k", [(1, 4, 1), (3, 1, 1), (40, 4, 4), (17, 6, 3)])
 def test_degenerate_routing(scheme, T, E, k):
