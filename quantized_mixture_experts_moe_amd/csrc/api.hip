@@ -288,13 +288,16 @@ static qmoe_status grouped_ffn_impl(const qmoe_ffn_desc* d, const void* x, const
   g2.N = d->H;
   g2.K = d->I;
   const bool resident = stage2_resident_ok(d->scheme, d->I);
+  // Where stage 1 takes runs of row tiles (several 128-row tiles per
+  // expert), stage 2 takes each tile as two 64-row work items.
+  const bool half_tiles = resident && g1.schedule == 1;
   int passes = 1;
   if (resident) {
     // Column passes per work item: as many as keep at least four items per
     // CU (by the capacity's tile count), so every item copies its rows to
     // LDS once for as many passes as possible.
     g2.ntiles_n = d->H / stage2_resident_cols();
-    const long tiles = (long)cap / d->block_m;
+    const long tiles = (long)cap / (half_tiles ? d->block_m / 2 : d->block_m);
     for (int p = g2.ntiles_n; p >= 1; p--) {
       if (g2.ntiles_n % p != 0 || p > stage2_resident_max_passes(d->scheme)) continue;
       passes = p;
@@ -310,7 +313,7 @@ static qmoe_status grouped_ffn_impl(const qmoe_ffn_desc* d, const void* x, const
   g2.out = y_pairs;
   g2.row_pmax = nullptr;
   g2.dump = dump ? reinterpret_cast<int32_t*>(wsb + lay.acc2) : nullptr;
-  e = resident ? launch_stage2_resident(d->scheme, d->block_m, packed, g2, passes, s)
+  e = resident ? launch_stage2_resident(d->scheme, d->block_m, half_tiles, packed, g2, passes, s)
                : launch_gemm(d->scheme, 2, d->block_m, packed, gs2.nsub, gs2.waves, g2, s);
   if (e == hipSuccess) e = mark(3);
   return hip_status(e);

@@ -65,7 +65,7 @@ __device__ inline void mfma_step_wa(typename Tr<S>::Acc& acc, const u32x4* a,
 
 template <int S, int BM, bool PK>
 __global__ __launch_bounds__(kS2Threads) __attribute__((amdgpu_waves_per_eu(2, 2))) void
-moe_stage2_resident(GemmArgs g, int passes) {
+moe_stage2_resident(GemmArgs g, int passes, int tile_div) {
   static_assert(S == kW8A8 || S == kA8W4, "one-byte activations only");
   using T_ = Tr<S>;
   using Acc = typename T_::Acc;
@@ -115,8 +115,9 @@ moe_stage2_resident(GemmArgs g, int passes) {
       sScale[tid] = ok ? g.a_scale[(size_t)mt * BM + tid] : 0.f;
       valid_here = ok;
     }
-    if (tid == kS2Threads - 1) sExpert = g.tile_expert[mt];
+    if (tid == kS2Threads - 1) sExpert = g.tile_expert[mt / tile_div];
     const int nvalid = __syncthreads_count(valid_here);
+    if (nvalid == 0) continue;  // a part of a tile past its expert's last row
     const int mvalid = (nvalid + 15) >> 4;
     const int e = sExpert;
     if constexpr (S == kW8A8) {
@@ -283,21 +284,23 @@ moe_stage2_resident(GemmArgs g, int passes) {
 }
 
 template <int S, int BM, bool PK>
-hipError_t launch_s2r(const GemmArgs& g, int passes, hipStream_t s) {
+hipError_t launch_s2r(const GemmArgs& g, int passes, int tile_div, hipStream_t s) {
   int nblk = device_cu_count();
   nblk = nblk < 8 ? 8 : (nblk / 8) * 8;
   hipLaunchKernelGGL((moe_stage2_resident<S, BM, PK>), dim3(nblk), dim3(kS2Threads), 0, s, g,
-                     passes);
+                     passes, tile_div);
   return hipGetLastError();
 }
 
+// rows: the work item's rows (block_m, or half of it, tile_div = 2).
 template <int S, bool PK>
-hipError_t launch_s2r_bm(int block_m, const GemmArgs& g, int passes, hipStream_t s) {
-  switch (block_m) {
-    case 16: return launch_s2r<S, 16, PK>(g, passes, s);
-    case 32: return launch_s2r<S, 32, PK>(g, passes, s);
-    case 64: return launch_s2r<S, 64, PK>(g, passes, s);
-    case 128: return launch_s2r<S, 128, PK>(g, passes, s);
+hipError_t launch_s2r_bm(int rows, int tile_div, const GemmArgs& g, int passes,
+                         hipStream_t s) {
+  switch (rows) {
+    case 16: return launch_s2r<S, 16, PK>(g, passes, tile_div, s);
+    case 32: return launch_s2r<S, 32, PK>(g, passes, tile_div, s);
+    case 64: return launch_s2r<S, 64, PK>(g, passes, tile_div, s);
+    case 128: return launch_s2r<S, 128, PK>(g, passes, tile_div, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -312,15 +315,16 @@ int stage2_resident_cols() { return kS2Cols; }
 
 int stage2_resident_max_passes(int scheme) { return scheme == 1 ? kS2MaxPasses : 1 << 30; }
 
-hipError_t launch_stage2_resident(int scheme, int block_m, bool packed, const GemmArgs& g,
-                                  int passes, hipStream_t s) {
+hipError_t launch_stage2_resident(int scheme, int block_m, bool half_tiles, bool packed,
+                                  const GemmArgs& g, int passes, hipStream_t s) {
   if (scheme == 1 && passes > kS2MaxPasses) return hipErrorInvalidValue;
+  const int rows = half_tiles ? block_m / 2 : block_m, div = half_tiles ? 2 : 1;
   if (scheme == 2)
-    return packed ? launch_s2r_bm<kA8W4, true>(block_m, g, passes, s)
-                  : launch_s2r_bm<kA8W4, false>(block_m, g, passes, s);
+    return packed ? launch_s2r_bm<kA8W4, true>(rows, div, g, passes, s)
+                  : launch_s2r_bm<kA8W4, false>(rows, div, g, passes, s);
   if (scheme == 1)
-    return packed ? launch_s2r_bm<kW8A8, true>(block_m, g, passes, s)
-                  : launch_s2r_bm<kW8A8, false>(block_m, g, passes, s);
+    return packed ? launch_s2r_bm<kW8A8, true>(rows, div, g, passes, s)
+                  : launch_s2r_bm<kW8A8, false>(rows, div, g, passes, s);
   return hipErrorInvalidValue;
 }
 

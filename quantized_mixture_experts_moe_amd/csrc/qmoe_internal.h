@@ -55,8 +55,10 @@ hipError_t launch_gemm(int scheme, int stage, int block_m, bool packed, int nsub
 bool stage2_resident_ok(int scheme, int I);
 int stage2_resident_cols();
 int stage2_resident_max_passes(int scheme);  // bound on passes per work item
-hipError_t launch_stage2_resident(int scheme, int block_m, bool packed, const GemmArgs& g,
-                                  int passes, hipStream_t s);
+// half_tiles: each block_m-row tile is taken as two work items of
+// block_m / 2 rows (an empty second half is skipped).
+hipError_t launch_stage2_resident(int scheme, int block_m, bool half_tiles, bool packed,
+                                  const GemmArgs& g, int passes, hipStream_t s);
 hipError_t launch_prepack(int scheme, int E, int N, int K, const void* codes, const void* scales,
                           void* codes_out, void* scales_out, hipStream_t s);
 hipError_t launch_requant(int scheme, const int32_t* sorted, const int32_t* num_padded,
