@@ -390,3 +390,59 @@ def test_unused_experts_poisoned_do_not_change_output(scheme):
         bad[key] = arr
     out = _run_gpu(sh, bad, bm=32)["out"].cpu()
     assert torch.equal(base.view(torch.int16), out.view(torch.int16))
+
+
+# ------------------------------------------------------------------ HIP graph
+
+@pytest.mark.parametrize("scheme", ["w4a16", "w8a8", "a8w4"])
+@pytest.mark.parametrize("T", [300, 2000])
+def test_graph_replay_matches_eager(scheme, T):
+    """The step (route, align, grouped FFN, combine) captured once as a HIP
+    graph, as bench.py times it.  Between replays an eager step on other
+    logits overwrites every buffer the graph uses; each replay must then
+    reproduce the eager step's outputs bit for bit."""
+    _flush(f"graph replay {scheme} T={T}")
+    I = 256 if scheme == "a8w4" else 128
+    sh = MoEShape(f"graph_{scheme}_T{T}", scheme, tokens=T, hidden=512, inter=I, experts=16,
+                  topk=4, seed=500 + T)
+    inp = synth.make_inputs(sh)
+    g = gpu_inputs(inp)
+    W = {key: g[key] for key in WEIGHT_KEYS}
+    E, k, bm = sh.experts, sh.topk, 64
+    f32 = scheme == "w8a8"
+    logits_other = torch.flip(g["logits"], dims=[1]).contiguous()
+    ids = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    tw = torch.empty((T, k), dtype=torch.float32, device=DEV)
+    ops.route(g["logits"], k, ids, tw)
+    al = ops.align(ids, E, bm)
+    y, ws = ops.grouped_ffn(scheme, g["x"], g["x_scale"], W, al, E, k)
+    ob, of = ops.combine(y, tw, want_bf16=True, want_f32=f32)
+    torch.cuda.synchronize()
+    ref_b, ref_f, ref_ids = ob.clone(), (of.clone() if f32 else None), ids.clone()
+
+    def step(logits):
+        ops.route(logits, k, ids, tw)
+        ops.align(ids, E, bm, out=al)
+        ops.grouped_ffn(scheme, g["x"], g["x_scale"], W, al, E, k, ws=ws, y_pairs=y)
+        ops.combine(y, tw, out_bf16=ob, out_f32=of, want_f32=f32)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(g["logits"])
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(g["logits"])
+    torch.cuda.synchronize()
+    for rep in range(3):
+        step(logits_other)  # eager, other routing, same buffers
+        torch.cuda.synchronize()
+        assert not torch.equal(ids, ref_ids)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ids, ref_ids), f"replay {rep}"
+        assert torch.equal(ob, ref_b), f"replay {rep}"
+        if f32:
+            assert torch.equal(of, ref_f), f"replay {rep}"
