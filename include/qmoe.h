@@ -181,7 +181,9 @@ qmoe_status qmoe_check_flags(const void* align_ws, int32_t* flags_out, void* str
  *   W4A16 and A8W4, fp32 for W8A8.
  * ws: workspace of at least qmoe_grouped_ffn_workspace(d) bytes, 256-byte
  *   aligned.
- * Requirements: H % 256 == 0, I % 128 == 0 (I % 256 for A8W4), k <= E.
+ * Requirements: H % 256 == 0, I % 128 == 0 (I % 256 for A8W4), k <= E;
+ *   below 4 GiB each: x (T*H elements), the stage-2 activations (cap*I
+ *   elements, cap = qmoe_align_capacity) and one expert's W13 or W2 codes.
  * Errors: QMOE_ERR_INVALID_ARG for null pointers, bad sizes or a short
  * workspace; QMOE_ERR_UNSUPPORTED for sizes outside the requirements.    */
 size_t qmoe_grouped_ffn_workspace(const qmoe_ffn_desc* d);

@@ -227,6 +227,18 @@ static qmoe_status grouped_ffn_impl(const qmoe_ffn_desc* d, const void* x, const
     return QMOE_ERR_INVALID_ARG;
   const FfnWs lay = ffn_ws_layout(*d);
   if (ws_bytes < lay.total) return QMOE_ERR_INVALID_ARG;
+  // The GEMM kernels address activation rows and one expert's weights with
+  // 32-bit byte offsets: x [T, H], the stage-2 activations [cap, I] and each
+  // expert's W13 / W2 codes must stay below 4 GiB.
+  {
+    const uint64_t lim = 1ull << 32;
+    const uint64_t ab = quant_act ? 1 : 2;  // bytes per activation element
+    const uint64_t capu = qmoe_align_capacity(d->T, d->k, d->E, d->block_m);
+    const uint64_t wrow = d->scheme == QMOE_W8A8_PERCHAN ? 2 : 1;  // weight bytes per 2 elements
+    if ((uint64_t)d->T * d->H * ab >= lim || capu * d->I * ab >= lim ||
+        (uint64_t)2 * d->I * d->H * wrow / 2 >= lim || (uint64_t)d->H * d->I * wrow / 2 >= lim)
+      return QMOE_ERR_UNSUPPORTED;
+  }
   uint8_t* wsb = reinterpret_cast<uint8_t*>(ws);
   const bool dump = d->scheme == QMOE_W8A8_PERCHAN && (d->flags & QMOE_FLAG_DUMP_ACC);
   const int cap = (int)qmoe_align_capacity(d->T, d->k, d->E, d->block_m);

@@ -113,6 +113,10 @@ def test_ffn_workspace_and_desc_validation():
     assert call(_desc(), ws=n - 1) == ops.QMOE_ERR_INVALID_ARG
     assert call(_desc(), xs=None) == ops.QMOE_ERR_INVALID_ARG  # a8w4 needs x_scale
     assert call(_desc(T=0)) == ops.QMOE_OK
+    # 32-bit offsets inside the kernels: x (T*H), the stage-2 activations and
+    # one expert's weights must each stay below 4 GiB.
+    assert call(_desc(scheme="w4a16", T=1 << 19, H=4096, I=128)) == ops.QMOE_ERR_UNSUPPORTED
+    assert call(_desc(scheme="w8a8", T=64, H=65536, I=65536)) == ops.QMOE_ERR_UNSUPPORTED
     assert L.qmoe_grouped_ffn(None, p, p, ctypes.byref(w), p, p, p, p, p, 1 << 40, None) == \
         ops.QMOE_ERR_INVALID_ARG
 
