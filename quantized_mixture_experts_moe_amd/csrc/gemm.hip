@@ -599,16 +599,15 @@ hipError_t launch_xt(const GemmArgs& g, hipStream_t s) {
 template <int S, int STAGE, int BM, bool PK, int NSUB, int WAVES>
 hipError_t launch_one(const GemmArgs& g, hipStream_t s) {
   const int nsteps = g.K / Tr<S>::BK;
+  // The cross-tile pipeline: stage 1 of every scheme; stage 2 here runs
+  // only for w4a16 and for long intermediates of the one-byte schemes
+  // (otherwise the LDS-resident kernel takes it), where it stays off.
+  constexpr bool XT2 = STAGE == 1 || S == kW4A16;
   if constexpr (BM <= (S == kA8W4 ? 16 : 32)) {
-    if (nsteps % 8 == 0) {
-      if (STAGE == 1) return launch_xt<S, STAGE, BM, PK, NSUB, WAVES, STAGE == 1, 8>(g, s);
-      return launch_xt<S, STAGE, BM, PK, NSUB, WAVES, false, 8>(g, s);
-    }
+    if (nsteps % 8 == 0) return launch_xt<S, STAGE, BM, PK, NSUB, WAVES, XT2, 8>(g, s);
   }
-  if constexpr (STAGE == 1) {
-    if (nsteps >= 4 && nsteps % 4 == 0)
-      return launch_xt<S, STAGE, BM, PK, NSUB, WAVES, true, 4>(g, s);
-  }
+  if (nsteps >= 4 && nsteps % 4 == 0)
+    return launch_xt<S, STAGE, BM, PK, NSUB, WAVES, XT2, 4>(g, s);
   return launch_xt<S, STAGE, BM, PK, NSUB, WAVES, false, 4>(g, s);
 }
 
