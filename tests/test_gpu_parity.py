@@ -241,6 +241,32 @@ def test_a8w4_runs_of_row_tiles(T, prepacked):
     _parity_full(sh, 128, prepacked)
 
 
+def _random_cases(n=10, seed=2024):
+    """Seeded random shapes: scheme, T, E, k, H, I, block_m and layout drawn
+    so that the oracle finishes each in seconds; with E small against T*k
+    some draws give several row tiles per expert (the a8w4 runs of row
+    tiles at block_m 128)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        scheme = ["w4a16", "w8a8", "a8w4"][i % 3]
+        E = int(rng.integers(1, 40))
+        k = int(rng.integers(1, min(E, 6) + 1))
+        T = int(rng.integers(1, 1600))
+        H = int(rng.choice([256, 512]))
+        I = 256 if scheme == "a8w4" else int(rng.choice([128, 256]))
+        bm = int(rng.choice([16, 32, 64, 128]))
+        out.append((scheme, T, E, k, H, I, bm, bool(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("scheme,T,E,k,H,I,bm,prepacked", _random_cases())
+def test_random_shapes(scheme, T, E, k, H, I, bm, prepacked):
+    sh = MoEShape(f"rand_{scheme}_T{T}_E{E}_k{k}_H{H}_I{I}", scheme, tokens=T, hidden=H,
+                  inter=I, experts=E, topk=k, seed=7000 + T + E)
+    _parity_full(sh, bm, prepacked)
+
+
 @pytest.mark.parametrize("scheme", ["w4a16", "w8a8", "a8w4"])
 @pytest.mark.parametrize("T,E,k", [(1, 4, 1), (3, 1, 1), (40, 4, 4), (17, 6, 3)])
 def test_degenerate_routing(scheme, T, E, k):
