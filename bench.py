@@ -384,8 +384,8 @@ def main():
                          "(--steps times); used to scale the FETCH_SIZE/WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
-              "multi-GPU path.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has "
+              "no multi-GPU path (see the sharding plan in the design notes).", file=sys.stderr)
         sys.exit(2)
 
     import torch
