@@ -573,16 +573,17 @@ __global__ __launch_bounds__(WAVES * 64)
 
 template <int S, int STAGE, int BM, bool PK, int NSUB, int WAVES, bool XT, int RING>
 hipError_t launch_xt(const GemmArgs& g, hipStream_t s) {
-  static int blocks_per_cu = 0;
-  if (blocks_per_cu == 0) {
+  // Resident blocks per CU, queried once per kernel (a function-local
+  // static: its initialisation is thread-safe).
+  static const int blocks_per_cu = [] {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
             &n, moe_gemm_kernel<S, STAGE, BM, PK, NSUB, WAVES, XT, RING>, WAVES * 64, 0) !=
             hipSuccess ||
         n < 1)
       n = 1;
-    blocks_per_cu = n;
-  }
+    return n;
+  }();
   int nblk = device_cu_count() * blocks_per_cu;
   nblk = nblk < 8 ? 8 : (nblk / 8) * 8;
   hipLaunchKernelGGL((moe_gemm_kernel<S, STAGE, BM, PK, NSUB, WAVES, XT, RING>), dim3(nblk),
