@@ -90,30 +90,39 @@ struct BFrag {
 };
 
 // Eight int4 codes (two's complement, element i in bits 4i..4i+3) times the
-// group scale, each rounded once to bf16 (RNE).  The nibbles are spread
-// into bytes and offset by 8 (q + 8 = nibble ^ 8, in 0..15), so each one
-// converts to float in one instruction; q*s = fma(q + 8, s, -8s) is exact
-// (q*s needs at most 15 significant bits), so the only rounding is the
-// final one to bf16: the same values as converting q and multiplying.
+// group scale, each rounded once to bf16 (RNE).  With n = nibble ^ 8 = q + 8
+// in 0..15, OR-ing a nibble into the fp16 pattern of 1024 gives the exact
+// fp16 value 1024 + n (nibble in mantissa bits 0-3) or 1024 + 16n (bits
+// 4-7), two per 32-bit word; a mixed-precision FMA then computes
+//   (1024 + n) * s - 1032 s      = q * s,   or
+//   (1024 + 16n) * (s/16) - 72 s = q * s,
+// every product and constant exact in fp32 (at most 22 significant bits),
+// so the only rounding is the final one to bf16: the same values as
+// converting q and multiplying.  Per eight weights: one XOR, one shift, four
+// three-input bit operations, eight mixed FMAs and four bf16 packs.
 __device__ inline bf16x8 dequant8_bf16(uint32_t v, float sc) {
-  uint32_t even = (v & 0x0F0F0F0Fu) ^ 0x08080808u;         // elements 0, 2, 4, 6
-  uint32_t odd = ((v >> 4) & 0x0F0F0F0Fu) ^ 0x08080808u;   // elements 1, 3, 5, 7
-  // An empty asm hides the known-zero high nibbles from the compiler, which
-  // otherwise re-extracts each byte with a shift and a mask instead of
-  // converting it in place (v_cvt_f32_ubyte1..3).
-  asm("" : "+v"(even), "+v"(odd));
-  const float off = -8.0f * sc;
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
   typedef float f32x2 __attribute__((ext_vector_type(2)));
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const uint32_t x = v ^ 0x88888888u;  // every nibble n = q + 8
+  const uint32_t y = x >> 8;           // elements 2, 3, 6, 7 in the low nibbles
+  const float s16 = sc * 0.0625f;
+  const float c0 = -1032.0f * sc, c1 = -72.0f * sc;
+  // (a & mask) | 0x64006400: bit function 0xEA of (a, mask, pattern).
+  auto pair = [](uint32_t a, uint32_t mask) __attribute__((always_inline)) {
+    return __builtin_bit_cast(f16x2, __builtin_amdgcn_bitop3_b32(a, mask, 0x64006400u, 0xEA));
+  };
+  const f16x2 p04 = pair(x, 0x000F000Fu), p15 = pair(x, 0x00F000F0u);
+  const f16x2 p26 = pair(y, 0x000F000Fu), p37 = pair(y, 0x00F000F0u);
+  const float e0 = __builtin_fmaf((float)p04[0], sc, c0), e4 = __builtin_fmaf((float)p04[1], sc, c0);
+  const float e1 = __builtin_fmaf((float)p15[0], s16, c1), e5 = __builtin_fmaf((float)p15[1], s16, c1);
+  const float e2 = __builtin_fmaf((float)p26[0], sc, c0), e6 = __builtin_fmaf((float)p26[1], sc, c0);
+  const float e3 = __builtin_fmaf((float)p37[0], s16, c1), e7 = __builtin_fmaf((float)p37[1], s16, c1);
   u32x4 w;
-#pragma unroll
-  for (int j = 0; j < 4; j++) {
-    const float e = (float)((even >> (8 * j)) & 0xFFu);
-    const float o = (float)((odd >> (8 * j)) & 0xFFu);
-    const bf16x2 pr = __builtin_convertvector(
-        (f32x2){__builtin_fmaf(e, sc, off), __builtin_fmaf(o, sc, off)}, bf16x2);
-    w[j] = __builtin_bit_cast(uint32_t, pr);
-  }
+  w[0] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){e0, e1}, bf16x2));
+  w[1] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){e2, e3}, bf16x2));
+  w[2] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){e4, e5}, bf16x2));
+  w[3] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){e6, e7}, bf16x2));
   return __builtin_bit_cast(bf16x8, w);
 }
 
