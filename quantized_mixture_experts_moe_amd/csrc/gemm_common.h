@@ -91,29 +91,31 @@ struct BFrag {
 
 // Eight int4 codes (two's complement, element i in bits 4i..4i+3) times the
 // group scale, each rounded once to bf16 (RNE).  With n = nibble ^ 8 = q + 8
-// in 0..15, OR-ing a nibble into the fp16 pattern of 1024 gives the exact
+// in 0..15, placing n into the fp16 pattern of 1024 gives the exact
 // fp16 value 1024 + n (nibble in mantissa bits 0-3) or 1024 + 16n (bits
 // 4-7), two per 32-bit word; a mixed-precision FMA then computes
 //   (1024 + n) * s - 1032 s      = q * s,   or
 //   (1024 + 16n) * (s/16) - 72 s = q * s,
 // every product and constant exact in fp32 (at most 22 significant bits),
 // so the only rounding is the final one to bf16: the same values as
-// converting q and multiplying.  Per eight weights: one XOR, one shift, four
+// converting q and multiplying.  Per eight weights: one shift, four
 // three-input bit operations, eight mixed FMAs and four bf16 packs.
 __device__ inline bf16x8 dequant8_bf16(uint32_t v, float sc) {
   typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
   typedef float f32x2 __attribute__((ext_vector_type(2)));
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const uint32_t x = v ^ 0x88888888u;  // every nibble n = q + 8
-  const uint32_t y = x >> 8;           // elements 2, 3, 6, 7 in the low nibbles
+  const uint32_t y = v >> 8;  // elements 2, 3, 6, 7 in the low nibbles
   const float s16 = sc * 0.0625f;
   const float c0 = -1032.0f * sc, c1 = -72.0f * sc;
-  // (a & mask) | 0x64006400: bit function 0xEA of (a, mask, pattern).
-  auto pair = [](uint32_t a, uint32_t mask) __attribute__((always_inline)) {
-    return __builtin_bit_cast(f16x2, __builtin_amdgcn_bitop3_b32(a, mask, 0x64006400u, 0xEA));
+  // One bit operation per pair: bit function 0x6A of (a, m, p) is
+  // m ? a ^ p : p, so with m = the two nibbles and p = 0x6400 in each half
+  // plus each nibble's bit 3, it gives ((a ^ 0x8888...) & m) | 0x64006400:
+  // the nibbles with n = q + 8 (bit 3 flipped) inside the fp16 pattern.
+  auto pair = [](uint32_t a, uint32_t m, uint32_t p) __attribute__((always_inline)) {
+    return __builtin_bit_cast(f16x2, __builtin_amdgcn_bitop3_b32(a, m, p, 0x6A));
   };
-  const f16x2 p04 = pair(x, 0x000F000Fu), p15 = pair(x, 0x00F000F0u);
-  const f16x2 p26 = pair(y, 0x000F000Fu), p37 = pair(y, 0x00F000F0u);
+  const f16x2 p04 = pair(v, 0x000F000Fu, 0x64086408u), p15 = pair(v, 0x00F000F0u, 0x64806480u);
+  const f16x2 p26 = pair(y, 0x000F000Fu, 0x64086408u), p37 = pair(y, 0x00F000F0u, 0x64806480u);
   const float e0 = __builtin_fmaf((float)p04[0], sc, c0), e4 = __builtin_fmaf((float)p04[1], sc, c0);
   const float e1 = __builtin_fmaf((float)p15[0], s16, c1), e5 = __builtin_fmaf((float)p15[1], s16, c1);
   const float e2 = __builtin_fmaf((float)p26[0], sc, c0), e6 = __builtin_fmaf((float)p26[1], sc, c0);
