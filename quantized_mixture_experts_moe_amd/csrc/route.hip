@@ -7,55 +7,49 @@
 // softmax of the picked logits because the full denominator cancels.
 //
 // One wave per token.  Each lane keeps EPL logits in registers (expert
-// e = lane + 64*i) as 64-bit sortable keys: the high word orders the fp32
-// values, the low word is ~e, so the largest key is the largest logit with
-// the lowest index among equal ones.  k rounds of a wave-wide maximum pick
-// the experts in slot order; the maximum runs on DPP row operations inside
-// each 16-lane row and four lane reads across the rows (no LDS traffic).
-// The weights use fp64 exp so that they match a correctly rounded fp32
-// result.
+// e = lane + 64*i) as 32-bit order-preserving keys (0 marks a taken or
+// missing expert; no finite logit maps to 0).  Each of the k rounds takes
+// the wave-wide maximum key, then the lowest expert index holding it (a
+// wave-wide minimum): the largest logit, ties to the lower index.  Both
+// reductions run on DPP row operations inside each 16-lane row and four
+// lane reads across the rows (no LDS traffic).  The weights use fp64 exp
+// so that they match a correctly rounded fp32 result.
 #include "qmoe_internal.h"
 
 namespace qmoe {
 namespace {
 
-typedef unsigned long long u64;
-
-__device__ inline u64 make_key(float v, int e) {
+__device__ inline uint32_t order_key(float v) {
   const uint32_t b = __float_as_uint(v);
-  const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-  return ((u64)ord << 32) | (uint32_t)~(uint32_t)e;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-__device__ inline float key_value(u64 k) {
-  const uint32_t ord = (uint32_t)(k >> 32);
+__device__ inline float key_value(uint32_t ord) {
   const uint32_t b = (ord & 0x80000000u) ? (ord & 0x7fffffffu) : ~ord;
   return __uint_as_float(b);
 }
 
-template <int CTRL>
-__device__ inline u64 dpp_max(u64 x) {
-  const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)x, CTRL, 0xf, 0xf, false);
-  const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(x >> 32), CTRL, 0xf, 0xf, false);
-  const u64 y = ((u64)(uint32_t)hi << 32) | (uint32_t)lo;
-  return y > x ? y : x;
+// x combined with the lane that DPP control CTRL names, by MAX or min.
+template <int CTRL, bool MAX>
+__device__ inline uint32_t dpp_op(uint32_t x) {
+  const uint32_t y = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xf, 0xf, false);
+  return MAX ? (y > x ? y : x) : (y < x ? y : x);
 }
 
-// Maximum of x over the 64 lanes, returned in every lane.
-__device__ inline u64 wave_max(u64 x) {
-  x = dpp_max<0xB1>(x);   // quad_perm [1,0,3,2]
-  x = dpp_max<0x4E>(x);   // quad_perm [2,3,0,1]
-  x = dpp_max<0x141>(x);  // row_half_mirror: the two quads of each half-row
-  x = dpp_max<0x140>(x);  // row_mirror: the two halves of each row
-  u64 best = 0;
+// Maximum (MAX) or minimum of x over the 64 lanes, in every lane.
+template <bool MAX>
+__device__ inline uint32_t wave_reduce(uint32_t x) {
+  x = dpp_op<0xB1, MAX>(x);   // quad_perm [1,0,3,2]
+  x = dpp_op<0x4E, MAX>(x);   // quad_perm [2,3,0,1]
+  x = dpp_op<0x141, MAX>(x);  // row_half_mirror: the two quads of each half-row
+  x = dpp_op<0x140, MAX>(x);  // row_mirror: the two halves of each row
+  uint32_t r = (uint32_t)__builtin_amdgcn_readlane((int)x, 0);
 #pragma unroll
-  for (int r = 0; r < 4; r++) {
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, 16 * r);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), 16 * r);
-    const u64 y = ((u64)hi << 32) | lo;
-    best = y > best ? y : best;
+  for (int row = 1; row < 4; row++) {
+    const uint32_t y = (uint32_t)__builtin_amdgcn_readlane((int)x, 16 * row);
+    r = MAX ? (y > r ? y : r) : (y < r ? y : r);
   }
-  return best;
+  return r;
 }
 
 template <int EPL>
@@ -66,25 +60,31 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;  // whole wave leaves together
   const float* row = logits + (size_t)t * E;
-  u64 key[EPL];
+  uint32_t key[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; i++) {
     const int e = lane + 64 * i;
-    key[i] = e < E ? make_key(row[e], e) : 0ull;  // 0 sorts below every real key
+    key[i] = e < E ? order_key(row[e]) : 0u;
   }
   float top0 = 0.f, my_v = 0.f;
   int my_e = 0;
   for (int j = 0; j < k; j++) {
-    u64 mine = key[0];
+    uint32_t mine = key[0];
 #pragma unroll
     for (int i = 1; i < EPL; i++) mine = key[i] > mine ? key[i] : mine;
-    const u64 best = wave_max(mine);
-    const int bi = (int)~(uint32_t)best;
+    const uint32_t best = wave_reduce<true>(mine);
+    // This lane's lowest expert holding the maximum (0xffffffff if none),
+    // then the lowest over the wave.
+    uint32_t cand = 0xffffffffu;
+#pragma unroll
+    for (int i = EPL - 1; i >= 0; i--)
+      if (key[i] == best) cand = (uint32_t)(lane + 64 * i);
+    const int bi = (int)wave_reduce<false>(cand);
     const float bv = key_value(best);
     if ((bi & 63) == lane) {
 #pragma unroll
       for (int i = 0; i < EPL; i++)
-        if (i == (bi >> 6)) key[i] = 0ull;  // taken
+        if (i == (bi >> 6)) key[i] = 0u;  // taken
     }
     if (j == 0) top0 = bv;
     if (lane == j) {
