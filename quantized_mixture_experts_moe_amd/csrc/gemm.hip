@@ -228,7 +228,7 @@ __global__ __launch_bounds__(WAVES * 64)
 
   u32x4 ar[NCH];
   // The weight ring: RING register sets, loads RING-1 steps ahead.
-  static_assert(RING == 4 || RING == 8, "ring of 4 or 8 steps");
+  static_assert(RING == 4 || RING == 6 || RING == 8, "ring of 4, 6 or 8 steps");
   BFrag<S> bq[RING][NSUB];
 
   // Set-up of tile w, in four parts.  setup_rows: row ids into sRow[bf],
@@ -609,6 +609,10 @@ hipError_t launch_one(const GemmArgs& g, hipStream_t s) {
   }
   if (nsteps >= 4 && nsteps % 4 == 0)
     return launch_xt<S, STAGE, BM, PK, NSUB, WAVES, XT2, 4>(g, s);
+  // w4a16 stage 2 with K = 768 (six steps): the whole K loop is one ring.
+  if constexpr (STAGE == 2 && S == kW4A16 && BM <= 64) {
+    if (nsteps == 6) return launch_xt<S, STAGE, BM, PK, NSUB, WAVES, true, 6>(g, s);
+  }
   return launch_xt<S, STAGE, BM, PK, NSUB, WAVES, false, 4>(g, s);
 }
 

@@ -230,6 +230,15 @@ def test_small_shapes_other_schemes(scheme, prepacked):
         _parity_full(sh, bm, prepacked)
 
 
+@pytest.mark.parametrize("bm", [16, 32, 64])
+def test_w4a16_six_step_stage2(bm):
+    """W4A16 with I = 768: the stage-2 K loop has six steps and runs as one
+    ring of six with the cross-tile pipeline (tiles of up to 64 rows)."""
+    sh = MoEShape(f"w4a16_I768_bm{bm}", "w4a16", tokens=300, hidden=256, inter=768,
+                  experts=12, topk=3, seed=640 + bm)
+    _parity_full(sh, bm, True)
+
+
 @LAYOUTS
 @pytest.mark.parametrize("T", [1000, 1500])
 def test_a8w4_runs_of_row_tiles(T, prepacked):
