@@ -25,6 +25,9 @@
 namespace qmoe {
 namespace {
 
+typedef float s2_f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 s2_bf16x2 __attribute__((ext_vector_type(2)));
+
 using namespace gk;
 
 constexpr int kS2Waves = 8;
@@ -233,12 +236,13 @@ moe_stage2_resident(GemmArgs g, int passes, int tile_div) {
           for (int s = 0; s < kS2Nsub; s++) {
             const int col = colw + s * 16;
             if constexpr (S == kA8W4) {
-              const __bf16 v0 = (__bf16)(acc[m][s][0] * rs), v1 = (__bf16)(acc[m][s][1] * rs);
-              const __bf16 v2 = (__bf16)(acc[m][s][2] * rs), v3 = (__bf16)(acc[m][s][3] * rs);
-              const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, v0) |
-                                  ((uint32_t)__builtin_bit_cast(uint16_t, v1) << 16);
-              const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, v2) |
-                                  ((uint32_t)__builtin_bit_cast(uint16_t, v3) << 16);
+              // Two values per conversion, each rounded to nearest even.
+              const uint32_t lo = __builtin_bit_cast(
+                  uint32_t, __builtin_convertvector(
+                                (s2_f32x2){acc[m][s][0] * rs, acc[m][s][1] * rs}, s2_bf16x2));
+              const uint32_t hi = __builtin_bit_cast(
+                  uint32_t, __builtin_convertvector(
+                                (s2_f32x2){acc[m][s][2] * rs, acc[m][s][3] * rs}, s2_bf16x2));
               if (pair >= 0)
                 *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(g.out) +
                                           (size_t)pair * g.H + col) = make_uint2(lo, hi);
