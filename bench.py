@@ -361,6 +361,74 @@ def run_workload(name: str, args, torch, with_cpu: bool) -> dict:
     return res
 
 
+TILE_SWEEP_SHARES = ("a8w4_large", "a8w4_tp2", "a8w4_tp4")
+TILE_SWEEP_TOKENS = (1, 16, 64, 256, 1024, 4096, 8192)
+TILE_SWEEP_BLOCKS = (16, 32, 64, 128)
+
+
+def tile_sweep(args, torch) -> None:
+    """Step time of every block_m for the large a8w4 block and its tensor-
+    parallel shares (inter 1024, 512, 256) at each token bucket.  Inputs are
+    drawn once per share at 8192 tokens; a bucket takes the leading tokens.
+    Accuracy gate: a block_m counts only if its output equals the block_m 16
+    output bit for bit (the row tiles change neither the order nor the
+    precision of any sum).  One JSON line per (share, tokens, block_m), then
+    one per (share, tokens) naming the fastest gated block_m."""
+    from quantized_mixture_experts_moe_amd import ops, synth
+    from quantized_mixture_experts_moe_amd.shapes import shape_by_name
+
+    dev = torch.device("cuda:0")
+    flush = torch.ones(64 << 20, dtype=torch.int64, device=dev)
+    for base in TILE_SWEEP_SHARES:
+        full = shape_by_name(f"{base}@T{max(TILE_SWEEP_TOKENS)}")
+        inp = synth.make_inputs(full)
+        g = {}
+        for key, a in inp.items():
+            if a is not None:
+                g[key] = torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+        W = ops.prepack_weights(full.scheme, {kk: g.pop(kk) for kk in
+                                              ("w13", "w13_scale", "w2", "w2_scale")})
+        del inp
+        E, k = full.experts, full.topk
+        for T in TILE_SWEEP_TOKENS:
+            sh = full.with_tokens(T)
+            gt = {"logits": g["logits"][:T], "x": g["x"][:T], "x_scale": g["x_scale"][:T]}
+            ref, times = None, {}
+            for bm in TILE_SWEEP_BLOCKS:
+                ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+                tw = torch.empty((T, k), dtype=torch.float32, device=dev)
+                ops.route(gt["logits"], k, ids, tw)
+                al = ops.align(ids, E, bm)
+                y, ws = ops.grouped_ffn(sh.scheme, gt["x"], gt["x_scale"], W, al, E, k)
+                out_bf16, _ = ops.combine(y, tw, want_bf16=True, want_f32=False)
+
+                def eager_step():
+                    ops.route(gt["logits"], k, ids, tw)
+                    ops.align(ids, E, bm, out=al)
+                    ops.grouped_ffn(sh.scheme, gt["x"], gt["x_scale"], W, al, E, k, ws=ws,
+                                    y_pairs=y)
+                    ops.combine(y, tw, out_bf16=out_bf16, out_f32=None, want_f32=False)
+
+                torch.cuda.synchronize()
+                if ref is None:
+                    ref = out_bf16.clone()
+                gate = bool(torch.equal(out_bf16, ref))
+                ms, med = graph_step_ms(torch, ops, args, flush, dict(
+                    shape=sh, g=gt, W=W, ids=ids, tw=tw, al=al, y=y, ws=ws, bm=bm,
+                    out_bf16=out_bf16, out_f32=None), eager_step)
+                if gate:
+                    times[bm] = ms
+                print(json.dumps({"tile_sweep": base, "inter": sh.inter, "tokens": T,
+                                  "block_m": bm, "ms_per_step": round(ms, 4),
+                                  "ms_median": round(med, 4), "gate_bitexact": gate}), flush=True)
+                del y, ws, al
+            best = min(times, key=times.get)
+            print(json.dumps({"tile_best": base, "inter": sh.inter, "tokens": T, "block_m": best,
+                              "ms_per_step": round(times[best], 4)}), flush=True)
+        del g, W
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -369,6 +437,9 @@ def main():
     ap.add_argument("--workload", default="a8w4_large@T4096")
     ap.add_argument("--sweep", action="store_true",
                     help="run every workload of the sweep, one JSON line each (no CPU baseline)")
+    ap.add_argument("--tile-sweep", action="store_true",
+                    help="time every block_m for the a8w4 block and its tensor-parallel shares "
+                         "at each token bucket")
     ap.add_argument("--block-m", type=int, default=0)
     ap.add_argument("--eager", action="store_true",
                     help="time the eager launches only (no HIP graph of the step)")
@@ -404,6 +475,9 @@ def main():
         return
 
     torch.cuda.set_device(torch.device("cuda:0"))
+    if args.tile_sweep:
+        tile_sweep(args, torch)
+        return
     if args.sweep:
         for name in SWEEP:
             print(json.dumps(run_workload(name, args, torch, False)), flush=True)

@@ -75,12 +75,20 @@ W8A8_T2048 = MoEShape("w8a8_t2048", "w8a8", tokens=2048, hidden=2048, inter=768,
 A8W4_LARGE = MoEShape("a8w4_large@T4096", "a8w4", tokens=4096, hidden=4096, inter=1024,
                       experts=512, topk=10, seed=1003, tokens_drawn=8192)
 A8W4_SWEEP_TOKENS = (256, 1024, 4096, 8192)
+# The same block split over two or four GPUs by tensor parallelism: each
+# GPU holds every expert with a share of the intermediate (inter 512, 256;
+# aiter PR 6090, section Changes).  Stage 1 is then column-parallel and
+# stage 2 row-parallel; one GPU's share is exactly this shape.
+A8W4_TP2 = MoEShape("a8w4_tp2@T4096", "a8w4", tokens=4096, hidden=4096, inter=512,
+                    experts=512, topk=10, seed=1005, tokens_drawn=8192)
+A8W4_TP4 = MoEShape("a8w4_tp4@T4096", "a8w4", tokens=4096, hidden=4096, inter=256,
+                    experts=512, topk=10, seed=1006, tokens_drawn=8192)
 # Long prefill with a Zipf-skewed router: a few experts get most rows.
 W4A16_SKEWED = MoEShape("w4a16_skewed_t8192", "w4a16", tokens=8192, hidden=4096,
                         inter=1024, experts=512, topk=10, seed=1004, zipf_s=1.2)
 
 ALL_SHAPES = {s.name: s for s in (W4A16_TINY, W4A16_QWEN3MOE, W8A8_T2048, A8W4_LARGE,
-                                  W4A16_SKEWED)}
+                                  A8W4_TP2, A8W4_TP4, W4A16_SKEWED)}
 
 
 def shape_by_name(name: str) -> MoEShape:
@@ -103,10 +111,15 @@ def default_block_m(shape: MoEShape) -> int:
     Up to 40: 64 (one or two tiles per expert; 32 measured slower).  Up to
     96: 128 (one tile per expert, weights read once).  Above 96 with an even
     routing, 64: a second 128-row tile would be mostly padding; except for
-    a8w4 above 128 rows, where 128-row tiles taken in runs of consecutive
-    row tiles (an expert's second tile reads its weights from the
-    memory-side cache) measured faster.  Skewed routing keeps 128 for its
-    heavy experts.
+    a8w4 above 128 rows with the full intermediate (1024), where 128-row
+    tiles taken in runs of consecutive row tiles (an expert's second tile
+    reads its weights from the memory-side cache) measured faster; with a
+    tensor-parallel share of it (512, 256) 64 is faster there (5% and 9% at
+    8192 tokens).  Skewed routing keeps 128 for its heavy experts.
+
+    ``bench.py --tile-sweep`` times every block_m for the large a8w4 block
+    and its shares at each token bucket (1 to 8192 tokens); this rule is
+    within 2% of the fastest gated choice at every point of that table.
     """
     mean_rows = shape.pairs / shape.experts
     if mean_rows <= 12:
@@ -115,6 +128,6 @@ def default_block_m(shape: MoEShape) -> int:
         return 64
     if mean_rows <= 96 or shape.zipf_s:
         return 128
-    if shape.scheme == "a8w4" and mean_rows > 128:
+    if shape.scheme == "a8w4" and mean_rows > 128 and shape.inter >= 1024:
         return 128
     return 64

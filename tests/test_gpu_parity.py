@@ -8,9 +8,9 @@ import torch
 
 import oracle as O
 from quantized_mixture_experts_moe_amd import ops, synth
-from quantized_mixture_experts_moe_amd.shapes import (A8W4_LARGE, W4A16_QWEN3MOE, W4A16_SKEWED,
-                                                      W4A16_TINY, W8A8_T2048, MoEShape,
-                                                      default_block_m)
+from quantized_mixture_experts_moe_amd.shapes import (A8W4_LARGE, A8W4_TP2, A8W4_TP4,
+                                                      W4A16_QWEN3MOE, W4A16_SKEWED, W4A16_TINY,
+                                                      W8A8_T2048, MoEShape, default_block_m)
 
 from _helpers import WEIGHT_KEYS, bf16_to_np, gpu_inputs, oracle_tokens, to_gpu
 
@@ -221,6 +221,14 @@ def test_a8w4_t256_full(bm, prepacked):
     _parity_full(A8W4_LARGE.with_tokens(256), bm, prepacked)
 
 
+@pytest.mark.parametrize("share", [A8W4_TP2, A8W4_TP4], ids=["tp2", "tp4"])
+@pytest.mark.parametrize("T,bm", [(16, 16), (128, 64)])
+def test_a8w4_tensor_parallel_shares_full(share, T, bm):
+    """One GPU's share of the large a8w4 block under two- and four-way tensor
+    parallelism (inter 512, 256) against the oracle on every token."""
+    _parity_full(share.with_tokens(T), bm, True)
+
+
 @LAYOUTS
 @pytest.mark.parametrize("scheme", ["w8a8", "a8w4"])
 def test_small_shapes_other_schemes(scheme, prepacked):
@@ -337,6 +345,14 @@ def test_a8w4_t4096_sampled(prepacked):
 
 def test_a8w4_t8192_sampled():
     _parity_sampled(A8W4_LARGE.with_tokens(8192), prepacked=True)
+
+
+@pytest.mark.parametrize("share", [A8W4_TP2, A8W4_TP4], ids=["tp2", "tp4"])
+@pytest.mark.parametrize("T", [4096, 8192])
+def test_a8w4_tensor_parallel_shares_sampled(share, T):
+    """The shares at the two largest token buckets, in the layout and tile
+    height the default path takes."""
+    _parity_sampled(share.with_tokens(T), prepacked=True)
 
 
 @LAYOUTS
