@@ -245,20 +245,30 @@ __global__ __launch_bounds__(kSmallT) void align_small_kernel(
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int P = T * k;
   const int bm = 1 << bm_shift;
+  const bool mine = tid < T;
+  // This thread's token ids (up to kRegK of them kept in registers), all
+  // loads issued before the mask is cleared so that their round trips
+  // overlap each other and the clearing.
+  constexpr int kRegK = 16;
+  int te[kRegK];
+#pragma unroll
+  for (int j = 0; j < kRegK; j++) te[j] = mine && j < k ? ids[(size_t)tid * k + j] : -1;
   for (int i = tid; i < kSmallWaves * E; i += kSmallT) mask[i] = 0ull;
   __syncthreads();
   int bad = 0;
-  if (tid < T) {
-    for (int j = 0; j < k; j++) {
-      const int e = ids[(size_t)tid * k + j];
-      if (e >= 0 && e < E) {
-        const unsigned long long old = atomicOr(&mask[wave * E + e], 1ull << lane);
-        if (old & (1ull << lane)) bad |= 2;
-      } else {
-        bad |= 1;
-      }
+  auto set_bit = [&](int e) __attribute__((always_inline)) {
+    if (e >= 0 && e < E) {
+      const unsigned long long old = atomicOr(&mask[wave * E + e], 1ull << lane);
+      if (old & (1ull << lane)) bad |= 2;
+    } else {
+      bad |= 1;
     }
-  }
+  };
+#pragma unroll
+  for (int j = 0; j < kRegK; j++)
+    if (mine && j < k) set_bit(te[j]);
+  for (int j = kRegK; j < k; j++)
+    if (mine) set_bit(ids[(size_t)tid * k + j]);
   const int b1 = __syncthreads_or(bad & 1);
   const int b2 = __syncthreads_or(bad & 2);
   // Totals, one expert per thread (E <= 1024), and their padded prefix.
@@ -282,21 +292,31 @@ __global__ __launch_bounds__(kSmallT) void align_small_kernel(
   }
   __syncthreads();
   // Scatter: rank inside the expert = pairs of earlier tokens.
-  if (tid < T) {
-    const unsigned long long below = (1ull << lane) - 1ull;
-    for (int j = 0; j < k; j++) {
-      const int e = ids[(size_t)tid * k + j];
-      if (e < 0 || e >= E) continue;
-      int rank = __popcll(mask[wave * E + e] & below);
-      for (int w = 0; w < wave; w++) rank += __popcll(mask[w * E + e]);
-      sorted[s_off[e] + rank] = tid * k + j;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  auto place = [&](int e, int j) __attribute__((always_inline)) {
+    if (e < 0 || e >= E) return;
+    int rank = __popcll(mask[wave * E + e] & below);
+    for (int w = 0; w < wave; w++) rank += __popcll(mask[w * E + e]);
+    sorted[s_off[e] + rank] = tid * k + j;
+  };
+#pragma unroll
+  for (int j = 0; j < kRegK; j++)
+    if (mine && j < k) place(te[j], j);
+  for (int j = kRegK; j < k; j++)
+    if (mine) place(ids[(size_t)tid * k + j], j);
+  // Sentinels and tile->expert entries: a group of block_m / 4 lanes (4 to
+  // 32) per expert, so that an expert's at most block_m - 1 sentinels take
+  // at most four stores per lane and a wave serves 64 / group experts at a
+  // time.
+  {
+    const int gs_shift = bm_shift - 2;  // block_m is 16..128
+    const int gs = 1 << gs_shift, per_wave = 64 >> gs_shift;
+    const int sub = lane >> gs_shift, sl = lane & (gs - 1);
+    for (int e = wave * per_wave + sub; e < E; e += kSmallWaves * per_wave) {
+      const int o = s_off[e], t = s_tot[e], end = s_off[e + 1];
+      for (int i = (o >> bm_shift) + sl; i < (end >> bm_shift); i += gs) tile_expert[i] = e;
+      for (int i = o + t + sl; i < end; i += gs) sorted[i] = P;
     }
-  }
-  // Sentinels and tile->expert entries, one wave per expert.
-  for (int e = wave; e < E; e += kSmallWaves) {
-    const int o = s_off[e], t = s_tot[e], end = s_off[e + 1];
-    for (int i = (o >> bm_shift) + lane; i < (end >> bm_shift); i += 64) tile_expert[i] = e;
-    for (int i = o + t + lane; i < end; i += 64) sorted[i] = P;
   }
   const int npad = s_off[E];
   for (int i = npad + tid; i < cap; i += kSmallT) sorted[i] = P;
@@ -418,6 +438,7 @@ hipError_t launch_align(const int32_t* ids, int T, int k, int E, int block_m, in
                         int32_t* chunk_counts, int32_t* chunk_flags, int32_t* totals,
                         int32_t* flags, int cap, hipStream_t s) {
   if (E > kMaxExperts) return hipErrorInvalidValue;
+  if (block_m < 16 || block_m > 128 || (block_m & (block_m - 1)) != 0) return hipErrorInvalidValue;
   const int nchunks = (T + kChunk - 1) / kChunk;
   const size_t lds = (size_t)4 * E * sizeof(unsigned long long);
   hipError_t err;
