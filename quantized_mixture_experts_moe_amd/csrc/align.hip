@@ -16,7 +16,7 @@
 //     the chunk base + the earlier waves' counts + popcount(mask & lanes
 //     below).  The same launch writes the padding sentinels, the
 //     tile->expert map and the tail, spread over at least 32 blocks.
-// Up to 1024 tokens all three steps run in one block of one launch
+// Up to 512 tokens all three steps run in one block of one launch
 // (align_small_kernel): short prefills pay one launch, not three.  Up to
 // 64 chunks (16384 tokens) the scan runs inside the scatter launch
 // (align_place_kernel): every block reads the whole count matrix and scans
@@ -209,8 +209,8 @@ __global__ __launch_bounds__(kChunk) void align_scatter_kernel(
     tile_expert[i] = -1;
 }
 
-// The whole of moe_align for T <= kSmallT in one block of 16 waves (64
-// tokens each): masks, expert totals (one expert per thread), the padded
+// The whole of moe_align for up to kSmallT tokens in one block of 16 waves
+// (64 tokens each; the launcher sends it at most 512): masks, expert totals (one expert per thread), the padded
 // offsets (block scan), the scatter, the padding sentinels, the
 // tile->expert map and the tail.  block_m is a power of two.
 constexpr int kSmallT = 1024;
@@ -417,11 +417,18 @@ __global__ __launch_bounds__(kChunk) void align_place_kernel(
     if (mine && j < k) place(te[j], j);
   for (int j = kRegK; j < k; j++)
     if (mine) place(ids[(size_t)t * k + j], j);
-  const int nwaves = gridDim.x * (kChunk / 64);
-  for (int e = blockIdx.x * (kChunk / 64) + wave; e < E; e += nwaves) {
-    const int o = s_off[e], n = s_tot[e], end = s_off[e + 1];
-    for (int i = (o >> bm_shift) + lane; i < (end >> bm_shift); i += 64) tile_expert[i] = e;
-    for (int i = o + n + lane; i < end; i += 64) sorted[i] = P;
+  // Sentinels and tile entries: a group of block_m / 4 lanes per expert
+  // (as in align_small_kernel).
+  {
+    const int gs_shift = bm_shift - 2;  // block_m is 16..128
+    const int gs = 1 << gs_shift, per_wave = 64 >> gs_shift;
+    const int sub = lane >> gs_shift, sl = lane & (gs - 1);
+    const int ngroups = gridDim.x * (kChunk / 64) * per_wave;
+    for (int e = (blockIdx.x * (kChunk / 64) + wave) * per_wave + sub; e < E; e += ngroups) {
+      const int o = s_off[e], n = s_tot[e], end = s_off[e + 1];
+      for (int i = (o >> bm_shift) + sl; i < (end >> bm_shift); i += gs) tile_expert[i] = e;
+      for (int i = o + n + sl; i < end; i += gs) sorted[i] = P;
+    }
   }
   const int npad = s_off[E];
   const int stride = gridDim.x * kChunk;
@@ -442,7 +449,11 @@ hipError_t launch_align(const int32_t* ids, int T, int k, int E, int block_m, in
   const int nchunks = (T + kChunk - 1) / kChunk;
   const size_t lds = (size_t)4 * E * sizeof(unsigned long long);
   hipError_t err;
-  if (T <= kSmallT) {
+  // One block up to 512 tokens; beyond that the two-launch path measured
+  // faster although the block could take 1024 (1024 tokens: 17.5 -> 14.0 us).
+  constexpr int kSmallPathT = 512;
+  static_assert(kSmallPathT <= kSmallT, "one thread per token");
+  if (T <= kSmallPathT) {
     const int bm_shift = __builtin_ctz((unsigned)block_m);
     const size_t lds_small = (size_t)kSmallWaves * E * sizeof(unsigned long long);
     hipLaunchKernelGGL(align_small_kernel, dim3(1), dim3(kSmallT), lds_small, s, ids, T, k, E,

@@ -63,6 +63,7 @@ def _check_align(al, ids_np, E, bm):
                                       (2048, 8, 128, 128),
                                       (4096, 10, 512, 128), (1, 1, 1, 16), (257, 3, 7, 32),
                                       (1000, 4, 1024, 64), (8192, 10, 512, 16),
+                                      (512, 10, 512, 128), (513, 10, 512, 16),
                                       (1025, 3, 7, 32), (2100, 16, 200, 64),
                                       (1500, 20, 64, 32), (17000, 2, 64, 64)])
 def test_align_matches_oracle(T, k, E, bm):
