@@ -64,12 +64,14 @@ def _check_align(al, ids_np, E, bm):
                                       (4096, 10, 512, 128), (1, 1, 1, 16), (257, 3, 7, 32),
                                       (1000, 4, 1024, 64), (8192, 10, 512, 16),
                                       (512, 10, 512, 128), (513, 10, 512, 16),
+                                      (300, 24, 64, 32),
                                       (1025, 3, 7, 32), (2100, 16, 200, 64),
                                       (1500, 20, 64, 32), (17000, 2, 64, 64)])
 def test_align_matches_oracle(T, k, E, bm):
-    """One launch up to 1024 tokens, one launch of one block per 1024-token
-    chunk up to 16384 tokens with k <= 16, three launches beyond (the last
-    two cases)."""
+    """One launch of one block up to 512 tokens; two launches (count, then
+    place, 256-token chunks) up to 16384 tokens; three launches beyond (the
+    last case).  k above 16 (the ids past the 16 a thread keeps in
+    registers) on both of the first two paths."""
     _flush(f"align T={T} k={k} E={E} bm={bm}")
     rng = np.random.default_rng(T + E + bm)
     L = rng.standard_normal((T, E)).astype(np.float32)
@@ -104,8 +106,8 @@ def test_align_empty_and_out_of_range():
     dup = np.array([[3, 3], [1, 2]], np.int32)
     al = ops.align(to_gpu(dup), 8, 16)
     assert ops.check_flags(al["ws"]) & 2
-    # The same cases past 1024 tokens (the chunked single-launch path): every
-    # block sees the bad ids of every chunk.
+    # The same cases past 512 tokens (the two-launch path): every block sees
+    # the bad ids of every chunk.
     rng = np.random.default_rng(5)
     ids_np, _ = O.route(rng.standard_normal((3000, 64)).astype(np.float32), 4)
     ids_np[2500, 1] = -3
