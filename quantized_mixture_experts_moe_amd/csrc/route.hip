@@ -8,7 +8,8 @@
 //
 // One wave per token.  Each lane keeps EPL logits in registers (expert
 // e = lane + 64*i) as 32-bit order-preserving keys (0 marks a taken or
-// missing expert; no finite logit maps to 0).  Each of the k rounds takes
+// missing expert; no finite logit maps to 0; -0 is keyed as +0, so that
+// the two zeros tie as equal logits do).  Each of the k rounds takes
 // the wave-wide maximum key, then the lowest expert index holding it (a
 // wave-wide minimum): the largest logit, ties to the lower index.  Both
 // reductions run on DPP row operations inside each 16-lane row and four
@@ -20,7 +21,7 @@ namespace qmoe {
 namespace {
 
 __device__ inline uint32_t order_key(float v) {
-  const uint32_t b = __float_as_uint(v);
+  const uint32_t b = __float_as_uint(v + 0.0f);  // -0 + +0 = +0 (round to nearest)
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 

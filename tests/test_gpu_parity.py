@@ -35,6 +35,10 @@ def test_route_matches_oracle(T, E, k):
         L[:, 5] = L[:, 3]  # ties everywhere
     if T > 2:
         L[1] = 0.5  # a fully tied row
+    if T > 3:
+        L[2, ::2] = -0.0  # signed zeros tie with each other
+        L[2, 1::2] = 0.0
+        L[3, : E // 2] = -0.0
     ids, w = ops.route(to_gpu(L), k)
     torch.cuda.synchronize()
     ids_o, w_o = O.route(L, k)

@@ -153,6 +153,14 @@ def test_route_ties_pick_lower_index():
     np.testing.assert_array_equal(w, np.full((2, 3), np.float32(1 / 3)))
 
 
+def test_route_signed_zeros_tie():
+    """-0 and +0 are equal logits, so they tie and the lower index wins."""
+    L = np.array([[-0.0, 0.0, -0.0, 0.0, -1.0]], np.float32)
+    ids, w = O.route(L, 3)
+    np.testing.assert_array_equal(ids, [[0, 1, 2]])
+    np.testing.assert_array_equal(w, np.full((1, 3), np.float32(1 / 3)))
+
+
 # ---------------------------------------------------------------- align
 
 def _align_brute(ids, E, bm):
