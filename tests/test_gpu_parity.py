@@ -168,9 +168,10 @@ def _unsort(dump_rows, sorted_ids, P):
     return out
 
 
-def _parity_full(shape, bm=None, prepacked=False):
+def _parity_full(shape, bm=None, prepacked=False, inp=None):
     _flush(f"ffn full {shape.name} bm={bm or default_block_m(shape)} prepacked={prepacked}")
-    inp = synth.make_inputs(shape)
+    if inp is None:
+        inp = synth.make_inputs(shape)
     flags = ops.QMOE_FLAG_DUMP_ACC if shape.scheme == "w8a8" else 0
     r = _run_gpu(shape, inp, bm, flags, prepacked)
     ids_o, w_o = O.route(inp["logits"], shape.topk)
@@ -300,6 +301,42 @@ def test_degenerate_routing(scheme, T, E, k):
     sh = MoEShape(f"edge_{scheme}_T{T}_E{E}_k{k}", scheme, tokens=T, hidden=256, inter=I,
                   experts=E, topk=k, seed=90 + T + E + k)
     _parity_full(sh, 16)
+
+
+@pytest.mark.parametrize("scheme", ["w4a16", "w8a8", "a8w4"])
+def test_zero_and_tiny_activation_rows(scheme):
+    """Tokens whose activations are all zero: their gate/up sums and h rows
+    are exactly zero, so the requantization takes the all-zero-row scale
+    (1, codes 0) and every output of those tokens is exactly zero.  Tokens
+    with a per-token scale of 1e-18 (W8A8, a8w4): h near 1e-35, a row scale
+    below 2^-60, where the requantization divides instead of multiplying by
+    a reciprocal; their outputs are checked on their own against the
+    oracle, since next to the other tokens they weigh nothing."""
+    sh = MoEShape(f"zero_rows_{scheme}", scheme, tokens=90, hidden=256, inter=256, experts=8,
+                  topk=3, seed=83)
+    _flush(f"zero and tiny rows {scheme}")
+    inp = synth.make_inputs(sh)
+    zero = np.arange(0, sh.tokens, 7)
+    tiny = np.arange(3, sh.tokens, 7)
+    inp["x"][zero] = 0
+    if inp["x_scale"] is not None:
+        inp["x_scale"][tiny] *= np.float32(1e-18)
+    ids_o, w_o = O.route(inp["logits"], sh.topk)
+    W = {k: inp[k] for k in WEIGHT_KEYS}
+    for bm, prepacked in ((16, True), (64, False)):
+        r = _run_gpu(sh, inp, bm, 0, prepacked)
+        np.testing.assert_array_equal(r["topk_ids"].cpu().numpy(), ids_o)
+        ref = O.moe_forward(sh.scheme, inp["x"], inp["x_scale"], W, ids_o,
+                            r["topk_w"].cpu().numpy())
+        got = r["out_f32"].cpu().numpy() if scheme == "w8a8" else bf16_to_np(r["out"])
+        want = ref["out32"] if scheme == "w8a8" else ref["out"]
+        assert O.rel_l2(got, want) <= TOL[scheme]
+        assert np.all(got[zero] == 0)
+        if inp["x_scale"] is not None:
+            assert np.all(np.isfinite(got[tiny])) and np.any(got[tiny] != 0)
+            err = O.rel_l2(got[tiny], want[tiny])
+            _flush(f"  bm {bm}: tiny-token rel_l2 {err:.3e}")
+            assert err <= TOL[scheme]
 
 
 @pytest.mark.parametrize("scheme", ["w4a16", "w8a8", "a8w4"])
