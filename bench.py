@@ -53,8 +53,8 @@ WRITE_FACTOR = 1024 * 1.0
 # they were taken with; traffic is reported only while the sources match.
 DOMINANT_COUNTERS = {
     "kernel": "stage1",
-    "fetch_kib": 1195782.7,
-    "write_kib": 165121.7,
+    "fetch_kib": 1195801.1,
+    "write_kib": 165125.2,
     "sources_sha256_16": "85de90551712eb6c",
     "workload": "a8w4_large@T4096",
     "block_m": 128,
@@ -145,8 +145,9 @@ def cpu_baseline(shape, inp, target_s: float = 15.0) -> dict:
             "tokens_per_s": total_tok / elapsed}
 
 
-SWEEP = ("w4a16_qwen3moe_t128", "w8a8_t2048", "a8w4_large@T256", "a8w4_large@T1024",
-         "a8w4_large@T4096", "a8w4_large@T8192", "w4a16_skewed_t8192")
+SWEEP = ("w4a16_qwen3moe_t128", "w8a8_t2048", "a8w4_large@T16", "a8w4_large@T256",
+         "a8w4_large@T1024", "a8w4_large@T4096", "a8w4_large@T8192", "a8w4_tp2@T4096",
+         "a8w4_tp4@T4096", "w4a16_skewed_t8192")
 
 
 def stage_flops(shape) -> dict:
