@@ -66,10 +66,13 @@ __device__ inline void mfma_step_wa(typename Tr<S>::Acc& acc, const u32x4* a,
   }
 }
 
-template <int S, int BM, bool PK>
+// SY: stage each pass's a8w4 outputs in LDS (activation rows of at most
+// half the LDS row; the launcher checks K).
+template <int S, int BM, bool PK, bool SY>
 __global__ __launch_bounds__(kS2Threads) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 moe_stage2_resident(GemmArgs g, int passes, int tile_div) {
   static_assert(S == kW8A8 || S == kA8W4, "one-byte activations only");
+  static_assert(!SY || S == kA8W4, "staged outputs are bf16");
   using T_ = Tr<S>;
   using Acc = typename T_::Acc;
   constexpr int MSUB = BM / 16;
@@ -103,6 +106,7 @@ moe_stage2_resident(GemmArgs g, int passes, int tile_div) {
   constexpr uint32_t S_KS = PK ? 128 : 8;
   constexpr int SB = 1;  // e8m0 bytes (a8w4); W8A8 scales are per channel
   const int G = passes * nsteps;  // weight steps of an item
+  static_assert(kS2Cols * 2 <= kS2RowBytes / 2, "a pass's bf16 row piece fits the free half");
 
   Acc acc[MSUB][kS2Nsub];
   BFrag<S> b0[kS2Nsub], b1[kS2Nsub], b2[kS2Nsub], b3[kS2Nsub];
@@ -224,7 +228,51 @@ moe_stage2_resident(GemmArgs g, int passes, int tile_div) {
     };
     // Outputs of column pass p: lane (lq, lr) holds, for row m*16 + lr,
     // the four columns 4*lq .. 4*lq+3 of each sub-tile.
+    //
+    // a8w4 with activation rows of at most half the LDS row: the pass's
+    // bf16 outputs are staged in the free second half of each row's LDS
+    // slot, then every row's 512-byte piece leaves as 32 16-byte stores
+    // side by side, instead of 32-byte pieces of 16 rows per store.
+    auto epilogue_staged = [&](int p) __attribute__((always_inline)) {
+      constexpr int kStage = kS2RowBytes / 2;
+      __syncthreads();  // the previous pass's copy-out is done with the staging half
+#pragma unroll
+      for (int m = 0; m < MSUB; m++) {
+        if (m < mvalid) {
+          const int row = m * 16 + lr;
+          const float rs = sScale[row];
+#pragma unroll
+          for (int s = 0; s < kS2Nsub; s++) {
+            const uint32_t lo = __builtin_bit_cast(
+                uint32_t, __builtin_convertvector(
+                              (s2_f32x2){acc[m][s][0] * rs, acc[m][s][1] * rs}, s2_bf16x2));
+            const uint32_t hi = __builtin_bit_cast(
+                uint32_t, __builtin_convertvector(
+                              (s2_f32x2){acc[m][s][2] * rs, acc[m][s][3] * rs}, s2_bf16x2));
+            *reinterpret_cast<uint2*>(sA + row * kS2Pitch + kStage +
+                                      (wave * kS2Nsub * 16 + s * 16 + 4 * lq) * 2) =
+                make_uint2(lo, hi);
+            acc[m][s] = Acc{0, 0, 0, 0};
+          }
+        }
+      }
+      __syncthreads();
+      constexpr int kChunks = kS2Cols * 2 / 16;  // 16-byte pieces of a row's pass
+      const int col0 = (c * passes + p) * kS2Cols;
+      for (int i = tid; i < mvalid * 16 * kChunks; i += kS2Threads) {
+        const int r = i / kChunks, ch = i - r * kChunks;
+        const int pair = sRow[r];
+        if (pair >= 0)
+          *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(g.out) + (size_t)pair * g.H +
+                                    col0 + ch * 8) =
+              *reinterpret_cast<const u32x4*>(sA + r * kS2Pitch + kStage + ch * 16);
+      }
+    };
     auto epilogue = [&](int p) __attribute__((always_inline)) {
+      if constexpr (SY) {
+        epilogue_staged(p);
+        return;
+      }
       const int colw = (c * passes + p) * kS2Cols + wave * kS2Nsub * 16 + 4 * lq;
 #pragma unroll
       for (int m = 0; m < MSUB; m++) {
@@ -291,8 +339,15 @@ template <int S, int BM, bool PK>
 hipError_t launch_s2r(const GemmArgs& g, int passes, int tile_div, hipStream_t s) {
   int nblk = device_cu_count();
   nblk = nblk < 8 ? 8 : (nblk / 8) * 8;
-  hipLaunchKernelGGL((moe_stage2_resident<S, BM, PK>), dim3(nblk), dim3(kS2Threads), 0, s, g,
-                     passes, tile_div);
+  if constexpr (S == kA8W4) {
+    if (g.K <= kS2RowBytes / 2) {
+      hipLaunchKernelGGL((moe_stage2_resident<S, BM, PK, true>), dim3(nblk), dim3(kS2Threads), 0,
+                         s, g, passes, tile_div);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((moe_stage2_resident<S, BM, PK, false>), dim3(nblk), dim3(kS2Threads), 0, s,
+                     g, passes, tile_div);
   return hipGetLastError();
 }
 
