@@ -66,13 +66,15 @@ __device__ inline void mfma_step_wa(typename Tr<S>::Acc& acc, const u32x4* a,
   }
 }
 
-// SY: stage each pass's a8w4 outputs in LDS (activation rows of at most
-// half the LDS row; the launcher checks K).
-template <int S, int BM, bool PK, bool SY>
+// SY: how each pass's a8w4 outputs leave: 0 straight from registers; 1
+// staged in the free half of the activation rows' LDS slots (rows of at
+// most half the slot; the launcher checks K); 2 staged 32 rows at a time in
+// a buffer of their own.
+template <int S, int BM, bool PK, int SY>
 __global__ __launch_bounds__(kS2Threads) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 moe_stage2_resident(GemmArgs g, int passes, int tile_div) {
   static_assert(S == kW8A8 || S == kA8W4, "one-byte activations only");
-  static_assert(!SY || S == kA8W4, "staged outputs are bf16");
+  static_assert(SY == 0 || S == kA8W4, "staged outputs are bf16");
   using T_ = Tr<S>;
   using Acc = typename T_::Acc;
   constexpr int MSUB = BM / 16;
@@ -85,6 +87,8 @@ moe_stage2_resident(GemmArgs g, int passes, int tile_div) {
   // contiguous range of passes * kS2Cols), copied at the item's start so
   // that no pass epilogue waits on a global load behind the weight stream.
   __shared__ __attribute__((aligned(16))) float sWs[S == kW8A8 ? kS2MaxPasses * kS2Cols : 4];
+  constexpr int kYRows = 32, kYPitch = kS2Cols * 2 + 16;
+  __shared__ __attribute__((aligned(16))) uint8_t sY[SY == 2 ? kYRows * kYPitch : 16];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lq = lane >> 4;
@@ -235,41 +239,55 @@ moe_stage2_resident(GemmArgs g, int passes, int tile_div) {
     // side by side, instead of 32-byte pieces of 16 rows per store.
     auto epilogue_staged = [&](int p) __attribute__((always_inline)) {
       constexpr int kStage = kS2RowBytes / 2;
-      __syncthreads();  // the previous pass's copy-out is done with the staging half
+      constexpr int CH = SY == 2 ? (MSUB < kYRows / 16 ? MSUB : kYRows / 16) : MSUB;
+      constexpr int kChunks = kS2Cols * 2 / 16;  // 16-byte pieces of a row's pass
+      auto stage_row = [&](int r) __attribute__((always_inline)) -> uint8_t* {
+        if constexpr (SY == 2)
+          return sY + (r % (CH * 16)) * kYPitch;
+        else
+          return sA + r * kS2Pitch + kStage;
+      };
+      const int col0 = (c * passes + p) * kS2Cols;
 #pragma unroll
-      for (int m = 0; m < MSUB; m++) {
-        if (m < mvalid) {
-          const int row = m * 16 + lr;
-          const float rs = sScale[row];
+      for (int m0 = 0; m0 < MSUB; m0 += CH) {
+        if (m0 < mvalid) {
+          __syncthreads();  // the previous copy-out is done with the staging rows
 #pragma unroll
-          for (int s = 0; s < kS2Nsub; s++) {
-            const uint32_t lo = __builtin_bit_cast(
-                uint32_t, __builtin_convertvector(
-                              (s2_f32x2){acc[m][s][0] * rs, acc[m][s][1] * rs}, s2_bf16x2));
-            const uint32_t hi = __builtin_bit_cast(
-                uint32_t, __builtin_convertvector(
-                              (s2_f32x2){acc[m][s][2] * rs, acc[m][s][3] * rs}, s2_bf16x2));
-            *reinterpret_cast<uint2*>(sA + row * kS2Pitch + kStage +
-                                      (wave * kS2Nsub * 16 + s * 16 + 4 * lq) * 2) =
-                make_uint2(lo, hi);
-            acc[m][s] = Acc{0, 0, 0, 0};
+          for (int mm = 0; mm < CH; mm++) {
+            const int m = m0 + mm;
+            if (m < mvalid) {
+              const int row = m * 16 + lr;
+              const float rs = sScale[row];
+#pragma unroll
+              for (int s = 0; s < kS2Nsub; s++) {
+                const uint32_t lo = __builtin_bit_cast(
+                    uint32_t, __builtin_convertvector(
+                                  (s2_f32x2){acc[m][s][0] * rs, acc[m][s][1] * rs}, s2_bf16x2));
+                const uint32_t hi = __builtin_bit_cast(
+                    uint32_t, __builtin_convertvector(
+                                  (s2_f32x2){acc[m][s][2] * rs, acc[m][s][3] * rs}, s2_bf16x2));
+                *reinterpret_cast<uint2*>(stage_row(row) +
+                                          (wave * kS2Nsub * 16 + s * 16 + 4 * lq) * 2) =
+                    make_uint2(lo, hi);
+                acc[m][s] = Acc{0, 0, 0, 0};
+              }
+            }
+          }
+          __syncthreads();
+          const int r0 = m0 * 16, r1 = min(m0 + CH, mvalid) * 16;
+          for (int i = tid; i < (r1 - r0) * kChunks; i += kS2Threads) {
+            const int r = r0 + i / kChunks, ch = i % kChunks;
+            const int pair = sRow[r];
+            if (pair >= 0)
+              *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(g.out) +
+                                        (size_t)pair * g.H + col0 + ch * 8) =
+                  *reinterpret_cast<const u32x4*>(stage_row(r) + ch * 16);
           }
         }
       }
-      __syncthreads();
-      constexpr int kChunks = kS2Cols * 2 / 16;  // 16-byte pieces of a row's pass
-      const int col0 = (c * passes + p) * kS2Cols;
-      for (int i = tid; i < mvalid * 16 * kChunks; i += kS2Threads) {
-        const int r = i / kChunks, ch = i - r * kChunks;
-        const int pair = sRow[r];
-        if (pair >= 0)
-          *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(g.out) + (size_t)pair * g.H +
-                                    col0 + ch * 8) =
-              *reinterpret_cast<const u32x4*>(sA + r * kS2Pitch + kStage + ch * 16);
-      }
     };
     auto epilogue = [&](int p) __attribute__((always_inline)) {
-      if constexpr (SY) {
+      if constexpr (SY != 0) {
         epilogue_staged(p);
         return;
       }
@@ -340,14 +358,16 @@ hipError_t launch_s2r(const GemmArgs& g, int passes, int tile_div, hipStream_t s
   int nblk = device_cu_count();
   nblk = nblk < 8 ? 8 : (nblk / 8) * 8;
   if constexpr (S == kA8W4) {
-    if (g.K <= kS2RowBytes / 2) {
-      hipLaunchKernelGGL((moe_stage2_resident<S, BM, PK, true>), dim3(nblk), dim3(kS2Threads), 0,
-                         s, g, passes, tile_div);
-      return hipGetLastError();
-    }
+    if (g.K <= kS2RowBytes / 2)
+      hipLaunchKernelGGL((moe_stage2_resident<S, BM, PK, 1>), dim3(nblk), dim3(kS2Threads), 0, s,
+                         g, passes, tile_div);
+    else
+      hipLaunchKernelGGL((moe_stage2_resident<S, BM, PK, 2>), dim3(nblk), dim3(kS2Threads), 0, s,
+                         g, passes, tile_div);
+    return hipGetLastError();
   }
-  hipLaunchKernelGGL((moe_stage2_resident<S, BM, PK, false>), dim3(nblk), dim3(kS2Threads), 0, s,
-                     g, passes, tile_div);
+  hipLaunchKernelGGL((moe_stage2_resident<S, BM, PK, 0>), dim3(nblk), dim3(kS2Threads), 0, s, g,
+                     passes, tile_div);
   return hipGetLastError();
 }
 
