@@ -66,15 +66,17 @@ __device__ inline void mfma_step_wa(typename Tr<S>::Acc& acc, const u32x4* a,
   }
 }
 
-// SY: how each pass's a8w4 outputs leave: 0 straight from registers; 1
+// SY: how each pass's outputs leave: 0 straight from registers; 1 (a8w4)
 // staged in the free half of the activation rows' LDS slots (rows of at
 // most half the slot; the launcher checks K); 2 staged 32 rows at a time in
-// a buffer of their own.
+// a buffer of their own (W8A8: tiles of up to 64 rows, no debug dump; the
+// launcher checks both).
 template <int S, int BM, bool PK, int SY>
 __global__ __launch_bounds__(kS2Threads) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 moe_stage2_resident(GemmArgs g, int passes, int tile_div) {
   static_assert(S == kW8A8 || S == kA8W4, "one-byte activations only");
-  static_assert(SY == 0 || S == kA8W4, "staged outputs are bf16");
+  static_assert(SY != 1 || S == kA8W4, "in-row staging holds bf16 outputs");
+  static_assert(SY != 2 || S == kA8W4 || BM <= 64, "W8A8 staging fits LDS up to 64 rows");
   using T_ = Tr<S>;
   using Acc = typename T_::Acc;
   constexpr int MSUB = BM / 16;
@@ -87,7 +89,8 @@ moe_stage2_resident(GemmArgs g, int passes, int tile_div) {
   // contiguous range of passes * kS2Cols), copied at the item's start so
   // that no pass epilogue waits on a global load behind the weight stream.
   __shared__ __attribute__((aligned(16))) float sWs[S == kW8A8 ? kS2MaxPasses * kS2Cols : 4];
-  constexpr int kYRows = 32, kYPitch = kS2Cols * 2 + 16;
+  constexpr int kYEs = S == kA8W4 ? 2 : 4;  // output bytes per element
+  constexpr int kYRows = 32, kYPitch = kS2Cols * kYEs + 16;
   __shared__ __attribute__((aligned(16))) uint8_t sY[SY == 2 ? kYRows * kYPitch : 16];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -233,14 +236,13 @@ moe_stage2_resident(GemmArgs g, int passes, int tile_div) {
     // Outputs of column pass p: lane (lq, lr) holds, for row m*16 + lr,
     // the four columns 4*lq .. 4*lq+3 of each sub-tile.
     //
-    // a8w4 with activation rows of at most half the LDS row: the pass's
-    // bf16 outputs are staged in the free second half of each row's LDS
-    // slot, then every row's 512-byte piece leaves as 32 16-byte stores
-    // side by side, instead of 32-byte pieces of 16 rows per store.
+    // Staged: the pass's outputs go to LDS first, then every row's piece
+    // (512 bytes of bf16, 1 KiB of fp32) leaves as 16-byte stores side by
+    // side, instead of 32- or 64-byte pieces of 16 rows per store.
     auto epilogue_staged = [&](int p) __attribute__((always_inline)) {
       constexpr int kStage = kS2RowBytes / 2;
       constexpr int CH = SY == 2 ? (MSUB < kYRows / 16 ? MSUB : kYRows / 16) : MSUB;
-      constexpr int kChunks = kS2Cols * 2 / 16;  // 16-byte pieces of a row's pass
+      constexpr int kChunks = kS2Cols * kYEs / 16;  // 16-byte pieces of a row's pass
       auto stage_row = [&](int r) __attribute__((always_inline)) -> uint8_t* {
         if constexpr (SY == 2)
           return sY + (r % (CH * 16)) * kYPitch;
@@ -260,15 +262,25 @@ moe_stage2_resident(GemmArgs g, int passes, int tile_div) {
               const float rs = sScale[row];
 #pragma unroll
               for (int s = 0; s < kS2Nsub; s++) {
-                const uint32_t lo = __builtin_bit_cast(
-                    uint32_t, __builtin_convertvector(
-                                  (s2_f32x2){acc[m][s][0] * rs, acc[m][s][1] * rs}, s2_bf16x2));
-                const uint32_t hi = __builtin_bit_cast(
-                    uint32_t, __builtin_convertvector(
-                                  (s2_f32x2){acc[m][s][2] * rs, acc[m][s][3] * rs}, s2_bf16x2));
-                *reinterpret_cast<uint2*>(stage_row(row) +
-                                          (wave * kS2Nsub * 16 + s * 16 + 4 * lq) * 2) =
-                    make_uint2(lo, hi);
+                const int cl = wave * kS2Nsub * 16 + s * 16 + 4 * lq;  // column in the pass
+                if constexpr (S == kA8W4) {
+                  const uint32_t lo = __builtin_bit_cast(
+                      uint32_t,
+                      __builtin_convertvector(
+                          (s2_f32x2){acc[m][s][0] * rs, acc[m][s][1] * rs}, s2_bf16x2));
+                  const uint32_t hi = __builtin_bit_cast(
+                      uint32_t,
+                      __builtin_convertvector(
+                          (s2_f32x2){acc[m][s][2] * rs, acc[m][s][3] * rs}, s2_bf16x2));
+                  *reinterpret_cast<uint2*>(stage_row(row) + cl * 2) = make_uint2(lo, hi);
+                } else {
+                  const float4 ws = *reinterpret_cast<const float4*>(&sWs[p * kS2Cols + cl]);
+                  *reinterpret_cast<float4*>(stage_row(row) + cl * 4) =
+                      make_float4(((float)acc[m][s][0] * rs) * ws.x,
+                                  ((float)acc[m][s][1] * rs) * ws.y,
+                                  ((float)acc[m][s][2] * rs) * ws.z,
+                                  ((float)acc[m][s][3] * rs) * ws.w);
+                }
                 acc[m][s] = Acc{0, 0, 0, 0};
               }
             }
@@ -279,8 +291,8 @@ moe_stage2_resident(GemmArgs g, int passes, int tile_div) {
             const int r = r0 + i / kChunks, ch = i % kChunks;
             const int pair = sRow[r];
             if (pair >= 0)
-              *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(g.out) +
-                                        (size_t)pair * g.H + col0 + ch * 8) =
+              *reinterpret_cast<u32x4*>(reinterpret_cast<uint8_t*>(g.out) +
+                                        ((size_t)pair * g.H + col0) * kYEs + ch * 16) =
                   *reinterpret_cast<const u32x4*>(stage_row(r) + ch * 16);
           }
         }
@@ -365,6 +377,13 @@ hipError_t launch_s2r(const GemmArgs& g, int passes, int tile_div, hipStream_t s
       hipLaunchKernelGGL((moe_stage2_resident<S, BM, PK, 2>), dim3(nblk), dim3(kS2Threads), 0, s,
                          g, passes, tile_div);
     return hipGetLastError();
+  }
+  if constexpr (BM <= 64) {
+    if (g.dump == nullptr) {
+      hipLaunchKernelGGL((moe_stage2_resident<S, BM, PK, 2>), dim3(nblk), dim3(kS2Threads), 0, s,
+                         g, passes, tile_div);
+      return hipGetLastError();
+    }
   }
   hipLaunchKernelGGL((moe_stage2_resident<S, BM, PK, 0>), dim3(nblk), dim3(kS2Threads), 0, s, g,
                      passes, tile_div);
