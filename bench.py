@@ -89,57 +89,81 @@ def weight_bytes_per_expert(shape, which: str) -> float:
 
 def algorithmic_bytes(shape, touched: int) -> dict:
     """Bytes each kernel must move at minimum (the per-unit figures times the
-    units one launch processes): weights of the touched experts, activations
-    in their scheme format, outputs once."""
+    units one launch processes): the weights (codes and scales) of the
+    touched experts, the activations in their scheme format, the output
+    once, and the routing.  The intermediate h and the per-pair outputs
+    y_pairs are implementation overhead and are reported apart
+    (``overhead_bytes``), not counted here."""
     T, H, I, k = shape.tokens, shape.hidden, shape.inter, shape.topk
     P = T * k
     xb = 2 if shape.scheme == "w4a16" else 1
     xs = 0 if shape.scheme == "w4a16" else 4
-    hb = 2 if shape.scheme == "w4a16" else 1
-    yb = 4 if shape.scheme == "w8a8" else 2
-    s1 = touched * weight_bytes_per_expert(shape, "w13") + T * (H * xb + xs) + P * (I * hb + xs)
-    s2 = touched * weight_bytes_per_expert(shape, "w2") + P * (I * hb + xs) + P * H * yb
-    comb = P * H * yb + P * 4 + T * H * 2
-    step = (touched * (weight_bytes_per_expert(shape, "w13") + weight_bytes_per_expert(shape, "w2"))
-            + T * (H * xb + xs) + T * H * 2 + T * shape.experts * 4 + P * 8)
+    w13 = touched * weight_bytes_per_expert(shape, "w13")
+    w2 = touched * weight_bytes_per_expert(shape, "w2")
+    s1 = w13 + T * (H * xb + xs)
+    s2 = w2
+    comb = T * H * 2 + P * 4
+    step = w13 + w2 + T * (H * xb + xs) + T * H * 2 + T * shape.experts * 4 + P * 8
     return {"stage1": s1, "stage2": s2, "combine": comb, "step": step}
 
 
+def overhead_bytes(shape) -> dict:
+    """Bytes of the intermediates the algorithm does not need to move: h
+    written by stage 1 (fp32 for the requantized schemes, bf16 for W4A16)
+    and read back, and y_pairs written by stage 2 and read by combine."""
+    P = shape.tokens * shape.topk
+    hb = 2 if shape.scheme == "w4a16" else 4
+    yb = 4 if shape.scheme == "w8a8" else 2
+    return {"h_write": P * shape.inter * hb, "h_read": P * shape.inter * hb,
+            "y_pairs_write": P * shape.hidden * yb, "y_pairs_read": P * shape.hidden * yb}
+
+
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
+
+
 def cpu_baseline(shape, inp, target_s: float = 15.0) -> dict:
-    """Time the CPU oracle on a bounded sample of the same workload."""
+    """Time the CPU oracle on a bounded sample of the same workload: whole
+    tokens drawn at random, routed by the oracle, every expert they touch
+    run on their rows; BLAS threads = the cores this process may use."""
     import oracle as O
+    from threadpoolctl import threadpool_limits
+
     from quantized_mixture_experts_moe_amd import synth
 
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
+    cores = len(os.sched_getaffinity(0))
     rng = np.random.default_rng(0)
     n_tok = 2
     elapsed = 0.0
     total_flops = 0.0
     total_pairs = 0
     total_tok = 0
-    while True:
-        toks = rng.choice(shape.tokens, n_tok, replace=False)
-        ids, w = O.route(inp["logits"][toks], shape.topk)
-        experts = sorted(set(ids.reshape(-1).tolist()))
-        wts = {e: synth.expert_weights(shape, e) for e in experts}  # generation: not timed
-        xs = None if inp["x_scale"] is None else inp["x_scale"][toks]
-        t0 = time.perf_counter()
-        O.moe_forward(shape.scheme, inp["x"][toks], xs, lambda e: wts[e], ids, w)
-        dt = time.perf_counter() - t0
-        elapsed += dt
-        total_pairs += n_tok * shape.topk
-        total_tok += n_tok
-        total_flops += 6.0 * shape.hidden * shape.inter * n_tok * shape.topk
-        log(f"cpu oracle: {n_tok} tokens in {dt:.2f}s")
-        if elapsed >= target_s * 0.5 or n_tok >= 256:
-            break
-        n_tok = int(min(256, max(n_tok * 2, n_tok * (target_s - elapsed) / max(dt, 1e-3) / 2)))
+    with threadpool_limits(cores):
+        while True:
+            toks = rng.choice(shape.tokens, min(n_tok, shape.tokens), replace=False)
+            ids, w = O.route(inp["logits"][toks], shape.topk)
+            experts = sorted(set(ids.reshape(-1).tolist()))
+            wts = {e: synth.expert_weights(shape, e) for e in experts}  # generation: not timed
+            xs = None if inp["x_scale"] is None else inp["x_scale"][toks]
+            t0 = time.perf_counter()
+            O.moe_forward(shape.scheme, inp["x"][toks], xs, lambda e: wts[e], ids, w)
+            dt = time.perf_counter() - t0
+            elapsed += dt
+            total_pairs += len(toks) * shape.topk
+            total_tok += len(toks)
+            total_flops += 6.0 * shape.hidden * shape.inter * len(toks) * shape.topk
+            log(f"cpu oracle: {len(toks)} tokens in {dt:.2f}s")
+            if elapsed >= target_s * 0.5 or n_tok >= 256 or len(toks) == shape.tokens:
+                break
+            n_tok = int(min(256, max(n_tok * 2, n_tok * (target_s - elapsed) / max(dt, 1e-3) / 2)))
     return {"value": total_flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(cores),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": _cpu_model(),
             "sample": f"{total_tok} tokens ({total_pairs} token-expert rows) of {shape.name}, "
                       f"fp64 numpy oracle, {elapsed:.1f}s; weight generation not timed",
             "tokens_per_s": total_tok / elapsed}
@@ -215,7 +239,7 @@ def graph_step_ms(torch, ops, args, flush, b: dict, eager_step):
     return float(ms.mean()), float(np.median(ms))
 
 
-def run_workload(name: str, args, torch, with_cpu: bool) -> dict:
+def run_workload(name: str, args, torch, with_cpu: bool, cpu_seconds: float = 20.0) -> dict:
     from quantized_mixture_experts_moe_amd import ops, synth
     from quantized_mixture_experts_moe_amd.shapes import default_block_m, shape_by_name
 
@@ -330,7 +354,7 @@ def run_workload(name: str, args, torch, with_cpu: bool) -> dict:
             and layout == c["weight_layout"] and kernel_sources_hash() == c["sources_sha256_16"]):
         traffic = int(round(c["fetch_kib"] * FETCH_FACTOR + c["write_kib"] * WRITE_FACTOR))
     roof.update({"traffic": traffic,
-                 "kernel": f"moe_gemm_kernel {dom} ({shape.scheme}, block_m {bm})",
+                 "kernel": f"{dom} ({shape.scheme}, block_m {bm})",
                  "kernel_ms": round(kern[dom], 4), "algorithmic_bytes": int(ab[dom]),
                  "algorithmic_flops": sf[dom]})
     step_gbs = ab["step"] / (ms_per_step * 1e-3) / 1e9
@@ -354,9 +378,11 @@ def run_workload(name: str, args, torch, with_cpu: bool) -> dict:
         "step_mfma_frac": round(tflops / peak_tf, 4),
         "kernel_ms": {n: round(v, 4) for n, v in kern.items()},
         "roofline": roof,
+        "overhead_bytes": overhead_bytes(shape),
+        "ms_per_step_stat": "mean over the timed steps (median in ms_per_step_median)",
     }
     if with_cpu:
-        res["cpu_baseline"] = cpu_baseline(shape, inp, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(shape, inp, cpu_seconds)
     del g, W, y, ws, flush
     torch.cuda.empty_cache()
     return res
@@ -437,7 +463,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="a8w4_large@T4096")
     ap.add_argument("--sweep", action="store_true",
-                    help="run every workload of the sweep, one JSON line each (no CPU baseline)")
+                    help="run every workload of the sweep, one JSON line each (CPU baseline on a "
+                         "shorter sample per workload unless --no-cpu-baseline)")
     ap.add_argument("--tile-sweep", action="store_true",
                     help="time every block_m for the a8w4 block and its tensor-parallel shares "
                          "at each token bucket")
@@ -481,9 +508,10 @@ def main():
         return
     if args.sweep:
         for name in SWEEP:
-            print(json.dumps(run_workload(name, args, torch, False)), flush=True)
+            print(json.dumps(run_workload(name, args, torch, not args.no_cpu_baseline,
+                                          min(args.cpu_seconds, 8.0))), flush=True)
         return
-    res = run_workload(args.workload, args, torch, not args.no_cpu_baseline)
+    res = run_workload(args.workload, args, torch, not args.no_cpu_baseline, args.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 

@@ -34,6 +34,18 @@ Schemes: ``w4a16`` (exact fp64 arithmetic on the dequantized int4 weights),
 the SiLU and the requantization so the integer results can be compared bit
 for bit), ``a8w4`` (the fp8 x e2m1 x 2^s products are exact in fp64 at these
 sizes; the fp8 requantization of h is decided in fp32 like the kernels).
+
+Pins (``tests/test_oracle.py``; every function below has at least one):
+format decoders and encoders against torch's float8/e8m0/bf16 casts and the
+OCP tables in ``tests/golden``; routing against a brute-force sort; grouping
+against a brute-force stable sort and its invariants; one expert with top-1
+against a textbook dense FFN; every expert on every token then select, against
+the grouped layer; W8A8 accumulators against Python integers and the W8A8
+rescale (``rescale_w8a8``) and the layer's gu and y against exact rationals
+rounded to fp32 after each product; a8w4 accumulators against exact
+rationals; the int8 and e4m3 requantization at exact ties where only the
+correctly rounded quotient h / s gives the right code; SiLU closed forms;
+``rel_l2`` closed forms.
 """
 from __future__ import annotations
 
@@ -268,18 +280,26 @@ def expert_w4a16(x_bits, w13, s13, w2, s2) -> dict:
     return {"gu": gu, "h": hin, "y": y}
 
 
+def rescale_w8a8(acc: np.ndarray, s_row: np.ndarray, s_col: np.ndarray) -> np.ndarray:
+    """fp32 rescale of exact int32 sums: ``f32(f32(f32(acc) * s_row) * s_col)``,
+    three roundings in this order (row = token or h row, col = output
+    channel).  ``acc`` stays below 2^24 in magnitude here, so ``f32(acc)`` is
+    exact; the two products are each rounded to nearest even."""
+    a = np.asarray(acc).astype(f32)
+    t = (a * np.asarray(s_row, f32)[:, None]).astype(f32)
+    return (t * np.asarray(s_col, f32)[None, :]).astype(f32)
+
+
 def expert_w8a8(xq, sx, w13, s13, w2, s2) -> dict:
     inter = w13.shape[0] // 2
     # int8 x int8 products summed over K < 2^31: integer-valued fp64 partial
     # sums stay exact (< 2^53), so the fp64 product is the exact integer.
     acc1 = np.rint(np.asarray(xq, f64) @ np.asarray(w13, f64).T).astype(np.int64)
-    gu = (acc1.astype(f32) * np.asarray(sx, f32)[:, None]).astype(f32) \
-        * np.asarray(s13, f32)[None, :]
-    gu = gu.astype(f32)
+    gu = rescale_w8a8(acc1, sx, s13)
     h = silu_mul_f32(gu, inter)
     hq, sh = quant_rows_int8(h)
     acc2 = np.rint(hq.astype(f64) @ np.asarray(w2, f64).T).astype(np.int64)
-    y = ((acc2.astype(f32) * sh[:, None]).astype(f32) * np.asarray(s2, f32)[None, :]).astype(f32)
+    y = rescale_w8a8(acc2, sh, s2)
     return {"acc1": acc1, "gu": gu, "h": h, "hq": hq, "h_scale": sh, "acc2": acc2, "y": y}
 
 
@@ -337,12 +357,16 @@ def combine(scheme: str, y_pairs: np.ndarray, topk_w: np.ndarray) -> dict:
 # ----------------------------------------------------------------------------
 
 
-def moe_forward(scheme: str, x, x_scale, weights, topk_ids, topk_w, keep=()) -> dict:
+def moe_forward(scheme: str, x, x_scale, weights, topk_ids, topk_w, keep=(),
+                map_fn=map) -> dict:
     """Run the experts over all (token, slot) pairs and combine.
 
     ``weights`` is a dict of stacked ``[E, ...]`` arrays or a callable
     ``e -> dict`` for one expert.  ``keep`` names per-pair intermediates to
-    return (e.g. ``("acc1", "acc2")``), indexed by pair id.
+    return (e.g. ``("acc1", "acc2")``), indexed by pair id.  The experts are
+    independent of one another; ``map_fn`` (the builtin ``map`` by default,
+    or a thread pool's ``map``) runs them, and the results are placed in
+    ascending expert order either way.
     """
     ids = np.asarray(topk_ids, np.int64)
     T, k = ids.shape
@@ -350,12 +374,16 @@ def moe_forward(scheme: str, x, x_scale, weights, topk_ids, topk_w, keep=()) -> 
     flat = ids.reshape(-1)
     y_pairs = None
     kept = {}
-    for e in np.unique(flat):
+
+    def run_expert(e):
         pairs = np.nonzero(flat == e)[0]
         tok = pairs // k
         wts = weights(int(e)) if callable(weights) else {n: v[e] for n, v in weights.items()}
         xs_rows = None if x_scale is None else np.asarray(x_scale)[tok]
         r = expert_ffn(scheme, np.asarray(x)[tok], xs_rows, wts)
+        return pairs, {n: r[n] for n in ("y",) + tuple(keep)}
+
+    for pairs, r in map_fn(run_expert, np.unique(flat)):
         if y_pairs is None:
             y_pairs = np.zeros((P, r["y"].shape[1]), r["y"].dtype)
         y_pairs[pairs] = r["y"]
@@ -381,6 +409,7 @@ def rel_l2(a: np.ndarray, b: np.ndarray) -> float:
 __all__ = [
     "bf16_bits_to_f64", "round_to_bf16", "bf16_bits_from_value", "int4_values",
     "E2M1_TABLE", "e2m1_values", "e8m0_values", "E4M3_TABLE", "e4m3_values", "e4m3_encode",
-    "route", "align", "quant_rows_int8", "quant_rows_e4m3", "silu_mul_f32", "dequant_int4_g32", "dequant_mxfp4", "expert_w4a16", "expert_w8a8",
+    "route", "align", "quant_rows_int8", "quant_rows_e4m3", "silu_mul_f32", "dequant_int4_g32",
+    "dequant_mxfp4", "rescale_w8a8", "expert_w4a16", "expert_w8a8",
     "expert_a8w4", "expert_ffn", "combine", "moe_forward", "rel_l2",
 ]

@@ -384,3 +384,158 @@ def test_generator_shapes_and_reproducible():
     assert a["w2"].shape == (8, 256, 64) and a["w2_scale"].shape == (8, 256, 4)
     e3 = synth.expert_weights(W4A16_TINY, 3)
     np.testing.assert_array_equal(e3["w2"], a["w2"][3])
+
+
+# ---------------------------------------------------------------- comparator
+
+def test_rel_l2_closed_forms():
+    """rel_l2(a, b) = ||a - b|| / ||b|| over all elements, values worked by hand."""
+    # [3, 4] against [0, 5]: difference [3, -1], ||.|| = sqrt(10); ||b|| = 5.
+    assert O.rel_l2(np.array([3.0, 4.0]), np.array([0.0, 5.0])) == pytest.approx(
+        math.sqrt(10) / 5, rel=1e-15)
+    # orthogonal unit vectors: ||[1, -1]|| / 1
+    assert O.rel_l2(np.array([1.0, 0.0]), np.array([0.0, 1.0])) == pytest.approx(
+        math.sqrt(2), rel=1e-15)
+    # [1, -2, 2] against [2, -2, 1]: difference [-1, 0, 1]; ||b|| = 3.
+    assert O.rel_l2(np.array([1.0, -2.0, 2.0]), np.array([2.0, -2.0, 1.0])) == pytest.approx(
+        math.sqrt(2) / 3, rel=1e-15)
+    b = np.random.default_rng(4).standard_normal((30, 17))
+    assert O.rel_l2(b, b) == 0.0
+    assert O.rel_l2(np.zeros_like(b), b) == pytest.approx(1.0, rel=1e-14)
+    assert O.rel_l2(3 * b, b) == pytest.approx(2.0, rel=1e-14)
+    assert O.rel_l2(b * (1 + 1e-3), b) == pytest.approx(1e-3, rel=1e-9)
+    # the whole array, not row by row: one bad row of 30 weighs 1/sqrt(30)
+    c = b.copy()
+    c[7] = -c[7]
+    assert O.rel_l2(c, b) == pytest.approx(
+        2 * np.linalg.norm(b[7]) / np.linalg.norm(b), rel=1e-12)
+
+
+# ---------------------------------------------------------------- fp32 recipes
+
+def _f32_rne(q: Fraction) -> Fraction:
+    """Nearest IEEE binary32 value to an exact rational, ties to even
+    (normal range only, which the callers assert)."""
+    if q == 0:
+        return Fraction(0)
+    sign = -1 if q < 0 else 1
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    assert -126 <= e <= 127, q
+    ulp = Fraction(2) ** (e - 23)
+    m = a / ulp
+    n = m.numerator // m.denominator
+    rem = m - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return sign * n * ulp
+
+
+def _frac(v) -> Fraction:
+    return Fraction(float(v))
+
+
+def test_w8a8_rescale_rounds_twice_in_order():
+    """The W8A8 rescale is f32(f32(f32(acc) * s_row) * s_col): checked against
+    exact rational arithmetic rounded to fp32 after each product.  The cases
+    include many where one rounding of the exact triple product, or the
+    other order of the two products, gives another fp32 value."""
+    rng = np.random.default_rng(12)
+    n = 400
+    acc = rng.integers(-2 ** 23, 2 ** 23, n)
+    sx = rng.uniform(1e-3, 5e-2, n).astype(np.float32)
+    sw = rng.uniform(1e-4, 1e-2, n).astype(np.float32)
+    single = swapped = 0
+    for i in range(n):
+        got = O.rescale_w8a8(acc[i:i + 1, None], sx[i:i + 1], sw[i:i + 1])
+        assert got.dtype == np.float32 and got.shape == (1, 1)
+        a, x, w = Fraction(int(acc[i])), _frac(sx[i]), _frac(sw[i])
+        want = _f32_rne(_f32_rne(_f32_rne(a) * x) * w)
+        assert _frac(got[0, 0]) == want, (acc[i], sx[i], sw[i])
+        single += _f32_rne(a * x * w) != want
+        swapped += _f32_rne(_f32_rne(a * w) * x) != want
+    assert single >= 20 and swapped >= 20, (single, swapped)
+
+
+def test_w8a8_layer_intermediates_against_rationals():
+    """gu and y of the W8A8 expert from Python integers and rationals: the
+    accumulators exact, then the two-step fp32 rescale of each."""
+    sh, inp = _tiny("w8a8", T=5, H=64, I=32, E=2, k=1, seed=21)
+    ids, w = O.route(inp["logits"], 1)
+    W = {k: inp[k] for k in ("w13", "w13_scale", "w2", "w2_scale")}
+    r = O.moe_forward("w8a8", inp["x"], inp["x_scale"], W, ids, w,
+                      keep=("gu", "hq", "h_scale", "acc2"))
+    for p in range(5):
+        e = int(ids[p, 0])
+        for n in (0, 9, 40, 63):
+            acc = sum(int(a) * int(b) for a, b in zip(inp["x"][p], inp["w13"][e, n]))
+            want = _f32_rne(_f32_rne(Fraction(acc) * _frac(inp["x_scale"][p]))
+                            * _frac(inp["w13_scale"][e, n]))
+            assert _frac(r["gu"][p, n]) == want
+        for n in (0, 31, 63):
+            acc = sum(int(a) * int(b) for a, b in zip(r["hq"][p], inp["w2"][e, n]))
+            assert r["acc2"][p, n] == acc
+            want = _f32_rne(_f32_rne(Fraction(acc) * _frac(r["h_scale"][p]))
+                            * _frac(inp["w2_scale"][e, n]))
+            assert _frac(r["y_pairs"][p, n]) == want
+
+
+def _tie_rows(qmax, n_rows, seed, midpoints):
+    """Rows [qmax * s, h] whose quotient h / s is exactly a midpoint m
+    between two codes, with s an fp32 of 16 significant bits (so h = m * s
+    and qmax * s are exact fp32 values and f32(qmax * s / qmax) = s).
+    Returns (h, s, m) triples where RN(h * RN(1/s)) is not m: there the
+    correctly rounded quotient and the reciprocal product take different
+    sides of the tie."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    tries = 0
+    while len(rows) < n_rows:
+        tries += 1
+        assert tries < 200000
+        mant = int(rng.integers(2 ** 15, 2 ** 16))
+        s = Fraction(mant, 2 ** 15) * Fraction(2) ** int(rng.integers(-8, 4))
+        m = midpoints[int(rng.integers(0, len(midpoints)))] * (1 if rng.integers(0, 2) else -1)
+        h = m * s
+        assert _f32_rne(h) == h and _f32_rne(qmax * s) == qmax * s
+        if _f32_rne(_f32_rne(h) * _f32_rne(1 / s)) != m:
+            rows.append((h, s, m))
+    return rows
+
+
+def test_requant_int8_quotient_is_correctly_rounded():
+    """Per-row int8 requantization: code = round_half_even(f32(h / s)) with
+    the correctly rounded fp32 quotient.  Every row here puts h / s exactly
+    on a .5 tie where h * RN(1/s) lands off the tie, so a reciprocal-product
+    quotient would give the other code."""
+    mids = [Fraction(2 * n + 1, 2) for n in range(0, 126)]
+    rows = _tie_rows(127, 40, 31, mids)
+    h = np.array([[float(127 * s), float(hv)] for hv, s, _ in rows], np.float32)
+    q, sc = O.quant_rows_int8(h)
+    for i, (hv, s, m) in enumerate(rows):
+        assert _frac(sc[i]) == s
+        fl = m.numerator // m.denominator  # floor
+        even = fl if fl % 2 == 0 else fl + 1
+        assert q[i, 0] == 127 and q[i, 1] == even, (float(hv), float(s), m)
+
+
+def test_requant_e4m3_quotient_is_correctly_rounded():
+    """Per-row e4m3 requantization: code = RNE(f32(h / s)) with the correctly
+    rounded fp32 quotient; h / s sits exactly halfway between two e4m3
+    values, where h * RN(1/s) lands off the tie.  Expected codes from torch's
+    own float8_e4m3fn cast of the exact quotient."""
+    vals = np.sort(np.unique(np.abs(O.E4M3_TABLE[~np.isnan(O.E4M3_TABLE)])))
+    normal = vals[vals >= 2.0 ** -6]
+    mids = [Fraction(float(a)) / 2 + Fraction(float(b)) / 2 for a, b in zip(normal[:-1], normal[1:])]
+    rows = _tie_rows(448, 40, 32, mids)
+    h = np.array([[float(448 * s), float(hv)] for hv, s, _ in rows], np.float32)
+    q, sc = O.quant_rows_e4m3(h)
+    want = torch.tensor([float(m) for _, _, m in rows], dtype=torch.float32) \
+        .to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    for i, (hv, s, m) in enumerate(rows):
+        assert _frac(sc[i]) == s
+        assert q[i, 0] == 0x7E and q[i, 1] == want[i], (float(hv), float(s), m)
