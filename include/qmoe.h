@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define QMOE_ABI_VERSION 2
+#define QMOE_ABI_VERSION 3
 
 typedef enum {
   QMOE_OK = 0,
@@ -166,6 +166,28 @@ qmoe_status qmoe_align(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
                        size_t ws_bytes, void* stream);
 /* Copies the align flag word to host memory *flags_out (synchronises).  */
 qmoe_status qmoe_check_flags(const void* align_ws, int32_t* flags_out, void* stream);
+
+/* ---------------------------------------------------------------------
+ * qmoe_align_noalloc -- qmoe_align for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same outputs, bit for bit, with no workspace
+ * argument.  The workspace lives in a device array inside the library, of
+ * QMOE_ALIGN_NOALLOC_MAX_BYTES per GPU, held from the library's load until
+ * the process ends; the call itself allocates nothing.
+ * flags: optional device int32 that receives the flag word qmoe_align
+ *   leaves in its workspace (bit 0: an id outside [0,E); bit 1: an id
+ *   repeated within a token); NULL to discard it.
+ * Limit: qmoe_align_workspace(T, k, E) <= QMOE_ALIGN_NOALLOC_MAX_BYTES
+ *   (up to 65024 tokens with 1024 experts, 130304 with 512, 260608 with
+ *   256); larger sizes return QMOE_ERR_UNSUPPORTED and launch nothing.
+ * All calls on one GPU share its array: calls that overlap in time on one
+ * GPU (two streams, or two host threads) race and give undefined outputs;
+ * calls ordered on one stream are safe.                                   */
+#define QMOE_ALIGN_NOALLOC_MAX_BYTES (1u << 20)
+qmoe_status qmoe_align_noalloc(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
+                               int32_t block_m, int32_t* sorted_pair_ids,
+                               int32_t* tile_expert, int32_t* expert_offsets,
+                               int32_t* num_padded, int32_t* flags, void* stream);
 
 /* ---------------------------------------------------------------------
  * qmoe_grouped_ffn -- stage 1 (gate/up projection of every expert in one

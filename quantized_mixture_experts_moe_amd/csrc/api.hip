@@ -181,6 +181,64 @@ qmoe_status qmoe_align(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
                                  (hipStream_t)stream));
 }
 
+// ---------------------------------------------------------------------------
+// qmoe_align_noalloc: qmoe_align with its workspace in a file-scope device
+// array instead of a caller buffer, for callers that cannot allocate.
+//
+// The array is statically sized (QMOE_ALIGN_NOALLOC_MAX_BYTES); every GPU the
+// library runs on holds its own copy until the process ends.  In host code
+// `scratch` only names the symbol: its device address on the current device
+// comes from hipGetSymbolAddress, taken once per device on the first call
+// there and cached below; only that address is ever passed to a kernel.
+static __device__ __align__(256) uint8_t scratch[QMOE_ALIGN_NOALLOC_MAX_BYTES];
+
+static hipError_t scratch_ptr(uint8_t** out) {
+  static std::mutex mu;
+  static uint8_t* cached[64] = {nullptr};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cached[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    cached[dev] = reinterpret_cast<uint8_t*>(p);
+  }
+  *out = cached[dev];
+  return hipSuccess;
+}
+
+qmoe_status qmoe_align_noalloc(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
+                               int32_t block_m, int32_t* sorted_pair_ids,
+                               int32_t* tile_expert, int32_t* expert_offsets,
+                               int32_t* num_padded, int32_t* flags, void* stream) {
+  if (T < 0 || k < 1 || E < 1 || k > E || !valid_block_m(block_m)) return QMOE_ERR_INVALID_ARG;
+  if ((long long)T * k > (1ll << 30)) return QMOE_ERR_INVALID_ARG;
+  if (E > 1024) return QMOE_ERR_UNSUPPORTED;
+  if ((T > 0 && !topk_ids) || !sorted_pair_ids || !tile_expert || !expert_offsets ||
+      !num_padded)
+    return QMOE_ERR_INVALID_ARG;
+  const AlignWs lay = align_ws_layout(T, E);
+  if (lay.total > (size_t)QMOE_ALIGN_NOALLOC_MAX_BYTES) return QMOE_ERR_UNSUPPORTED;
+  uint8_t* w = nullptr;
+  hipError_t e = scratch_ptr(&w);
+  if (e != hipSuccess) return hip_status(e);
+  // Every region of the workspace is written before it is read within one
+  // call (counts and chunk flags by the count kernel, totals and the flag
+  // word by the scan or place kernel), so nothing is cleared first.
+  const int cap = (int)qmoe_align_capacity(T, k, E, block_m);
+  int32_t* fl = flags ? flags : reinterpret_cast<int32_t*>(w + lay.flags);
+  return hip_status(launch_align(topk_ids, T, k, E, block_m, sorted_pair_ids, tile_expert,
+                                 expert_offsets, num_padded,
+                                 reinterpret_cast<int32_t*>(w + lay.counts),
+                                 reinterpret_cast<int32_t*>(w + lay.chunk_flags),
+                                 reinterpret_cast<int32_t*>(w + lay.totals), fl, cap,
+                                 (hipStream_t)stream));
+}
+
 qmoe_status qmoe_check_flags(const void* align_ws, int32_t* flags_out, void* stream) {
   if (!align_ws || !flags_out) return QMOE_ERR_INVALID_ARG;
   int32_t v = 0;

@@ -22,12 +22,13 @@ QMOE_FLAG_DUMP_ACC = 1
 QMOE_FLAG_PREPACKED = 2
 # QMOE_ABI_VERSION of the include/qmoe.h this binding follows; loading a
 # library that reports another version fails.
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 # Every symbol include/qmoe.h declares.
 EXPORTS = (
     "qmoe_abi_version", "qmoe_status_str", "qmoe_last_hip_error", "qmoe_route",
     "qmoe_align_capacity", "qmoe_align_workspace", "qmoe_align", "qmoe_check_flags",
+    "qmoe_align_noalloc",
     "qmoe_grouped_ffn_workspace", "qmoe_grouped_ffn_debug_offsets", "qmoe_grouped_ffn",
     "qmoe_grouped_ffn_profiled", "qmoe_combine", "qmoe_prepack",
 )
@@ -77,6 +78,8 @@ def _lib() -> ctypes.CDLL:
     L.qmoe_align_workspace.argtypes = [i32, i32, i32]
     L.qmoe_align.restype = ctypes.c_int
     L.qmoe_align.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+    L.qmoe_align_noalloc.restype = ctypes.c_int
+    L.qmoe_align_noalloc.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]
     L.qmoe_check_flags.restype = ctypes.c_int
     L.qmoe_check_flags.argtypes = [vp, ctypes.POINTER(ctypes.c_int32), vp]
     L.qmoe_grouped_ffn_workspace.restype = sz
@@ -178,6 +181,29 @@ def align(topk_ids: torch.Tensor, E: int, block_m: int, ws: Optional[torch.Tenso
                              _ptr(out["tile_expert"]), _ptr(out["expert_offsets"]),
                              _ptr(out["num_padded"]), _ptr(ws), ws.numel(), _stream(dev)),
            "qmoe_align")
+    return out
+
+
+def align_noalloc(topk_ids: torch.Tensor, E: int, block_m: int, out: Optional[dict] = None,
+                  flags: Optional[torch.Tensor] = None) -> dict:
+    """qmoe_align_noalloc: the outputs of qmoe_align with the workspace held
+    inside the library (``out`` reuses a previous result's buffers; ``flags``
+    is an optional int32 device tensor of one element for the flag word)."""
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    cap = align_capacity(T, k, E, block_m)
+    if out is None:
+        out = {
+            "sorted_pair_ids": torch.empty(cap, dtype=torch.int32, device=dev),
+            "tile_expert": torch.empty(cap // block_m, dtype=torch.int32, device=dev),
+            "expert_offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
+            "num_padded": torch.empty(1, dtype=torch.int32, device=dev),
+            "block_m": block_m,
+        }
+    _check(_lib().qmoe_align_noalloc(_ptr(topk_ids), T, k, E, block_m,
+                                     _ptr(out["sorted_pair_ids"]), _ptr(out["tile_expert"]),
+                                     _ptr(out["expert_offsets"]), _ptr(out["num_padded"]),
+                                     _ptr(flags), _stream(dev)), "qmoe_align_noalloc")
     return out
 
 

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = ops.lib()
-    assert L.qmoe_abi_version() == 2 == ops.ABI_VERSION
+    assert L.qmoe_abi_version() == 3 == ops.ABI_VERSION
     for s in range(4):
         assert L.qmoe_status_str(s)
     assert L.qmoe_status_str(99) == b"unknown status"
@@ -78,6 +78,31 @@ def test_align_validation():
     assert L.qmoe_align(p, 64, 2, 2000, 16, p, p, p, p, p, 1 << 30, None) == \
         ops.QMOE_ERR_UNSUPPORTED
     assert L.qmoe_check_flags(None, None, None) == ops.QMOE_ERR_INVALID_ARG
+
+
+def test_align_noalloc_validation():
+    """The no-allocation align refuses bad arguments like qmoe_align, and
+    sizes whose workspace exceeds its static array, before touching the
+    GPU."""
+    L = ops.lib()
+    p = ctypes.c_void_p(0x1000)
+    lim = 1 << 20
+    assert L.qmoe_align_noalloc(p, 64, 2, 8, 24, p, p, p, p, None, None) == \
+        ops.QMOE_ERR_INVALID_ARG
+    assert L.qmoe_align_noalloc(p, 64, 9, 8, 16, p, p, p, p, None, None) == \
+        ops.QMOE_ERR_INVALID_ARG
+    assert L.qmoe_align_noalloc(None, 64, 2, 8, 16, p, p, p, p, None, None) == \
+        ops.QMOE_ERR_INVALID_ARG
+    assert L.qmoe_align_noalloc(p, 64, 2, 8, 16, None, p, p, p, None, None) == \
+        ops.QMOE_ERR_INVALID_ARG
+    assert L.qmoe_align_noalloc(p, 64, 2, 2000, 16, p, p, p, p, None, None) == \
+        ops.QMOE_ERR_UNSUPPORTED
+    # the limit is the workspace qmoe_align would need
+    assert L.qmoe_align_workspace(65024, 10, 1024) <= lim
+    big = (65025, 10, 1024)
+    assert L.qmoe_align_workspace(*big) > lim
+    assert L.qmoe_align_noalloc(p, big[0], big[1], big[2], 16, p, p, p, p, None, None) == \
+        ops.QMOE_ERR_UNSUPPORTED
 
 
 def _desc(**kw):
