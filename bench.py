@@ -2,8 +2,9 @@
 """Benchmark of the grouped, weight-quantized MoE FFN on one MI355X.
 
 A step is one pass of the whole layer on one batch of synthetic inputs that
-already sit in HBM: route (softmax top-k) -> align (group pairs by expert)
--> grouped FFN (stage 1 + requant + stage 2) -> combine.  Default workload:
+already sit in HBM: route (softmax top-k) and align (group pairs by expert),
+one launch up to 16 tokens -> grouped FFN (stage 1 + requant + stage 2) ->
+combine.  Default workload:
 fp8 activations x MXFP4 weights, hidden 4096, 512 experts, top-10, expert
 inter 1024, 4096 tokens (40960 (token, expert) rows).
 
@@ -169,7 +170,8 @@ def cpu_baseline(shape, inp, target_s: float = 15.0) -> dict:
             "tokens_per_s": total_tok / elapsed}
 
 
-SWEEP = ("w4a16_qwen3moe_t128", "w8a8_t2048", "a8w4_large@T16", "a8w4_large@T256",
+SWEEP = ("w4a16_qwen3moe_t128", "w8a8_t2048", "a8w4_large@T1", "a8w4_large@T4",
+         "a8w4_large@T16", "a8w4_large@T64", "a8w4_large@T256",
          "a8w4_large@T1024", "a8w4_large@T4096", "a8w4_large@T8192", "a8w4_tp2@T4096",
          "a8w4_tp4@T4096", "w4a16_skewed_t8192")
 
@@ -190,8 +192,7 @@ def graph_step_ms(torch, ops, args, flush, b: dict, eager_step):
     sh, g, E, k = b["shape"], b["g"], b["shape"].experts, b["shape"].topk
 
     def body():
-        ops.route(g["logits"], k, b["ids"], b["tw"])
-        ops.align(b["ids"], E, b["bm"], out=b["al"])
+        ops.route_align(g["logits"], k, b["bm"], b["ids"], b["tw"], out=b["al"])
         ops.grouped_ffn(sh.scheme, g["x"], g["x_scale"], b["W"], b["al"], E, k, ws=b["ws"],
                         y_pairs=b["y"])
         ops.combine(b["y"], b["tw"], out_bf16=b["out_bf16"], out_f32=b["out_f32"],
@@ -267,8 +268,7 @@ def run_workload(name: str, args, torch, with_cpu: bool, cpu_seconds: float = 20
     T, E, k, H = shape.tokens, shape.experts, shape.topk, shape.hidden
     ids = torch.empty((T, k), dtype=torch.int32, device=dev)
     tw = torch.empty((T, k), dtype=torch.float32, device=dev)
-    ops.route(g["logits"], k, ids, tw)
-    al = ops.align(ids, E, bm)
+    _, _, al = ops.route_align(g["logits"], k, bm, ids, tw)
     y, ws = ops.grouped_ffn(shape.scheme, g["x"], g["x_scale"], W, al, E, k)
     out_bf16, out_f32 = ops.combine(y, tw, want_bf16=True, want_f32=shape.scheme == "w8a8")
     torch.cuda.synchronize()
@@ -289,10 +289,9 @@ def run_workload(name: str, args, torch, with_cpu: bool, cpu_seconds: float = 20
             torch.amax(flush)
         if ev is not None:
             ev[0].record()
-        ops.route(g["logits"], k, ids, tw)
+        ops.route_align(g["logits"], k, bm, ids, tw, out=al)
         if ev is not None:
             ev[1].record()
-        ops.align(ids, E, bm, out=al)
         ops.grouped_ffn(shape.scheme, g["x"], g["x_scale"], W, al, E, k, ws=ws, y_pairs=y,
                         stage_events=None if ev is None else ev[2:6])
         ops.combine(y, tw, out_bf16=out_bf16, out_f32=out_f32, want_f32=out_f32 is not None)
@@ -323,7 +322,7 @@ def run_workload(name: str, args, torch, with_cpu: bool, cpu_seconds: float = 20
             shape=shape, g=g, W=W, ids=ids, tw=tw, al=al, y=y, ws=ws, bm=bm,
             out_bf16=out_bf16, out_f32=out_f32), lambda: step(0))
         ms_per_step = graph_ms
-    kern = {"route": per_step(0, 1).mean(), "align": per_step(1, 2).mean(),
+    kern = {"route_align": per_step(0, 1).mean(),
             "stage1": per_step(2, 3).mean(), "requant": per_step(3, 4).mean(),
             "stage2": per_step(4, 5).mean(), "combine": per_step(5, 6).mean(),
             "step_events": step_ms.mean()}
@@ -424,14 +423,12 @@ def tile_sweep(args, torch) -> None:
             for bm in TILE_SWEEP_BLOCKS:
                 ids = torch.empty((T, k), dtype=torch.int32, device=dev)
                 tw = torch.empty((T, k), dtype=torch.float32, device=dev)
-                ops.route(gt["logits"], k, ids, tw)
-                al = ops.align(ids, E, bm)
+                _, _, al = ops.route_align(gt["logits"], k, bm, ids, tw)
                 y, ws = ops.grouped_ffn(sh.scheme, gt["x"], gt["x_scale"], W, al, E, k)
                 out_bf16, _ = ops.combine(y, tw, want_bf16=True, want_f32=False)
 
                 def eager_step():
-                    ops.route(gt["logits"], k, ids, tw)
-                    ops.align(ids, E, bm, out=al)
+                    ops.route_align(gt["logits"], k, bm, ids, tw, out=al)
                     ops.grouped_ffn(sh.scheme, gt["x"], gt["x_scale"], W, al, E, k, ws=ws,
                                     y_pairs=y)
                     ops.combine(y, tw, out_bf16=out_bf16, out_f32=None, want_f32=False)

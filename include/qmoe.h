@@ -164,6 +164,22 @@ qmoe_status qmoe_align(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
                        int32_t block_m, int32_t* sorted_pair_ids, int32_t* tile_expert,
                        int32_t* expert_offsets, int32_t* num_padded, void* ws,
                        size_t ws_bytes, void* stream);
+/* ---------------------------------------------------------------------
+ * qmoe_route_align -- qmoe_route followed by qmoe_align, with the same
+ * outputs bit for bit (topk_ids, topk_w, and the grouping with its flag word
+ * in `ws`, qmoe_align_workspace(T,k,E) bytes, 256-byte aligned).  Up to 16
+ * tokens both steps run in one launch of one block, for the decode regime,
+ * where the number of dependent launches bounds the step (vLLM issue,
+ * section Problem: decode is bound by weight streaming and dispatch count;
+ * aiter PR 6090, section Changes: token bucket 1-256).  Larger batches take
+ * the two launches of the separate calls.  Requirements and errors are those
+ * of qmoe_route and qmoe_align together.                                  */
+qmoe_status qmoe_route_align(const float* logits, int32_t T, int32_t E, int32_t k,
+                             int32_t block_m, int32_t* topk_ids, float* topk_w,
+                             int32_t* sorted_pair_ids, int32_t* tile_expert,
+                             int32_t* expert_offsets, int32_t* num_padded, void* ws,
+                             size_t ws_bytes, void* stream);
+
 /* Copies the align flag word to host memory *flags_out (synchronises).  */
 qmoe_status qmoe_check_flags(const void* align_ws, int32_t* flags_out, void* stream);
 
@@ -221,8 +237,10 @@ qmoe_status qmoe_grouped_ffn(const qmoe_ffn_desc* d, const void* x, const float*
 
 /* Same as qmoe_grouped_ffn, and also records stage_events[0..3] (each a
  * hipEvent_t created by the caller) on the stream: before stage 1, after
- * stage 1, after the requantization of h (same point as after stage 1 for
- * W4A16), after stage 2.  For measuring each kernel inside a timed run.  */
+ * stage 1, after the separate requantization of h (the same point as after
+ * stage 1 where stage 2 quantizes h itself: W4A16, and the one-byte schemes
+ * with I <= 1024), after stage 2.  For measuring each kernel inside a
+ * timed run.                                                             */
 qmoe_status qmoe_grouped_ffn_profiled(const qmoe_ffn_desc* d, const void* x,
                                       const float* x_scale, const qmoe_weights* w,
                                       const int32_t* sorted_pair_ids,

@@ -22,6 +22,7 @@
 // (align_place_kernel): every block reads the whole count matrix and scans
 // it itself, so two launches remain.
 #include "qmoe_internal.h"
+#include "route_common.h"
 
 namespace qmoe {
 namespace {
@@ -233,11 +234,14 @@ __device__ inline int block_excl_scan(int v, int* s_wave) {
   return before + x - v;
 }
 
-__global__ __launch_bounds__(kSmallT) void align_small_kernel(
-    const int32_t* __restrict__ ids, int T, int k, int E, int bm_shift, int cap,
-    int32_t* __restrict__ sorted, int32_t* __restrict__ tile_expert,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ num_padded,
-    int32_t* __restrict__ flags) {
+// Body of the single-block align; getid(t, j) returns token t's j-th id.
+template <typename GetId>
+__device__ inline void align_small_body(GetId getid, int T, int k, int E, int bm_shift, int cap,
+                                        int32_t* __restrict__ sorted,
+                                        int32_t* __restrict__ tile_expert,
+                                        int32_t* __restrict__ offsets,
+                                        int32_t* __restrict__ num_padded,
+                                        int32_t* __restrict__ flags) {
   extern __shared__ unsigned long long mask[];  // [kSmallWaves][E]
   __shared__ int s_tot[kMaxExperts];
   __shared__ int s_off[kMaxExperts + 1];
@@ -252,7 +256,7 @@ __global__ __launch_bounds__(kSmallT) void align_small_kernel(
   constexpr int kRegK = 16;
   int te[kRegK];
 #pragma unroll
-  for (int j = 0; j < kRegK; j++) te[j] = mine && j < k ? ids[(size_t)tid * k + j] : -1;
+  for (int j = 0; j < kRegK; j++) te[j] = mine && j < k ? getid(tid, j) : -1;
   for (int i = tid; i < kSmallWaves * E; i += kSmallT) mask[i] = 0ull;
   __syncthreads();
   int bad = 0;
@@ -268,7 +272,7 @@ __global__ __launch_bounds__(kSmallT) void align_small_kernel(
   for (int j = 0; j < kRegK; j++)
     if (mine && j < k) set_bit(te[j]);
   for (int j = kRegK; j < k; j++)
-    if (mine) set_bit(ids[(size_t)tid * k + j]);
+    if (mine) set_bit(getid(tid, j));
   const int b1 = __syncthreads_or(bad & 1);
   const int b2 = __syncthreads_or(bad & 2);
   // Totals, one expert per thread (E <= 1024), and their padded prefix.
@@ -303,7 +307,7 @@ __global__ __launch_bounds__(kSmallT) void align_small_kernel(
   for (int j = 0; j < kRegK; j++)
     if (mine && j < k) place(te[j], j);
   for (int j = kRegK; j < k; j++)
-    if (mine) place(ids[(size_t)tid * k + j], j);
+    if (mine) place(getid(tid, j), j);
   // Sentinels and tile->expert entries: a group of block_m / 4 lanes (4 to
   // 32) per expert, so that an expert's at most block_m - 1 sentinels take
   // at most four stores per lane and a wave serves 64 / group experts at a
@@ -321,6 +325,49 @@ __global__ __launch_bounds__(kSmallT) void align_small_kernel(
   const int npad = s_off[E];
   for (int i = npad + tid; i < cap; i += kSmallT) sorted[i] = P;
   for (int i = (npad >> bm_shift) + tid; i < (cap >> bm_shift); i += kSmallT) tile_expert[i] = -1;
+}
+
+__global__ __launch_bounds__(kSmallT) void align_small_kernel(
+    const int32_t* __restrict__ ids, int T, int k, int E, int bm_shift, int cap,
+    int32_t* __restrict__ sorted, int32_t* __restrict__ tile_expert,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ num_padded,
+    int32_t* __restrict__ flags) {
+  align_small_body([&](int t, int j) { return ids[(size_t)t * k + j]; }, T, k, E, bm_shift, cap,
+                   sorted, tile_expert, offsets, num_padded, flags);
+}
+
+// Routing and grouping of a small batch in one launch (the decode regime,
+// where every launch of the step counts; vLLM issue, section Problem: decode
+// is bound by weight streaming and dispatch count).  Each of the 16 waves
+// routes one token (route_common.h), writes its ids and weights out and
+// keeps the ids in LDS; the block then groups them as align_small_kernel
+// does.  Up to 16 tokens: with more, each wave would route several tokens
+// one after the other (64 tokens measured 44 us, against ~22 us for the
+// routing kernel's one wave per token on many blocks followed by the
+// single-block align).
+constexpr int kRouteAlignMaxT = kSmallWaves;
+
+template <int EPL>
+__global__ __launch_bounds__(kSmallT) void route_align_small_kernel(
+    const float* __restrict__ logits, int T, int k, int E, int bm_shift, int cap,
+    int32_t* __restrict__ ids, float* __restrict__ wts, int32_t* __restrict__ sorted,
+    int32_t* __restrict__ tile_expert, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ num_padded, int32_t* __restrict__ flags) {
+  __shared__ int s_ids[kRouteAlignMaxT * 16];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int t = wave; t < T; t += kSmallWaves) {  // one token per wave (T <= 16)
+    int e;
+    float w;
+    rt::route_token<EPL>(logits + (size_t)t * E, E, k, &e, &w);
+    if (lane < k) {
+      ids[(size_t)t * k + lane] = e;
+      wts[(size_t)t * k + lane] = w;
+      s_ids[t * k + lane] = e;
+    }
+  }
+  __syncthreads();
+  align_small_body([&](int t, int j) { return s_ids[t * k + j]; }, T, k, E, bm_shift, cap,
+                   sorted, tile_expert, offsets, num_padded, flags);
 }
 
 // count + scan + scatter in two launches for nchunks <= kPlaceMaxChunks:
@@ -484,5 +531,31 @@ hipError_t launch_align(const int32_t* ids, int T, int k, int E, int block_m, in
 }
 
 size_t align_chunk_count(int T) { return (size_t)(T + kChunk - 1) / kChunk; }
+
+int route_align_fused_max_tokens() { return kRouteAlignMaxT; }
+
+hipError_t launch_route_align(const float* logits, int T, int E, int k, int block_m,
+                              int32_t* ids, float* w, int32_t* sorted, int32_t* tile_expert,
+                              int32_t* offsets, int32_t* num_padded, int32_t* flags, int cap,
+                              hipStream_t s) {
+  if (T < 1 || T > kRouteAlignMaxT || k > 16 || E > kMaxExperts) return hipErrorInvalidValue;
+  if (block_m < 16 || block_m > 128 || (block_m & (block_m - 1)) != 0) return hipErrorInvalidValue;
+  const int bm_shift = __builtin_ctz((unsigned)block_m);
+  const size_t lds_small = (size_t)kSmallWaves * E * sizeof(unsigned long long);
+#define QMOE_RA_CASE(EPL)                                                                   \
+  if (E <= 64 * EPL) {                                                                      \
+    hipLaunchKernelGGL(route_align_small_kernel<EPL>, dim3(1), dim3(kSmallT), lds_small, s, \
+                       logits, T, k, E, bm_shift, cap, ids, w, sorted, tile_expert, offsets, \
+                       num_padded, flags);                                                  \
+    return hipGetLastError();                                                               \
+  }
+  QMOE_RA_CASE(1)
+  QMOE_RA_CASE(2)
+  QMOE_RA_CASE(4)
+  QMOE_RA_CASE(8)
+  QMOE_RA_CASE(16)
+#undef QMOE_RA_CASE
+  return hipErrorInvalidValue;
+}
 
 }  // namespace qmoe

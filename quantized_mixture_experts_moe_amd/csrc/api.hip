@@ -36,6 +36,10 @@ int device_cu_count() {
 }
 
 static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Pairs up to which the resident stage 2 quantizes h itself (see
+// grouped_ffn_impl).
+constexpr int kFuseRequantPairs = 12288;
 static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 static bool valid_block_m(int bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128; }
 
@@ -66,10 +70,14 @@ static FfnWs ffn_ws_layout(const qmoe_ffn_desc& d) {
   w.h = off;
   off = align_up(off + cap * I * (d.scheme == QMOE_W4A16_G32 ? 2 : 4), 256);
   if (d.scheme != QMOE_W4A16_G32) {
-    w.hq = off;
-    off = align_up(off + cap * I, 256);
-    w.hs = off;
-    off = align_up(off + cap * 4, 256);
+    // The quantized h and its row scales are materialized unless the
+    // resident stage 2 quantizes while it copies.
+    if (!stage2_resident_ok(d.scheme, d.I) || (size_t)d.T * d.k > (size_t)kFuseRequantPairs) {
+      w.hq = off;
+      off = align_up(off + cap * I, 256);
+      w.hs = off;
+      off = align_up(off + cap * 4, 256);
+    }
     w.pmax = off;
     off = align_up(off + cap * (I / kMinStage1Cols) * 4, 256);
   }
@@ -179,6 +187,39 @@ qmoe_status qmoe_align(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
                                  reinterpret_cast<int32_t*>(w + lay.totals),
                                  reinterpret_cast<int32_t*>(w + lay.flags), cap,
                                  (hipStream_t)stream));
+}
+
+qmoe_status qmoe_route_align(const float* logits, int32_t T, int32_t E, int32_t k,
+                             int32_t block_m, int32_t* topk_ids, float* topk_w,
+                             int32_t* sorted_pair_ids, int32_t* tile_expert,
+                             int32_t* expert_offsets, int32_t* num_padded, void* ws,
+                             size_t ws_bytes, void* stream) {
+  if (T < 0 || E < 1 || k < 1 || k > E || k > 16 || !valid_block_m(block_m))
+    return QMOE_ERR_INVALID_ARG;
+  if (E > 1024) return QMOE_ERR_UNSUPPORTED;
+  if ((T > 0 && (!logits || !topk_ids || !topk_w)) || !sorted_pair_ids || !tile_expert ||
+      !expert_offsets || !num_padded || !ws)
+    return QMOE_ERR_INVALID_ARG;
+  const AlignWs lay = align_ws_layout(T, E);
+  if (ws_bytes < lay.total || !aligned(ws, 256)) return QMOE_ERR_INVALID_ARG;
+  const int cap = (int)qmoe_align_capacity(T, k, E, block_m);
+  uint8_t* w = reinterpret_cast<uint8_t*>(ws);
+  hipStream_t s = (hipStream_t)stream;
+  if (T >= 1 && T <= route_align_fused_max_tokens())
+    return hip_status(launch_route_align(logits, T, E, k, block_m, topk_ids, topk_w,
+                                         sorted_pair_ids, tile_expert, expert_offsets,
+                                         num_padded, reinterpret_cast<int32_t*>(w + lay.flags),
+                                         cap, s));
+  if (T > 0) {
+    const hipError_t e = launch_route(logits, T, E, k, topk_ids, topk_w, s);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  return hip_status(launch_align(topk_ids, T, k, E, block_m, sorted_pair_ids, tile_expert,
+                                 expert_offsets, num_padded,
+                                 reinterpret_cast<int32_t*>(w + lay.counts),
+                                 reinterpret_cast<int32_t*>(w + lay.chunk_flags),
+                                 reinterpret_cast<int32_t*>(w + lay.totals),
+                                 reinterpret_cast<int32_t*>(w + lay.flags), cap, s));
 }
 
 // ---------------------------------------------------------------------------
@@ -344,7 +385,15 @@ static qmoe_status grouped_ffn_impl(const qmoe_ffn_desc* d, const void* x, const
   if (e == hipSuccess) e = mark(1);
   if (e != hipSuccess) return hip_status(e);
 
-  if (quant_act) {
+  const bool resident = stage2_resident_ok(d->scheme, d->I);
+  // The resident stage 2 quantizes h itself while it copies each row tile
+  // into LDS (one launch and one pass over h fewer) up to kFuseRequantPairs
+  // pairs.  Beyond that its copy of fp32 rows, which no other block on the
+  // CU overlaps, cost more than the separate pass (measured: 4096 tokens of
+  // the a8w4 block, stage 2 334 -> 416 us against 54 us of requantization;
+  // at 256 and 1024 tokens the fused form is 6-8 us faster).
+  const bool fuse_requant = quant_act && resident && g1.P <= kFuseRequantPairs;
+  if (quant_act && !fuse_requant) {
     e = launch_requant(d->scheme, sorted_pair_ids, num_padded, g1.P, d->I, g1.ntiles_n, cap,
                        reinterpret_cast<const float*>(wsb + lay.h),
                        reinterpret_cast<const float*>(wsb + lay.pmax), wsb + lay.hq,
@@ -357,7 +406,6 @@ static qmoe_status grouped_ffn_impl(const qmoe_ffn_desc* d, const void* x, const
   g2.schedule = 0;
   g2.N = d->H;
   g2.K = d->I;
-  const bool resident = stage2_resident_ok(d->scheme, d->I);
   // Where stage 1 takes runs of row tiles (several 128-row tiles per
   // expert), stage 2 takes each tile as two 64-row work items.
   const bool half_tiles = resident && g1.schedule == 1;
@@ -376,12 +424,21 @@ static qmoe_status grouped_ffn_impl(const qmoe_ffn_desc* d, const void* x, const
   } else {
     g2.ntiles_n = d->H / stage_cols(2, gs2.nsub, gs2.waves);
   }
-  g2.a = quant_act ? (const void*)(wsb + lay.hq) : (const void*)(wsb + lay.h);
-  g2.a_scale = quant_act ? reinterpret_cast<const float*>(wsb + lay.hs) : nullptr;
+  if (fuse_requant) {
+    // fp32 h and the per-column-tile maxima; quantized in the row copy.
+    g2.a = wsb + lay.h;
+    g2.a_scale = nullptr;
+    g2.row_pmax = reinterpret_cast<float*>(wsb + lay.pmax);
+    g2.pmax_stride = g1.ntiles_n;
+  } else {
+    g2.a = quant_act ? (const void*)(wsb + lay.hq) : (const void*)(wsb + lay.h);
+    g2.a_scale = quant_act ? reinterpret_cast<const float*>(wsb + lay.hs) : nullptr;
+    g2.row_pmax = nullptr;
+    g2.pmax_stride = 0;
+  }
   g2.b = w->w2;
   g2.b_scale = w->w2_scale;
   g2.out = y_pairs;
-  g2.row_pmax = nullptr;
   g2.dump = dump ? reinterpret_cast<int32_t*>(wsb + lay.acc2) : nullptr;
   e = resident ? launch_stage2_resident(d->scheme, d->block_m, half_tiles, packed, g2, passes, s)
                : launch_gemm(d->scheme, 2, d->block_m, packed, gs2.nsub, gs2.waves, g2, s);

@@ -2,14 +2,17 @@
 // rows resident in LDS (aiter PR 6090, Test Plan: stage2 tiles; hip-ep PR
 // "perf(qmoe): group prefill expert matmuls": one launch for every expert).
 //
-//   y_pairs[pair(row)] = h[row] . W2[e]^T,  rescaled by the row's h scale
+//   y_pairs[pair(row)] = hq[row] . W2[e]^T * s_h[row]
 //
 // For the schemes whose stage-2 activations are one byte (a8w4 fp8, W8A8
-// int8), a row tile's h rows (BM x I bytes, I <= 1024) fit in LDS.  A work
-// item is (row tile, chunk of `passes` column passes of 256 outputs): the
-// block copies the rows into LDS once, then streams the expert's W2 rows for
-// every pass of the chunk through a register ring that runs three K steps
-// ahead across pass boundaries.  No barrier is needed between steps (the
+// int8), a row tile's quantized h rows (BM x I bytes, I <= 1024) fit in
+// LDS.  A work item is (row tile, chunk of `passes` column passes of 256
+// outputs): the block takes each row's scale s_h from the |h| maxima stage 1
+// wrote per column tile, reads the tile's fp32 h rows once, quantizes them
+// (the recipe of quant_common.h, the same codes a separate requantization
+// pass gives) straight into LDS, then streams the expert's W2 rows for every
+// pass of the chunk through a register ring that runs three K steps ahead
+// across pass boundaries.  No barrier is needed between steps (the
 // activations are read-only), and no activation row is loaded again.
 //
 // One block = 8 waves (two per SIMD), one block per CU; each wave owns two
@@ -21,6 +24,7 @@
 // fp4/fp8 pairing and the per-lane e8m0 scale routing do not depend on which
 // operand slot holds which format).
 #include "gemm_common.h"
+#include "quant_common.h"
 
 namespace qmoe {
 namespace {
@@ -83,7 +87,8 @@ moe_stage2_resident(GemmArgs g, int passes, int tile_div) {
   constexpr int NF = T_::A_FRAG / 16;
   __shared__ __attribute__((aligned(16))) uint8_t sA[BM * kS2Pitch];
   __shared__ __attribute__((aligned(16))) int sRow[BM];
-  __shared__ __attribute__((aligned(16))) float sScale[BM];
+  __shared__ __attribute__((aligned(16))) float sScale[BM];  // s_h of each row
+  __shared__ __attribute__((aligned(16))) float sRcp[BM];    // RN(1 / s_h)
   __shared__ int sExpert;
   // W8A8: the item's per-channel weight scales (its columns are one
   // contiguous range of passes * kS2Cols), copied at the item's start so
@@ -106,6 +111,9 @@ moe_stage2_resident(GemmArgs g, int passes, int tile_div) {
   const int chunk = (total + 7) >> 3;
   const int w_begin = xcd * chunk, w_end = min(total, w_begin + chunk);
   const uint8_t* __restrict__ Aglob = reinterpret_cast<const uint8_t*>(g.a);
+  // Fused quantization: g.a is stage 1's fp32 h and g.row_pmax its |h|
+  // maxima; otherwise g.a holds the codes and g.a_scale the row scales.
+  const bool fused = g.row_pmax != nullptr;
   const uint8_t* __restrict__ B = reinterpret_cast<const uint8_t*>(g.b);
   const uint32_t sshift = ((PK ? lane : lq) & 1) * 16;
   constexpr uint32_t B_KS = PK ? 16 * T_::B_STEP : T_::B_STEP;
@@ -126,7 +134,16 @@ moe_stage2_resident(GemmArgs g, int passes, int tile_div) {
       const int p = g.sorted_pair_ids[mt * BM + tid];
       const bool ok = p < g.P;
       sRow[tid] = ok ? p : -1;
-      sScale[tid] = ok ? g.a_scale[(size_t)mt * BM + tid] : 0.f;
+      // Row scale: the row's |h| max over stage 1's column tiles (fused
+      // quantization), or the scale the requantization pass wrote.
+      float a = 0.f;
+      if (ok && fused) {
+        const float* pm = g.row_pmax + ((size_t)mt * BM + tid) * g.pmax_stride;
+        for (int i = 0; i < g.pmax_stride; i++) a = fmaxf(a, pm[i]);
+      }
+      const float sh = fused ? rq::row_scale<S == kA8W4>(a) : 1.0f;
+      sScale[tid] = ok ? (fused ? sh : g.a_scale[(size_t)mt * BM + tid]) : 0.f;
+      sRcp[tid] = ok ? 1.0f / sh : 0.f;
       valid_here = ok;
     }
     if (tid == kS2Threads - 1) sExpert = g.tile_expert[mt / tile_div];
@@ -174,30 +191,69 @@ moe_stage2_resident(GemmArgs g, int passes, int tile_div) {
     load_b(b1, 1);
     load_b(b2, 2);
 
-    // The tile's activation rows (real rows and the rest of their 16-row
-    // group; those extra rows only feed discarded outputs) into LDS, eight
-    // 16-byte loads per thread in flight at a time.
-    {
+    // The tile's h rows into LDS as codes.  Fused quantization: a thread
+    // takes 16 consecutive values of a row (four 16-byte loads of fp32 h),
+    // quantizes them with the row's scale and writes one 16-byte piece of
+    // codes; kBatch pieces per thread are loaded before any is quantized.
+    // Otherwise the requantization pass's codes are copied, eight 16-byte
+    // pieces per thread in flight.  Rows past the tile's last real row, to
+    // the end of its 16-row group, only feed discarded outputs and are
+    // written as zeros.
+    if (!fused) {
       constexpr int kBatch = 8;
-      const int cpr = K * T_::A_ELEM / 16;  // 16-byte chunks per row
+      const int cpr = K / 16;  // 16-byte pieces per row
       const int n = mvalid * 16 * cpr;
       for (int i0 = tid; i0 < n; i0 += kBatch * kS2Threads) {
         u32x4 v[kBatch];
 #pragma unroll
         for (int j = 0; j < kBatch; j++) {
           const int i = i0 + j * kS2Threads;
-          if (i < n) {
-            const int r = i / cpr, cc = i - r * cpr;
-            v[j] = *reinterpret_cast<const u32x4*>(
-                Aglob + ((size_t)mt * BM + r) * (size_t)(K * T_::A_ELEM) + cc * 16);
+          const int r = i / cpr, cc = i - r * cpr;
+          v[j] = u32x4{0u, 0u, 0u, 0u};
+          if (i < n && r < nvalid)
+            v[j] = *reinterpret_cast<const u32x4*>(Aglob + ((size_t)mt * BM + r) * (size_t)K +
+                                                   cc * 16);
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; j++) {
+          const int i = i0 + j * kS2Threads;
+          const int r = i / cpr, cc = i - r * cpr;
+          if (i < n) *reinterpret_cast<u32x4*>(sA + r * kS2Pitch + cc * 16) = v[j];
+        }
+      }
+    } else {
+      constexpr int kBatch = 2;
+      const int cpr = K / 16;  // 16-value pieces per row
+      const int n = mvalid * 16 * cpr;
+      const float* __restrict__ H32 = reinterpret_cast<const float*>(Aglob);
+      for (int i0 = tid; i0 < n; i0 += kBatch * kS2Threads) {
+        f32x4 v[kBatch][4];
+#pragma unroll
+        for (int j = 0; j < kBatch; j++) {
+          const int i = i0 + j * kS2Threads;
+          const int r = i / cpr, cc = i - r * cpr;
+          if (i < n && r < nvalid) {
+            const f32x4* src =
+                reinterpret_cast<const f32x4*>(H32 + ((size_t)mt * BM + r) * K + cc * 16);
+#pragma unroll
+            for (int u = 0; u < 4; u++) v[j][u] = __builtin_nontemporal_load(src + u);
           }
         }
 #pragma unroll
         for (int j = 0; j < kBatch; j++) {
           const int i = i0 + j * kS2Threads;
+          const int r = i / cpr, cc = i - r * cpr;
           if (i < n) {
-            const int r = i / cpr, cc = i - r * cpr;
-            *reinterpret_cast<u32x4*>(sA + r * kS2Pitch + cc * 16) = v[j];
+            u32x4 q = {0u, 0u, 0u, 0u};
+            if (r < nvalid) {
+              const float sh = sScale[r], rc = sRcp[r];
+              const bool refine = sh >= 0x1p-60f;
+#pragma unroll
+              for (int u = 0; u < 4; u++)
+                q[u] = rq::quant4<S == kA8W4>(v[j][u][0], v[j][u][1], v[j][u][2], v[j][u][3], sh,
+                                              rc, refine);
+            }
+            *reinterpret_cast<u32x4*>(sA + r * kS2Pitch + cc * 16) = q;
           }
         }
       }

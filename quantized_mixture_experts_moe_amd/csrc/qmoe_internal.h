@@ -35,7 +35,9 @@ struct GemmArgs {
   const void* b;         // weight codes [E, N, K(/2)]
   const void* b_scale;   // weight scales
   void* out;             // stage 1: h (bf16 or f32) [cap, I]; stage 2: y_pairs [P, H]
-  float* row_pmax;       // stage 1 (w8a8/a8w4): |h| max per row and column tile
+  float* row_pmax;       // stage 1 (w8a8/a8w4): |h| max per row and column tile, written;
+                         // resident stage 2: read, to quantize h while copying it
+  int pmax_stride;       // column tiles of stage 1 (row pitch of row_pmax)
   int32_t* dump;         // w8a8 debug accumulators or nullptr
   int schedule;          // stage-1 work order: 0 strided items, 1 runs of row tiles
 };
@@ -51,7 +53,9 @@ hipError_t launch_gemm(int scheme, int stage, int block_m, bool packed, int nsub
 // Stage 2 with the tile's activation rows resident in LDS (gemm_s2.hip):
 // available for the one-byte-activation schemes with I <= 1024; its column
 // passes are stage2_resident_cols() wide and a work item covers `passes`
-// of them (ntiles_n must be a multiple of passes).
+// of them (ntiles_n must be a multiple of passes).  It reads stage 1's fp32
+// h (g.a) and per-column-tile |h| maxima (g.row_pmax, g.pmax_stride) and
+// quantizes each row as it copies it into LDS (no separate requant pass).
 bool stage2_resident_ok(int scheme, int I);
 int stage2_resident_cols();
 int stage2_resident_max_passes(int scheme);  // bound on passes per work item
@@ -68,6 +72,13 @@ hipError_t launch_combine(const void* y, int y_f32, const float* w, int T, int k
                           uint16_t* out_bf16, float* out_f32, hipStream_t s);
 
 size_t align_chunk_count(int T);
+// Routing + grouping of up to route_align_fused_max_tokens() tokens in one
+// launch of one block (align.hip).
+int route_align_fused_max_tokens();
+hipError_t launch_route_align(const float* logits, int T, int E, int k, int block_m,
+                              int32_t* ids, float* w, int32_t* sorted, int32_t* tile_expert,
+                              int32_t* offsets, int32_t* num_padded, int32_t* flags, int cap,
+                              hipStream_t s);
 int device_cu_count();
 
 }  // namespace qmoe

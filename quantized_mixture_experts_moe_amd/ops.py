@@ -28,7 +28,7 @@ ABI_VERSION = 3
 EXPORTS = (
     "qmoe_abi_version", "qmoe_status_str", "qmoe_last_hip_error", "qmoe_route",
     "qmoe_align_capacity", "qmoe_align_workspace", "qmoe_align", "qmoe_check_flags",
-    "qmoe_align_noalloc",
+    "qmoe_align_noalloc", "qmoe_route_align",
     "qmoe_grouped_ffn_workspace", "qmoe_grouped_ffn_debug_offsets", "qmoe_grouped_ffn",
     "qmoe_grouped_ffn_profiled", "qmoe_combine", "qmoe_prepack",
 )
@@ -78,6 +78,8 @@ def _lib() -> ctypes.CDLL:
     L.qmoe_align_workspace.argtypes = [i32, i32, i32]
     L.qmoe_align.restype = ctypes.c_int
     L.qmoe_align.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+    L.qmoe_route_align.restype = ctypes.c_int
+    L.qmoe_route_align.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.qmoe_align_noalloc.restype = ctypes.c_int
     L.qmoe_align_noalloc.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]
     L.qmoe_check_flags.restype = ctypes.c_int
@@ -182,6 +184,38 @@ def align(topk_ids: torch.Tensor, E: int, block_m: int, ws: Optional[torch.Tenso
                              _ptr(out["num_padded"]), _ptr(ws), ws.numel(), _stream(dev)),
            "qmoe_align")
     return out
+
+
+def route_align(logits: torch.Tensor, k: int, block_m: int, ids=None, w=None,
+                out: Optional[dict] = None):
+    """qmoe_route_align: (topk_ids, topk_w, grouping dict) in one call (one
+    launch up to 16 tokens); ``out`` reuses a previous grouping's buffers."""
+    T, E = logits.shape
+    assert logits.dtype == torch.float32
+    dev = logits.device
+    if ids is None:
+        ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if w is None:
+        w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    cap = align_capacity(T, k, E, block_m)
+    if out is None:
+        out = {
+            "sorted_pair_ids": torch.empty(cap, dtype=torch.int32, device=dev),
+            "tile_expert": torch.empty(cap // block_m, dtype=torch.int32, device=dev),
+            "expert_offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
+            "num_padded": torch.empty(1, dtype=torch.int32, device=dev),
+            "block_m": block_m,
+        }
+    need = align_workspace(T, k, E)
+    ws = out.get("ws")
+    if ws is None or ws.numel() < need:
+        ws = _ws(need, dev)
+    out["ws"] = ws
+    _check(_lib().qmoe_route_align(_ptr(logits), T, E, k, block_m, _ptr(ids), _ptr(w),
+                                   _ptr(out["sorted_pair_ids"]), _ptr(out["tile_expert"]),
+                                   _ptr(out["expert_offsets"]), _ptr(out["num_padded"]),
+                                   _ptr(ws), ws.numel(), _stream(dev)), "qmoe_route_align")
+    return ids, w, out
 
 
 def align_noalloc(topk_ids: torch.Tensor, E: int, block_m: int, out: Optional[dict] = None,
@@ -310,11 +344,15 @@ def combine(y_pairs: torch.Tensor, topk_w: torch.Tensor, want_bf16: bool = True,
 
 def moe_forward(scheme: str, logits: torch.Tensor, x: torch.Tensor,
                 x_scale: Optional[torch.Tensor], weights: dict, k: int, block_m: int,
-                flags: int = 0, want_f32: bool = False) -> dict:
-    """route -> align -> grouped_ffn -> combine, all on the current stream."""
+                flags: int = 0, want_f32: bool = False, fused_routing: bool = False) -> dict:
+    """route -> align -> grouped_ffn -> combine, all on the current stream
+    (``fused_routing``: route and align through qmoe_route_align)."""
     E = logits.shape[1]
-    ids, w = route(logits, k)
-    al = align(ids, E, block_m)
+    if fused_routing:
+        ids, w, al = route_align(logits, k, block_m)
+    else:
+        ids, w = route(logits, k)
+        al = align(ids, E, block_m)
     y, ws = grouped_ffn(scheme, x, x_scale, weights, al, E, k, flags=flags)
     out_bf16, out_f32 = combine(y, w, want_bf16=True, want_f32=want_f32)
     return {"topk_ids": ids, "topk_w": w, "align": al, "y_pairs": y, "ws": ws,

@@ -80,6 +80,29 @@ def test_align_validation():
     assert L.qmoe_check_flags(None, None, None) == ops.QMOE_ERR_INVALID_ARG
 
 
+def test_route_align_validation():
+    """qmoe_route_align checks what qmoe_route and qmoe_align check."""
+    L = ops.lib()
+    p = ctypes.c_void_p(0x1000)
+    ws = L.qmoe_align_workspace(16, 4, 64)
+    ok = dict(T=16, E=64, k=4, bm=16)
+
+    def call(T=16, E=64, k=4, bm=16, logits=p, ids=p, w=p, srt=p, wsp=p, wsb=ws):
+        return L.qmoe_route_align(logits, T, E, k, bm, ids, w, srt, p, p, p, wsp, wsb, None)
+    assert call(bm=24) == ops.QMOE_ERR_INVALID_ARG
+    assert call(k=17, E=64) == ops.QMOE_ERR_INVALID_ARG
+    assert call(k=65) == ops.QMOE_ERR_INVALID_ARG
+    assert call(T=-1) == ops.QMOE_ERR_INVALID_ARG
+    assert call(logits=None) == ops.QMOE_ERR_INVALID_ARG
+    assert call(w=None) == ops.QMOE_ERR_INVALID_ARG
+    assert call(srt=None) == ops.QMOE_ERR_INVALID_ARG
+    assert call(wsp=None) == ops.QMOE_ERR_INVALID_ARG
+    assert call(wsb=ws - 1) == ops.QMOE_ERR_INVALID_ARG
+    assert call(wsp=ctypes.c_void_p(0x1010)) == ops.QMOE_ERR_INVALID_ARG  # not 256-aligned
+    assert call(E=2000, wsb=1 << 30) == ops.QMOE_ERR_UNSUPPORTED
+    assert ok
+
+
 def test_align_noalloc_validation():
     """The no-allocation align refuses bad arguments like qmoe_align, and
     sizes whose workspace exceeds its static array, before touching the

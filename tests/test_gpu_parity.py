@@ -126,6 +126,34 @@ def test_align_empty_and_out_of_range():
     assert ops.check_flags(al["ws"]) == 2
 
 
+@pytest.mark.parametrize("T,E,k,bm", [(1, 512, 10, 16), (4, 512, 10, 16), (16, 128, 8, 16),
+                                      (16, 1024, 16, 128), (7, 3, 3, 32), (1, 1, 1, 16),
+                                      (17, 64, 4, 64), (64, 512, 10, 16), (300, 512, 10, 16)])
+def test_route_align_matches_route_then_align(T, E, k, bm):
+    """qmoe_route_align (one launch up to 16 tokens, two above) gives
+    qmoe_route's and qmoe_align's outputs bit for bit, and the oracle's."""
+    _flush(f"route_align T={T} E={E} k={k} bm={bm}")
+    rng = np.random.default_rng(T * 13 + E + k)
+    L = rng.standard_normal((T, E)).astype(np.float32)
+    if E > 5:
+        L[:, 5] = L[:, 3]  # ties
+    if T > 2:
+        L[1] = 0.25  # a fully tied row
+    lg = to_gpu(L)
+    ids, w, al = ops.route_align(lg, k, bm)
+    ids2, w2 = ops.route(lg, k)
+    al2 = ops.align(ids2, E, bm)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids2) and torch.equal(w, w2)
+    for key in ("sorted_pair_ids", "tile_expert", "expert_offsets", "num_padded"):
+        assert torch.equal(al[key], al2[key]), key
+    ids_o, w_o = O.route(L, k)
+    np.testing.assert_array_equal(ids.cpu().numpy(), ids_o)
+    np.testing.assert_allclose(w.cpu().numpy(), w_o, rtol=2.0 ** -23, atol=0)
+    _check_align(al, ids_o, E, bm)
+    assert ops.check_flags(al["ws"]) == 0
+
+
 # ------------------------------------------------------------------ combine
 
 @pytest.mark.parametrize("T,k,H,f32", [(64, 2, 256, False), (2048, 8, 2048, True),
@@ -147,14 +175,14 @@ def test_combine_matches_oracle(T, k, H, f32):
 
 # ------------------------------------------------------------------ full layer
 
-def _run_gpu(shape, inp, bm=None, flags=0, prepacked=False):
+def _run_gpu(shape, inp, bm=None, flags=0, prepacked=False, fused_routing=False):
     g = gpu_inputs(inp)
     W = {k: g[k] for k in WEIGHT_KEYS}
     if prepacked:
         W = ops.prepack_weights(shape.scheme, W)
     r = ops.moe_forward(shape.scheme, g["logits"], g["x"], g["x_scale"], W, shape.topk,
                         bm or default_block_m(shape), flags=flags,
-                        want_f32=shape.scheme == "w8a8")
+                        want_f32=shape.scheme == "w8a8", fused_routing=fused_routing)
     torch.cuda.synchronize()
     return r
 
@@ -416,16 +444,17 @@ def _large_reference(base):
     return _REF_CACHE[base.name]
 
 
-def _parity_large(base, T, prepacked):
+def _parity_large(base, T, prepacked, fused_routing=False):
     full, inp, ids_o, w_o, y_ref = _large_reference(base)
     sh = full.with_tokens(T)
     bm = default_block_m(sh)
-    case = f"{sh.name} bm={bm} {'prepacked' if prepacked else 'canonical'}"
+    case = (f"{sh.name} bm={bm} {'prepacked' if prepacked else 'canonical'}"
+            + (" fused routing" if fused_routing else ""))
     _flush(f"ffn full {case}")
     inp_t = dict(inp)
     for key in ("logits", "x", "x_scale"):
         inp_t[key] = None if inp[key] is None else np.ascontiguousarray(inp[key][:T])
-    r = _run_gpu(sh, inp_t, bm, 0, prepacked)
+    r = _run_gpu(sh, inp_t, bm, 0, prepacked, fused_routing)
     P = T * sh.topk
     ref = O.combine(sh.scheme, y_ref[:P], w_o[:T])
     ref["y_pairs"] = y_ref[:P]
@@ -442,9 +471,26 @@ def test_a8w4_large_every_token(T, prepacked):
     _parity_large(A8W4_LARGE, T, prepacked)
 
 
+# Decode buckets (aiter PR 6090, section Changes: token bucket 1-256; vLLM
+# issue, section Problem: decode is M = 1 per expert): each scheme's block
+# at 1-256 tokens through qmoe_route_align, on every output element.  The
+# W4A16 and W8A8 blocks (hidden 2048, 128 experts, top-8, inter 768) draw
+# 2048 tokens, the a8w4 block 8192; a bucket takes the leading tokens.
+W4A16_DECODE = MoEShape("w4a16_qwen3moe", "w4a16", tokens=128, hidden=2048, inter=768,
+                        experts=128, topk=8, seed=1001, tokens_drawn=2048)
+
+
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("share", [A8W4_TP2, A8W4_TP4], ids=["tp2", "tp4"])
+@pytest.mark.parametrize("T", [1, 4, 16, 64, 256])
+@pytest.mark.parametrize("base", [A8W4_LARGE, W8A8_T2048, W4A16_DECODE],
+                         ids=["a8w4", "w8a8", "w4a16"])
+def test_decode_buckets_every_token(base, T):
+    _parity_large(base, T, True, fused_routing=True)
+
+
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("T", [4096, 8192])
+@pytest.mark.parametrize("share", [A8W4_TP2, A8W4_TP4], ids=["tp2", "tp4"])
 def test_a8w4_tensor_parallel_shares_every_token(share, T):
     """One GPU's share of the block under two- and four-way tensor
     parallelism (inter 512, 256) at the two largest token buckets."""
