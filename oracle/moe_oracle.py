@@ -30,6 +30,11 @@ What is computed, step by step:
    order with no atomics (hip-ep PR, description: deterministic scatter order).
 
 Schemes: ``w4a16`` (exact fp64 arithmetic on the dequantized int4 weights),
+``w4a8`` (int4 weights upconverted for an integer product with int8
+activations: exact integer sums per 32-wide group, the group scales applied
+after them, exact in fp64; the int8 requantization of h decided in fp32 as
+for w8a8; vLLM issue, section Constraint: W4A8 with the weights upconverted
+to 8 bits before the integer MMA),
 ``w8a8`` (exact integer accumulators; a fixed fp32 recipe for the rescales,
 the SiLU and the requantization so the integer results can be compared bit
 for bit), ``a8w4`` (the fp8 x e2m1 x 2^s products are exact in fp64 at these
@@ -315,6 +320,50 @@ def expert_a8w4(xq, sx, w13, s13, w2, s2) -> dict:
     return {"acc1": acc1, "gu": gu, "h": h, "hq": hq, "h_scale": sh, "acc2": acc2, "y": y}
 
 
+def group_sums_int4(xq: np.ndarray, codes: np.ndarray) -> np.ndarray:
+    """Exact integer dot products of int8 rows with int4 weight rows, one per
+    32-wide group along K: ``acc[p, n, g] = sum_{c in group g} xq[p, c] *
+    q[n, c]`` (fp64 products of integers below 2^53 are exact)."""
+    x = np.asarray(xq, f64)
+    q = int4_values(codes).astype(f64)
+    P, K = x.shape
+    N = q.shape[0]
+    G = K // 32
+    acc = np.empty((P, N, G), np.int64)
+    for g in range(G):
+        acc[:, :, g] = np.rint(x[:, 32 * g:32 * g + 32] @ q[:, 32 * g:32 * g + 32].T)
+    return acc
+
+
+def apply_group_scales(acc: np.ndarray, scales: np.ndarray, s_row: np.ndarray) -> np.ndarray:
+    """``s_row[p] * sum_g s[n, g] * acc[p, n, g]`` in fp64: the group scales
+    multiply the exact integer group sums.  The sum over groups is exact
+    here: with fp16 scales in [2^-8, 2^-5) and |acc| < 2^15 every product is
+    a multiple of 2^-18 below 2^10, and a sum of up to 128 of them stays
+    below 2^17 (35 bits); the product with the fp32 row scale is then the
+    one rounding (to fp64)."""
+    sc = np.asarray(scales).astype(f64)  # [N, G]
+    dot = np.einsum("png,ng->pn", acc.astype(f64), sc)
+    return dot * np.asarray(s_row, f64)[:, None]
+
+
+def expert_w4a8(xq, sx, w13, s13, w2, s2) -> dict:
+    """int4 weights (fp16 scale per 32 along K) x int8 per-token activations.
+
+    Integer group sums, group scales applied after them, the per-token
+    scale last; gu rounded to fp32, then the fp32 SiLU recipe and the
+    per-row int8 requantization of W8A8 (the scheme's activation format);
+    stage 2 the same way with the row scale of h."""
+    inter = w13.shape[0] // 2
+    acc1 = group_sums_int4(xq, w13)
+    gu = apply_group_scales(acc1, s13, sx).astype(f32)
+    h = silu_mul_f32(gu, inter)
+    hq, sh = quant_rows_int8(h)
+    acc2 = group_sums_int4(hq, w2)
+    y = apply_group_scales(acc2, s2, sh)
+    return {"acc1": acc1, "gu": gu, "h": h, "hq": hq, "h_scale": sh, "acc2": acc2, "y": y}
+
+
 def expert_ffn(scheme: str, x_rows, xs_rows, wts: dict) -> dict:
     if scheme == "w4a16":
         return expert_w4a16(x_rows, wts["w13"], wts["w13_scale"], wts["w2"], wts["w2_scale"])
@@ -323,6 +372,9 @@ def expert_ffn(scheme: str, x_rows, xs_rows, wts: dict) -> dict:
                            wts["w2_scale"])
     if scheme == "a8w4":
         return expert_a8w4(x_rows, xs_rows, wts["w13"], wts["w13_scale"], wts["w2"],
+                           wts["w2_scale"])
+    if scheme == "w4a8":
+        return expert_w4a8(x_rows, xs_rows, wts["w13"], wts["w13_scale"], wts["w2"],
                            wts["w2_scale"])
     raise ValueError(scheme)
 
@@ -410,6 +462,7 @@ __all__ = [
     "bf16_bits_to_f64", "round_to_bf16", "bf16_bits_from_value", "int4_values",
     "E2M1_TABLE", "e2m1_values", "e8m0_values", "E4M3_TABLE", "e4m3_values", "e4m3_encode",
     "route", "align", "quant_rows_int8", "quant_rows_e4m3", "silu_mul_f32", "dequant_int4_g32",
-    "dequant_mxfp4", "rescale_w8a8", "expert_w4a16", "expert_w8a8",
+    "dequant_mxfp4", "rescale_w8a8", "group_sums_int4", "apply_group_scales", "expert_w4a16",
+    "expert_w8a8", "expert_w4a8",
     "expert_a8w4", "expert_ffn", "combine", "moe_forward", "rel_l2",
 ]

@@ -15,15 +15,19 @@ are the three lowerings the pages discuss:
   with one e8m0 scale per 32 along K) weights (aiter PR 6090, sections
   Motivation and Changes: model_dim 4096, 512 experts, topk 10, fp8 act,
   MXFP4 weight, inter_dim 1024).
+* ``w4a8`` -- the int4 group-32 weights of w4a16 with the int8 per-token
+  activations of w8a8, upconverted to 8 bits for an integer product (vLLM
+  issue, section Constraint: W4A8 with upconversion of weights to IU8
+  before the MMA).
 """
 from __future__ import annotations
 
 from dataclasses import dataclass, replace
 from typing import Optional
 
-SCHEMES = ("w4a16", "w8a8", "a8w4")
+SCHEMES = ("w4a16", "w8a8", "a8w4", "w4a8")
 # Numeric codes shared with the C ABI (qmoe_scheme in include/qmoe.h).
-SCHEME_CODE = {"w4a16": 0, "w8a8": 1, "a8w4": 2}
+SCHEME_CODE = {"w4a16": 0, "w8a8": 1, "a8w4": 2, "w4a8": 3}
 
 
 @dataclass(frozen=True)
@@ -87,8 +91,18 @@ A8W4_TP4 = MoEShape("a8w4_tp4@T4096", "a8w4", tokens=4096, hidden=4096, inter=25
 W4A16_SKEWED = MoEShape("w4a16_skewed_t8192", "w4a16", tokens=8192, hidden=4096,
                         inter=1024, experts=512, topk=10, seed=1004, zipf_s=1.2)
 
+# W4A8 on the Qwen3-MoE-style block (128 and 2048 tokens) and on the skewed
+# long prefill.
+W4A8_QWEN3MOE = MoEShape("w4a8_qwen3moe_t128", "w4a8", tokens=128, hidden=2048, inter=768,
+                         experts=128, topk=8, seed=1007, tokens_drawn=2048)
+W4A8_T2048 = MoEShape("w4a8_t2048", "w4a8", tokens=2048, hidden=2048, inter=768, experts=128,
+                      topk=8, seed=1007)
+W4A8_SKEWED = MoEShape("w4a8_skewed_t8192", "w4a8", tokens=8192, hidden=4096, inter=1024,
+                       experts=512, topk=10, seed=1008, zipf_s=1.2)
+
 ALL_SHAPES = {s.name: s for s in (W4A16_TINY, W4A16_QWEN3MOE, W8A8_T2048, A8W4_LARGE,
-                                  A8W4_TP2, A8W4_TP4, W4A16_SKEWED)}
+                                  A8W4_TP2, A8W4_TP4, W4A16_SKEWED, W4A8_QWEN3MOE, W4A8_T2048,
+                                  W4A8_SKEWED)}
 
 
 def shape_by_name(name: str) -> MoEShape:

@@ -10,14 +10,14 @@ Canonical layouts (row-major, K contiguous):
 * ``logits``  fp32 ``[T, E]``: N(0,1), plus ``log p(r)`` with
   ``p(r) ~ r^-s`` over expert rank ``r = e + 1`` when a Zipf bias is set.
 * ``x``: w4a16 -> bf16 bits (uint16) ``[T, H]`` from N(0,1);
-  w8a8 -> int8 ``[T, H]`` + fp32 ``x_scale [T]``; a8w4 -> OCP e4m3 codes
+  w8a8 and w4a8 -> int8 ``[T, H]`` + fp32 ``x_scale [T]``; a8w4 -> OCP e4m3 codes
   (uint8) ``[T, H]`` + fp32 ``x_scale [T]``.  The quantized activations come
   from the same bf16 N(0,1) source, quantized per token as
   ``s = absmax / qmax`` (qmax 127 or 448), round-half-even, saturating.
 * ``w13`` ``[E, 2I, H]`` (rows 0..I-1 gate, I..2I-1 up) and ``w2 [E, H, I]``:
-  w4a16 -> two's-complement int4 packed two per byte, low nibble = even K
-  (uniform bytes = independent uniform codes in [-8, 7]), fp16 scales
-  ``[E, N, K/32]`` uniform in [0.005, 0.02];
+  w4a16 and w4a8 -> two's-complement int4 packed two per byte, low nibble =
+  even K (uniform bytes = independent uniform codes in [-8, 7]), fp16
+  scales ``[E, N, K/32]`` uniform in [0.005, 0.02];
   w8a8 -> int8 per output channel from N(0, 1/K) masters, fp32 scales ``[E, N]``;
   a8w4 -> e2m1 codes packed the same way (uniform over the 16 codes), e8m0
   scale bytes ``[E, N, K/32]`` uniform over {120, 121, 122} (2^-7..2^-5).
@@ -75,11 +75,12 @@ def activations(shape: MoEShape):
     if shape.scheme == "w4a16":
         return bits, None
     xf = torch.from_numpy(_bf16_bits_to_f32(bits))
-    qmax = 127.0 if shape.scheme == "w8a8" else 448.0
+    int8 = shape.scheme in ("w8a8", "w4a8")
+    qmax = 127.0 if int8 else 448.0
     amax = xf.abs().amax(dim=1)
     s = torch.where(amax > 0, amax / qmax, torch.ones_like(amax))
     v = xf / s[:, None]
-    if shape.scheme == "w8a8":
+    if int8:
         q = torch.clamp(torch.round(v), -127, 127).to(torch.int8).numpy()
     else:
         v = torch.clamp(v, -448.0, 448.0)
@@ -93,7 +94,7 @@ def _packed_codes(shape: MoEShape, stream: int, e: int, n: int, kdim: int) -> np
 
 def _group_scales(shape: MoEShape, stream: int, e: int, n: int, kdim: int) -> np.ndarray:
     rng = _rng(shape, stream, e)
-    if shape.scheme == "w4a16":
+    if shape.scheme in ("w4a16", "w4a8"):
         return rng.uniform(0.005, 0.02, size=(n, kdim // 32)).astype(np.float16)
     return rng.integers(120, 123, size=(n, kdim // 32), dtype=np.uint8)  # a8w4 e8m0
 

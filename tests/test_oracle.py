@@ -232,6 +232,21 @@ def _dense_reference(scheme, inp, e, rows):
         h = torch.nn.functional.silu(gu[:, :I]) * gu[:, I:]
         h = h.float().to(torch.bfloat16).double()
         return (h @ W2.T).numpy()
+    if scheme == "w4a8":
+        x = torch.from_numpy(inp["x"][rows].astype(np.float64)) * \
+            torch.from_numpy(inp["x_scale"][rows].astype(np.float64))[:, None]
+
+        def deq4(codes, s):
+            b = torch.from_numpy(codes.astype(np.int16))
+            lo = (b & 15) - 16 * ((b & 15) >= 8).to(torch.int16)
+            hi = (b >> 4) - 16 * ((b >> 4) >= 8).to(torch.int16)
+            q = torch.stack([lo, hi], -1).reshape(codes.shape[0], -1).double()
+            return q * torch.from_numpy(s.astype(np.float64)).repeat_interleave(32, 1)
+        gu = x @ deq4(inp["w13"][e], inp["w13_scale"][e]).T
+        h = torch.nn.functional.silu(gu[:, :I]) * gu[:, I:]
+        s = h.abs().amax(1, keepdim=True) / 127
+        hq = torch.clamp(torch.round(h / s), -127, 127) * s
+        return (hq @ deq4(inp["w2"][e], inp["w2_scale"][e]).T).numpy()
     if scheme == "w8a8":
         x = torch.from_numpy(inp["x"][rows].astype(np.float64)) * \
             torch.from_numpy(inp["x_scale"][rows].astype(np.float64))[:, None]
@@ -263,7 +278,8 @@ def _dense_reference(scheme, inp, e, rows):
     return (hq @ W2.T).numpy()
 
 
-@pytest.mark.parametrize("scheme,tol", [("w4a16", 1e-9), ("w8a8", 1e-5), ("a8w4", 1e-4)])
+@pytest.mark.parametrize("scheme,tol", [("w4a16", 1e-9), ("w8a8", 1e-5), ("a8w4", 1e-4),
+                                        ("w4a8", 1e-5)])
 def test_one_expert_top1_is_dense_ffn(scheme, tol):
     """E = 1, k = 1: the MoE layer is one dense FFN and every weight is 1."""
     sh, inp = _tiny(scheme, T=40, H=128, I=64, E=1, k=1)
@@ -276,7 +292,7 @@ def test_one_expert_top1_is_dense_ffn(scheme, tol):
     assert O.rel_l2(got, ref) < tol
 
 
-@pytest.mark.parametrize("scheme", ["w4a16", "w8a8", "a8w4"])
+@pytest.mark.parametrize("scheme", ["w4a16", "w8a8", "a8w4", "w4a8"])
 def test_brute_force_every_expert_then_select(scheme):
     """Run every expert on every token densely, then pick each token's k
     outputs and weight them: must equal the grouped oracle."""
@@ -539,3 +555,53 @@ def test_requant_e4m3_quotient_is_correctly_rounded():
     for i, (hv, s, m) in enumerate(rows):
         assert _frac(sc[i]) == s
         assert q[i, 0] == 0x7E and q[i, 1] == want[i], (float(hv), float(s), m)
+
+
+# ---------------------------------------------------------------- W4A8
+
+def test_w4a8_group_sums_against_python_ints():
+    """Each 32-wide group's int8 x int4 dot product, against Python integers
+    (two's-complement nibbles read by hand, low nibble = even K)."""
+    sh, inp = _tiny("w4a8", T=4, H=128, I=32, E=2, k=1, seed=41)
+    acc = O.group_sums_int4(inp["x"], inp["w13"][1])
+    assert acc.shape == (4, 64, 4) and acc.dtype == np.int64
+
+    def nib(v):
+        return v - 16 if v >= 8 else v
+    for p in range(4):
+        for n in (0, 17, 63):
+            row = inp["w13"][1, n]
+            q = [nib(int(b) & 15) if c % 2 == 0 else nib(int(b) >> 4)
+                 for b in row for c in (0, 1)]
+            for g in range(4):
+                want = sum(int(inp["x"][p, c]) * q[c] for c in range(32 * g, 32 * g + 32))
+                assert acc[p, n, g] == want
+
+
+def test_w4a8_group_scales_against_rationals():
+    """The group scales multiply the exact integer group sums, then the row
+    scale: one fp64 rounding of the exact rational value."""
+    rng = np.random.default_rng(42)
+    acc = rng.integers(-32512, 32513, (3, 5, 16))
+    sc = rng.uniform(0.005, 0.02, (5, 16)).astype(np.float16)
+    sr = rng.uniform(1e-3, 5e-2, 3).astype(np.float32)
+    got = O.apply_group_scales(acc, sc, sr)
+    for p in range(3):
+        for n in range(5):
+            exact = Fraction(float(sr[p])) * sum(Fraction(float(sc[n, g])) * int(acc[p, n, g])
+                                                 for g in range(16))
+            assert got[p, n] == float(exact)  # Python's int/int division rounds correctly
+
+
+def test_w4a8_unit_scales_reduce_to_the_integer_dot_product():
+    """With every group scale 1 and a unit token scale, gu is the plain
+    integer dot product of the int8 row with the int4 row (exact in fp32
+    below 2^24)."""
+    sh, inp = _tiny("w4a8", T=6, H=256, I=64, E=1, k=1, seed=43)
+    s13 = np.ones_like(inp["w13_scale"][0])
+    r = O.expert_w4a8(inp["x"], np.ones(6, np.float32), inp["w13"][0], s13, inp["w2"][0],
+                      np.ones_like(inp["w2_scale"][0]))
+    q = O.int4_values(inp["w13"][0]).astype(np.int64)
+    dot = inp["x"].astype(np.int64) @ q.T
+    np.testing.assert_array_equal(r["gu"], dot.astype(np.float32))
+    np.testing.assert_array_equal(r["acc1"].sum(axis=2), dot)
