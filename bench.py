@@ -41,8 +41,8 @@ if ROOT not in sys.path:
 
 METRIC = "grouped MoE FFN TFLOP/s + % MFMA/HBM roofline at M=4096 prefill, 1 GPU"
 HBM_PEAK_GBS = 8000.0
-MFMA_PEAK_TFLOPS = {"a8w4": 5000.0, "w8a8": 5000.0, "w4a16": 2500.0}
-DTYPE = {"a8w4": "fp8e4m3*fp4e2m1", "w8a8": "int8", "w4a16": "bf16"}
+MFMA_PEAK_TFLOPS = {"a8w4": 5000.0, "w8a8": 5000.0, "w4a16": 2500.0, "w4a8": 5000.0}
+DTYPE = {"a8w4": "fp8e4m3*fp4e2m1", "w8a8": "int8", "w4a16": "bf16", "w4a8": "int8*int4"}
 # Counter calibration: HBM bytes per KiB that FETCH_SIZE / WRITE_SIZE report,
 # measured on a plain 1 GiB device copy (__amd_rocclr_copyBuffer, run with
 # --copy-calibration-mib 1024): FETCH_SIZE reads 524,300 KiB for 1 GiB read,
@@ -83,7 +83,7 @@ def weight_bytes_per_expert(shape, which: str) -> float:
     n, kdim = (2 * shape.inter, shape.hidden) if which == "w13" else (shape.hidden, shape.inter)
     if shape.scheme == "w8a8":
         return n * kdim + n * 4
-    if shape.scheme == "w4a16":
+    if shape.scheme in ("w4a16", "w4a8"):
         return n * kdim / 2 + n * (kdim // 32) * 2
     return n * kdim / 2 + n * (kdim // 32)  # a8w4: e2m1 + e8m0
 
@@ -173,7 +173,8 @@ def cpu_baseline(shape, inp, target_s: float = 15.0) -> dict:
 SWEEP = ("w4a16_qwen3moe_t128", "w8a8_t2048", "a8w4_large@T1", "a8w4_large@T4",
          "a8w4_large@T16", "a8w4_large@T64", "a8w4_large@T256",
          "a8w4_large@T1024", "a8w4_large@T4096", "a8w4_large@T8192", "a8w4_tp2@T4096",
-         "a8w4_tp4@T4096", "w4a16_skewed_t8192")
+         "a8w4_tp4@T4096", "w4a16_skewed_t8192", "w4a8_qwen3moe_t128", "w4a8_t2048",
+         "w4a8_skewed_t8192")
 
 
 def stage_flops(shape) -> dict:

@@ -60,18 +60,28 @@ typedef enum {
  *             requantized per row to int8 with an fp32 scale.
  * A8W4_MXFP4: x OCP fp8 e4m3 [T,H] + fp32 per-token scale [T]; W e2m1 with
  *             one e8m0 scale byte per 32 along K [E,N,K/32].  h is
- *             requantized per row to e4m3 with an fp32 scale.            */
+ *             requantized per row to e4m3 with an fp32 scale.
+ * W4A8_G32:   x int8 [T,H] + fp32 per-token scale [T]; W int4 two's
+ *             complement with one fp16 scale per 32 along K [E,N,K/32]
+ *             (8-byte aligned).  Each 32-wide group's int8 x int4 sum is
+ *             exact, the group scale multiplies it, the token scale the
+ *             total (vLLM issue, section Constraint: W4A8 with the weights
+ *             upconverted to 8 bits before the integer MMA).  h is
+ *             requantized per row to int8 with an fp32 scale.           */
 typedef enum {
   QMOE_W4A16_G32 = 0,
   QMOE_W8A8_PERCHAN = 1,
-  QMOE_A8W4_MXFP4 = 2
+  QMOE_A8W4_MXFP4 = 2,
+  QMOE_W4A8_G32 = 3
 } qmoe_scheme;
 
 typedef enum { QMOE_DT_BF16 = 0, QMOE_DT_F32 = 1 } qmoe_dtype;
 
-/* Debug flag for qmoe_grouped_ffn (W8A8 only): also write the int32
+/* Debug flag for qmoe_grouped_ffn (W8A8 and W4A8): also write the
  * accumulators of both projections into the workspace (see
- * qmoe_grouped_ffn_debug_offsets).                                       */
+ * qmoe_grouped_ffn_debug_offsets): W8A8 the int32 sums; W4A8 the fp32 sum
+ * over groups of group scale x exact group sum, before the token (stage 1)
+ * or row (stage 2) scale.                                                 */
 #define QMOE_FLAG_DUMP_ACC 1u
 /* Flag for qmoe_grouped_ffn: the codes and scales of w13 and w2 are in the
  * streaming layout written by qmoe_prepack instead of the canonical one.  */
@@ -111,16 +121,22 @@ typedef struct {
  * Codes: byte b of row n of expert e, with ks = b/S, r = b%S, i = r/64,
  *   q = (r%64)/16, c = r%16, goes to
  *   (e*N + G)*KB + ks*16*S + i*1024 + (16*q + n%16)*16 + c.
- * Scales (R = scale bytes per row; 8 bytes per row per step in both
- *   schemes): for q = 0..3, row n and step ks, the two bytes at
+ *   W4A8 (S = 64) moves nibbles instead: the byte at
+ *   (e*N + G)*KB + ks*1024 + (16*q + n%16)*16 + 4*j + b, for q, j, b in
+ *   0..3, holds the code of K = 128*ks + 32*j + 8*q + b of row n in its low
+ *   nibble and that of K + 4 in its high nibble.
+ * Scales (R = scale bytes per row; 8 bytes per row per step in every
+ *   scheme): for q = 0..3, row n and step ks, the two bytes at
  *   (e*N + G)*R + ks*128 + (16*q + n%16)*2 hold, for A8W4, the e8m0 bytes
  *   of the 32-K blocks 8*ks + q and 8*ks + 4 + q of the row (in that
- *   order); for W4A16, the fp16 scale of group 4*ks + q.
+ *   order); for W4A16, the fp16 scale of group 4*ks + q.  W4A8: the eight
+ *   bytes at (e*N + G)*R + ks*128 + (n%16)*8 are the fp16 scales of groups
+ *   4*ks .. 4*ks + 3 of row n.
  * W8A8 per-channel fp32 scales are copied unchanged (scales_out may be
  * NULL for W8A8, then nothing is copied).
  * codes_out / scales_out have the byte sizes of codes / scales and must not
  * overlap them.  Requires N % 16 == 0 and K a multiple of 256 (A8W4) or
- * 128 (W4A16, W8A8).  QMOE_ERR_INVALID_ARG otherwise.                    */
+ * 128 (W4A16, W8A8, W4A8).  QMOE_ERR_INVALID_ARG otherwise.              */
 qmoe_status qmoe_prepack(int32_t scheme, int32_t E, int32_t N, int32_t K, const void* codes,
                          const void* scales, void* codes_out, void* scales_out, void* stream);
 
@@ -216,18 +232,19 @@ qmoe_status qmoe_align_noalloc(const int32_t* topk_ids, int32_t T, int32_t k, in
  * sorted_pair_ids / tile_expert / num_padded: qmoe_align's outputs for the
  *   same T, k, E and block_m.
  * y_pairs: [T*k, H], row p = pair p, unweighted expert output; bf16 for
- *   W4A16 and A8W4, fp32 for W8A8.
+ *   W4A16, A8W4 and W4A8, fp32 for W8A8.
  * ws: workspace of at least qmoe_grouped_ffn_workspace(d) bytes, 256-byte
  *   aligned.
  * Requirements: H % 256 == 0, I % 128 == 0 (I % 256 for A8W4), k <= E;
+ *   W4A8 scales 8-byte aligned;
  *   below 4 GiB each: x (T*H elements), the stage-2 activations (cap*I
  *   elements, cap = qmoe_align_capacity) and one expert's W13 or W2 codes.
  * Errors: QMOE_ERR_INVALID_ARG for null pointers, bad sizes or a short
  * workspace; QMOE_ERR_UNSUPPORTED for sizes outside the requirements.    */
 size_t qmoe_grouped_ffn_workspace(const qmoe_ffn_desc* d);
-/* Byte offsets inside ws of the int32 debug dumps written with
+/* Byte offsets inside ws of the 4-byte debug dumps written with
  * QMOE_FLAG_DUMP_ACC: acc1 [cap, 2I] and acc2 [cap, H], row = sorted slot.
- * Returns QMOE_ERR_INVALID_ARG unless the scheme is W8A8.               */
+ * Returns QMOE_ERR_INVALID_ARG unless the scheme is W8A8 or W4A8.       */
 qmoe_status qmoe_grouped_ffn_debug_offsets(const qmoe_ffn_desc* d, size_t* acc1_off,
                                            size_t* acc2_off);
 qmoe_status qmoe_grouped_ffn(const qmoe_ffn_desc* d, const void* x, const float* x_scale,

@@ -81,7 +81,8 @@ static FfnWs ffn_ws_layout(const qmoe_ffn_desc& d) {
     w.pmax = off;
     off = align_up(off + cap * (I / kMinStage1Cols) * 4, 256);
   }
-  if (d.scheme == QMOE_W8A8_PERCHAN && (d.flags & QMOE_FLAG_DUMP_ACC)) {
+  if ((d.scheme == QMOE_W8A8_PERCHAN || d.scheme == QMOE_W4A8_G32) &&
+      (d.flags & QMOE_FLAG_DUMP_ACC)) {
     w.acc1 = off;
     off = align_up(off + cap * 2 * I * 4, 256);
     w.acc2 = off;
@@ -112,7 +113,7 @@ static GemmShape choose_shape(int scheme, int stage, int block_m) {
 
 static qmoe_status check_desc(const qmoe_ffn_desc* d) {
   if (d == nullptr) return QMOE_ERR_INVALID_ARG;
-  if (d->scheme < 0 || d->scheme > 2) return QMOE_ERR_INVALID_ARG;
+  if (d->scheme < 0 || d->scheme > 3) return QMOE_ERR_INVALID_ARG;
   if (d->T < 0 || d->H <= 0 || d->I <= 0 || d->E <= 0 || d->k < 1 || d->k > d->E)
     return QMOE_ERR_INVALID_ARG;
   if (d->H % 32 != 0 || d->I % 32 != 0) return QMOE_ERR_INVALID_ARG;
@@ -300,7 +301,8 @@ qmoe_status qmoe_grouped_ffn_debug_offsets(const qmoe_ffn_desc* d, size_t* acc1_
                                            size_t* acc2_off) {
   const qmoe_status st = check_desc(d);
   if (st != QMOE_OK) return st;
-  if (d->scheme != QMOE_W8A8_PERCHAN || !(d->flags & QMOE_FLAG_DUMP_ACC) || !acc1_off ||
+  if ((d->scheme != QMOE_W8A8_PERCHAN && d->scheme != QMOE_W4A8_G32) ||
+      !(d->flags & QMOE_FLAG_DUMP_ACC) || !acc1_off ||
       !acc2_off)
     return QMOE_ERR_INVALID_ARG;
   const FfnWs lay = ffn_ws_layout(*d);
@@ -321,8 +323,10 @@ static qmoe_status grouped_ffn_impl(const qmoe_ffn_desc* d, const void* x, const
   if (!x || !w || !w->w13 || !w->w13_scale || !w->w2 || !w->w2_scale || !sorted_pair_ids ||
       !tile_expert || !num_padded || !y_pairs || !ws || (quant_act && !x_scale))
     return QMOE_ERR_INVALID_ARG;
+  const size_t scale_align = d->scheme == QMOE_W4A8_G32 ? 8 : 4;  // w4a8: 8-byte scale loads
   if (!aligned(x, 16) || !aligned(w->w13, 16) || !aligned(w->w2, 16) || !aligned(ws, 256) ||
-      !aligned(y_pairs, 16) || !aligned(w->w13_scale, 4) || !aligned(w->w2_scale, 4))
+      !aligned(y_pairs, 16) || !aligned(w->w13_scale, scale_align) ||
+      !aligned(w->w2_scale, scale_align))
     return QMOE_ERR_INVALID_ARG;
   const FfnWs lay = ffn_ws_layout(*d);
   if (ws_bytes < lay.total) return QMOE_ERR_INVALID_ARG;
@@ -339,7 +343,8 @@ static qmoe_status grouped_ffn_impl(const qmoe_ffn_desc* d, const void* x, const
       return QMOE_ERR_UNSUPPORTED;
   }
   uint8_t* wsb = reinterpret_cast<uint8_t*>(ws);
-  const bool dump = d->scheme == QMOE_W8A8_PERCHAN && (d->flags & QMOE_FLAG_DUMP_ACC);
+  const bool dump = (d->scheme == QMOE_W8A8_PERCHAN || d->scheme == QMOE_W4A8_G32) &&
+                    (d->flags & QMOE_FLAG_DUMP_ACC);
   const int cap = (int)qmoe_align_capacity(d->T, d->k, d->E, d->block_m);
   hipStream_t s = (hipStream_t)stream;
 
@@ -473,7 +478,7 @@ qmoe_status qmoe_grouped_ffn_profiled(const qmoe_ffn_desc* d, const void* x,
 
 qmoe_status qmoe_prepack(int32_t scheme, int32_t E, int32_t N, int32_t K, const void* codes,
                          const void* scales, void* codes_out, void* scales_out, void* stream) {
-  if (scheme < 0 || scheme > 2 || E < 1 || N < 1 || K < 1) return QMOE_ERR_INVALID_ARG;
+  if (scheme < 0 || scheme > 3 || E < 1 || N < 1 || K < 1) return QMOE_ERR_INVALID_ARG;
   if (N % 16 != 0 || K % (scheme == QMOE_A8W4_MXFP4 ? 256 : 128) != 0) return QMOE_ERR_INVALID_ARG;
   if ((long long)E * N > (1ll << 31)) return QMOE_ERR_INVALID_ARG;
   if (!codes || !codes_out || !scales) return QMOE_ERR_INVALID_ARG;
@@ -484,7 +489,7 @@ qmoe_status qmoe_prepack(int32_t scheme, int32_t E, int32_t N, int32_t K, const 
   const size_t cb = (size_t)E * N * (scheme == QMOE_W8A8_PERCHAN ? K : K / 2);
   const size_t sbytes = scheme == QMOE_W8A8_PERCHAN
                             ? (size_t)E * N * 4
-                            : (size_t)E * N * (K / 32) * (scheme == QMOE_W4A16_G32 ? 2 : 1);
+                            : (size_t)E * N * (K / 32) * (scheme == QMOE_A8W4_MXFP4 ? 1 : 2);
   auto overlap = [](const void* a, size_t na, const void* b, size_t nb) {
     const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
     return x < y + nb && y < x + na;

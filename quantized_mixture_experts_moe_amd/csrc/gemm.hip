@@ -28,7 +28,11 @@
 //          section Constraint: integer products need int8 activations);
 //   a8w4:  v_mfma_scale_f32_16x16x128_f8f6f4, A = fp8 e4m3, B = fp4 e2m1
 //          with the e8m0 block scale fed per lane (aiter PR 6090, section
-//          Changes: fp8 act, MXFP4 weight).
+//          Changes: fp8 act, MXFP4 weight);
+//   w4a8:  v_mfma_i32_16x16x32_i8, int4 weights upconverted to int8 in
+//          registers (vLLM issue, section Constraint: W4A8 with upconversion
+//          of weights to IU8 before the MMA), one MFMA per 32-wide scale
+//          group, its exact int32 sum scaled by the group scale in fp32.
 //
 // Per-lane fragment layout of a 16x16xK MFMA (lane = 16*q + r): A row r and
 // B column r hold a contiguous quarter q of the instruction's K (bf16, i8,
@@ -170,7 +174,8 @@ __global__ __launch_bounds__(WAVES * 64)
     if (tid < BM) next_ri = next_pair < g.P ? (STAGE == 1 ? next_pair / g.k : next_pair) : -1;
   };
 
-  constexpr int SB = S == kW4A16 ? 2 : 1;  // scale bytes (w4a16 fp16, a8w4 e8m0)
+  // scale bytes (w4a16 and w4a8 fp16, a8w4 e8m0)
+  constexpr int SB = (S == kW4A16 || S == kW4A8) ? 2 : 1;
   constexpr uint32_t B_KS = PK ? 16 * T_::B_STEP : T_::B_STEP;  // code bytes per step
   constexpr uint32_t B_PIECE = PK ? 1024 : 16;                   // between a lane's pieces
   constexpr uint32_t S_KS = PK ? 128 : 8;                         // scale bytes per step
@@ -196,17 +201,34 @@ __global__ __launch_bounds__(WAVES * 64)
 #pragma unroll
     for (int s = 0; s < NSUB; s++) {
       const uint32_t o = boff[s] + (uint32_t)ks * B_KS;
+      if constexpr (S == kW4A8 && !PK) {
+        // Canonical W4A8: MFMA j's 8 codes of the lane are the 4 bytes at
+        // 16j (+ 4 lq, in boff) of the row's step bytes.
 #pragma unroll
-      for (int i = 0; i < T_::B_FRAG / 16; i++)
-        bf[s].q[i] = *reinterpret_cast<const u32x4*>(Bexp + (uint32_t)(o + B_PIECE * i));
-      // The lane's two scale bytes as part of the aligned 32-bit word that
-      // holds them (a 16-bit load is zero-extended in the loop, which made
-      // every fourth step wait for all loads in flight).
-      if (S == kW4A16 || S == kA8W4)
+        for (int j = 0; j < 4; j++)
+          bf[s].q[0][j] = *reinterpret_cast<const uint32_t*>(Bexp + (uint32_t)(o + 16 * j));
+      } else {
+#pragma unroll
+        for (int i = 0; i < T_::B_FRAG / 16; i++)
+          bf[s].q[i] = *reinterpret_cast<const u32x4*>(Bexp + (uint32_t)(o + B_PIECE * i));
+      }
+      if constexpr (S == kW4A8) {
+        // The four fp16 group scales of the lane's column for this step, 8
+        // contiguous bytes in both layouts.
+        typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 v =
+            *reinterpret_cast<const u32x2*>(Sexp + (uint32_t)(soff[s] + ks * S_KS));
+        bf[s].sc = v.x;
+        bf[s].sc2 = v.y;
+      } else if constexpr (S == kW4A16 || S == kA8W4) {
+        // The lane's two scale bytes as part of the aligned 32-bit word that
+        // holds them (a 16-bit load is zero-extended in the loop, which made
+        // every fourth step wait for all loads in flight).
         bf[s].sc = *reinterpret_cast<const uint32_t*>(
             Sexp + ((uint32_t)(soff[s] + ks * S_KS) & ~3u));
-      else
+      } else {
         bf[s].sc = 0;
+      }
     }
   };
   auto load_a = [&](u32x4(&ar)[NCH], int ks) __attribute__((always_inline)) {
@@ -271,10 +293,11 @@ __global__ __launch_bounds__(WAVES * 64)
       if constexpr (PK) {
         const uint32_t g16 = (uint32_t)(nrow[s] - lr);  // first row of the 16-row group
         boff[s] = g16 * (uint32_t)kbytes + lane * 16;
-        soff[s] = g16 * (uint32_t)(K / 32) * SB + lane * 2;
+        // w4a8: 16 rows x 8 bytes per step, row lr's at 8 lr
+        soff[s] = g16 * (uint32_t)(K / 32) * SB + (S == kW4A8 ? lr * 8 : lane * 2);
       } else {
-        boff[s] = (uint32_t)nrow[s] * (uint32_t)kbytes + lq * T_::B_FRAG;
-        soff[s] = (uint32_t)nrow[s] * (uint32_t)(K / 32) * SB + lq * 2;
+        boff[s] = (uint32_t)nrow[s] * (uint32_t)kbytes + lq * (S == kW4A8 ? 4 : T_::B_FRAG);
+        soff[s] = (uint32_t)nrow[s] * (uint32_t)(K / 32) * SB + (S == kW4A8 ? 0 : lq * 2);
       }
     }
   };
@@ -316,9 +339,21 @@ __global__ __launch_bounds__(WAVES * 64)
     // hoisting every group's reads (which would need ~8x the registers).
     auto read_frag = [&](u32x4(&af)[NF], int stage, int m) __attribute__((always_inline)) {
       const uint8_t* src = sA(stage) + (m * 16 + lr) * PITCH;
+      if constexpr (S == kW4A8) {
+        // MFMA j's 8 bytes: K [32j + 8 lq, +8) of the row; pieces 2f and
+        // 2f + 1 share af[f].
+        typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
-      for (int f = 0; f < NF; f++)
-        af[f] = *reinterpret_cast<const u32x4*>(src + a_frag_offset<S, PK>(lq, f));
+        for (int f = 0; f < NF; f++) {
+          const u32x2 p0 = *reinterpret_cast<const u32x2*>(src + 64 * f + 8 * lq);
+          const u32x2 p1 = *reinterpret_cast<const u32x2*>(src + 64 * f + 32 + 8 * lq);
+          af[f] = u32x4{p0.x, p0.y, p1.x, p1.y};
+        }
+      } else {
+#pragma unroll
+        for (int f = 0; f < NF; f++)
+          af[f] = *reinterpret_cast<const u32x4*>(src + a_frag_offset<S, PK>(lq, f));
+      }
     };
     // With FRAG2 the reads run one group ahead (two fragment buffers);
     // otherwise each group's reads directly precede its MFMAs and the other
@@ -328,7 +363,7 @@ __global__ __launch_bounds__(WAVES * 64)
     auto compute = [&](int stage, const BFrag<S>(&bcr)[NSUB]) __attribute__((always_inline)) {
       BReady<S> bc[NSUB];
 #pragma unroll
-      for (int s = 0; s < NSUB; s++) bc[s] = prepare_b<S>(bcr[s], sshift);
+      for (int s = 0; s < NSUB; s++) bc[s] = prepare_b<S, PK>(bcr[s], sshift);
       u32x4 fa[NF], fb[NF];
       if constexpr (FRAG2) read_frag(fa, stage, 0);
 #pragma unroll
@@ -496,10 +531,14 @@ __global__ __launch_bounds__(WAVES * 64)
                   g.dump[orow * 2 * g.I + enrow[s]] = acc[m][s][r];
                   g.dump[orow * 2 * g.I + enrow[s + HALF]] = acc[m][s + HALF][r];
                 }
-              } else if constexpr (S == kA8W4) {
+              } else if constexpr (S == kA8W4 || S == kW4A8) {
                 const float xs = rscs[r];
                 gf = acc[m][s][r] * xs;
                 uf = acc[m][s + HALF][r] * xs;
+                if (S == kW4A8 && g.dump != nullptr && tok >= 0) {
+                  g.dump[orow * 2 * g.I + enrow[s]] = __float_as_int(acc[m][s][r]);
+                  g.dump[orow * 2 * g.I + enrow[s + HALF]] = __float_as_int(acc[m][s + HALF][r]);
+                }
               } else {
                 gf = acc[m][s][r];
                 uf = acc[m][s + HALF][r];
@@ -520,8 +559,10 @@ __global__ __launch_bounds__(WAVES * 64)
                 const float ws2 = t_ws[s];
                 *reinterpret_cast<float*>(trow + cl * 4) = ((float)acc[m][s][r] * rs) * ws2;
                 if (g.dump != nullptr && pair >= 0) g.dump[orow * g.H + enrow[s]] = acc[m][s][r];
-              } else if constexpr (S == kA8W4) {
+              } else if constexpr (S == kA8W4 || S == kW4A8) {
                 *reinterpret_cast<__bf16*>(trow + cl * 2) = (__bf16)(acc[m][s][r] * rs);
+                if (S == kW4A8 && g.dump != nullptr && pair >= 0)
+                  g.dump[orow * g.H + enrow[s]] = __float_as_int(acc[m][s][r]);
               } else {
                 *reinterpret_cast<__bf16*>(trow + cl * 2) = (__bf16)acc[m][s][r];
               }
@@ -663,6 +704,8 @@ hipError_t launch_gemm(int scheme, int stage, int block_m, bool packed, int nsub
     case 3: return launch_layout<kW8A8, 2>(packed, block_m, nsub, waves, g, s);
     case 4: return launch_layout<kA8W4, 1>(packed, block_m, nsub, waves, g, s);
     case 5: return launch_layout<kA8W4, 2>(packed, block_m, nsub, waves, g, s);
+    case 6: return launch_layout<kW4A8, 1>(packed, block_m, nsub, waves, g, s);
+    case 7: return launch_layout<kW4A8, 2>(packed, block_m, nsub, waves, g, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -17,7 +17,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 // out of registers).
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-enum { kW4A16 = 0, kW8A8 = 1, kA8W4 = 2 };
+enum { kW4A16 = 0, kW8A8 = 1, kA8W4 = 2, kW4A8 = 3 };
 
 // s_waitcnt immediate (gfx9 encoding) waiting for vmcnt == 0 only:
 // vmcnt bits [3:0] and [15:14] = 0, expcnt [6:4] = 7, lgkmcnt [11:8] = 15.
@@ -59,6 +59,22 @@ struct Tr<kA8W4> {
   typedef f32x4 Acc;
 };
 
+// W4A8: int8 activations x int4 weights, one v_mfma_i32_16x16x32_i8 per
+// 32-wide scale group (its int32 result is the exact group sum, scaled once
+// in fp32).  A step is 128 K = four groups; per MFMA j a lane holds 8 bytes
+// of K [32j + 8q, +8) of its row (A) and of its column (B).
+template <>
+struct Tr<kW4A8> {
+  static constexpr int BK = 128;
+  static constexpr int A_ELEM = 1;
+  static constexpr int A_STEP = 128;
+  static constexpr int A_FRAG = 32;   // four 8-byte pieces per lane per 16-row group
+  static constexpr int B_STEP = 64;   // int4 codes per row per step
+  static constexpr int B_FRAG = 16;   // four 4-byte code words per lane per sub-tile
+  static constexpr int KB_NUM = 1, KB_DEN = 2;
+  typedef f32x4 Acc;
+};
+
 // Byte offset, inside a staged activation row of one step, of the f-th
 // 16-byte piece of lane group q's A fragment (a8w4: pieces 2j, 2j+1 feed
 // MFMA j; w8a8 and w4a16: piece j feeds MFMA j).  With the streaming weight
@@ -86,7 +102,9 @@ __device__ inline int a_frag_offset(int q, int f) {
 template <int S>
 struct BFrag {
   u32x4 q[Tr<S>::B_FRAG / 16];
-  uint32_t sc;  // w4a16: fp16 group scale bits; a8w4: two e8m0 bytes; w8a8: unused
+  uint32_t sc;   // w4a16: fp16 group scale bits; a8w4: two e8m0 bytes; w8a8: unused;
+                 // w4a8: the fp16 scales of MFMAs 0 and 1
+  uint32_t sc2;  // w4a8: the fp16 scales of MFMAs 2 and 3 (others: unused)
 };
 
 // Eight int4 codes (two's complement, element i in bits 4i..4i+3) times the
@@ -139,12 +157,49 @@ template <>
 struct BReady<kW4A16> {
   bf16x8 v[4];
 };
+// w4a8: per MFMA j the 8 int8 weights 16*q of K [32j + 8q, +8) in natural K
+// order (w[2j]: K 0-3, w[2j+1]: K 4-7) and the group scale / 16.
+template <>
+struct BReady<kW4A8> {
+  uint32_t w[8];
+  float s[4];
+};
+
+// W4A8 unpacking: a nibble placed in the high half of a byte is the int8
+// value 16*q exactly (two's complement), so (v << 4) & 0xF0F0F0F0 holds the
+// low nibbles of v's four bytes and v & 0xF0F0F0F0 the high ones.  The
+// streaming layout stores K b and b + 4 in byte b of each word (low, high
+// nibble), which gives K 0-3 and 4-7 directly; the canonical layout stores K
+// 2c and 2c + 1 in byte c, so two byte permutations interleave them.
+template <bool PK>
+__device__ inline void unpack_w4a8(uint32_t v, uint32_t& k03, uint32_t& k47) {
+  const uint32_t lo = (v << 4) & 0xF0F0F0F0u, hi = v & 0xF0F0F0F0u;
+  if constexpr (PK) {
+    k03 = lo;
+    k47 = hi;
+  } else {
+    // lo = K 0, 2, 4, 6 and hi = K 1, 3, 5, 7 (one byte each): interleave.
+    k03 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+    k47 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
+  }
+}
 
 // `sshift` (0 or 16) picks this lane's 16-bit scale field out of the
-// aligned 32-bit word the weight loads fetch.
-template <int S>
+// aligned 32-bit word the weight loads fetch (w4a16, a8w4).
+template <int S, bool PK = true>
 __device__ inline BReady<S> prepare_b(const BFrag<S>& b, uint32_t sshift) {
-  if constexpr (S == kW4A16) {
+  if constexpr (S == kW4A8) {
+    BReady<S> r;
+    const uint32_t words[4] = {b.q[0].x, b.q[0].y, b.q[0].z, b.q[0].w};
+#pragma unroll
+    for (int j = 0; j < 4; j++) unpack_w4a8<PK>(words[j], r.w[2 * j], r.w[2 * j + 1]);
+    const uint32_t sw[2] = {b.sc, b.sc2};
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+      r.s[j] = __half2float(__ushort_as_half((unsigned short)(sw[j >> 1] >> (16 * (j & 1))))) *
+               0.0625f;
+    return r;
+  } else if constexpr (S == kW4A16) {
     BReady<S> r;
     const float sc = __half2float(__ushort_as_half((unsigned short)(b.sc >> sshift)));
     r.v[0] = dequant8_bf16(b.q[0].x, sc);
@@ -173,6 +228,20 @@ __device__ inline void mfma_step(typename Tr<S>::Acc& acc, const u32x4* a, const
     for (int j = 0; j < 2; j++) {
       acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, a[j]),
                                                  __builtin_bit_cast(i32x4, b.q[j]), acc, 0, 0, 0);
+    }
+  } else if constexpr (S == kW4A8) {
+    // a[j >> 1] holds the 8-byte A pieces of MFMAs 2(j>>1) and 2(j>>1)+1.
+    // Each MFMA starts from zero: its int32 result is 16 * the exact group
+    // sum (|16 * sum| < 2^20, exact in fp32), scaled by s/16 in one fma.
+    const i32x4 zero = {0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const u32x4 ap = a[j >> 1];
+      const long av = (long)(((unsigned long)(j & 1 ? ap.w : ap.y) << 32) | (j & 1 ? ap.z : ap.x));
+      const long bv = (long)(((unsigned long)br.w[2 * j + 1] << 32) | br.w[2 * j]);
+      const i32x4 t = __builtin_amdgcn_mfma_i32_16x16x32_i8(av, bv, zero, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 4; r++) acc[r] = __builtin_fmaf((float)t[r], br.s[j], acc[r]);
     }
   } else {
     const BFrag<S>& b = br.f;

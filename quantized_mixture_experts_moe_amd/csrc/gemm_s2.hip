@@ -461,6 +461,9 @@ hipError_t launch_s2r_bm(int rows, int tile_div, const GemmArgs& g, int passes,
 
 }  // namespace
 
+// W4A8 (scheme 3) takes the row-major stage 2 of gemm.hip: with the weights
+// as the first operand its group scales would differ across a lane's four
+// outputs.
 bool stage2_resident_ok(int scheme, int I) {
   return (scheme == 1 || scheme == 2) && I <= kS2RowBytes;
 }

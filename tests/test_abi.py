@@ -167,6 +167,18 @@ def test_ffn_workspace_and_desc_validation():
     assert call(_desc(scheme="w8a8", T=64, H=65536, I=65536)) == ops.QMOE_ERR_UNSUPPORTED
     assert L.qmoe_grouped_ffn(None, p, p, ctypes.byref(w), p, p, p, p, p, 1 << 40, None) == \
         ops.QMOE_ERR_INVALID_ARG
+    # W4A8: scheme code 3; its scales are read 8 bytes at a time
+    w4 = _desc(scheme="w4a8", I=128)
+    w4d = _desc(scheme="w4a8", I=128, flags=ops.QMOE_FLAG_DUMP_ACC)
+    assert ops.grouped_ffn_workspace(w4d) > ops.grouped_ffn_workspace(w4) > 0
+    assert 0 < ops.grouped_ffn_debug_offsets(w4d)[0]
+    w_mis = ops.Weights(p, ctypes.c_void_p(0x1004), p, p)
+    assert L.qmoe_grouped_ffn(ctypes.byref(w4), p, p, ctypes.byref(w_mis), p, p, p, p, p,
+                              1 << 40, None) == ops.QMOE_ERR_INVALID_ARG
+    assert call(w4, xs=None) == ops.QMOE_ERR_INVALID_ARG  # w4a8 needs x_scale
+    bad_scheme = ops.FfnDesc(4, 64, 512, 256, 8, 2, 32, 0)
+    assert ops.grouped_ffn_workspace(bad_scheme) == 0
+    assert call(bad_scheme) == ops.QMOE_ERR_INVALID_ARG
 
 
 def test_combine_validation():
@@ -185,7 +197,10 @@ def test_prepack_validation():
     L = ops.lib()
     a, b, c, d = (ctypes.c_void_p(x) for x in (0x100000, 0x200000, 0x10000000, 0x20000000))
     INV = ops.QMOE_ERR_INVALID_ARG
-    assert L.qmoe_prepack(3, 2, 32, 256, a, b, c, d, None) == INV          # scheme
+    assert L.qmoe_prepack(4, 2, 32, 256, a, b, c, d, None) == INV          # scheme
+    assert L.qmoe_prepack(-1, 2, 32, 256, a, b, c, d, None) == INV         # scheme
+    assert L.qmoe_prepack(3, 2, 32, 64, a, b, c, d, None) == INV           # w4a8 K % 128
+    assert L.qmoe_prepack(3, 2, 32, 256, a, b, c, None, None) == INV       # w4a8 needs scales_out
     assert L.qmoe_prepack(2, 0, 32, 256, a, b, c, d, None) == INV          # E
     assert L.qmoe_prepack(2, 2, 24, 256, a, b, c, d, None) == INV          # N % 16
     assert L.qmoe_prepack(2, 2, 32, 128, a, b, c, d, None) == INV          # a8w4 K % 256
