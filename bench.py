@@ -388,70 +388,162 @@ def run_workload(name: str, args, torch, with_cpu: bool, cpu_seconds: float = 20
     return res
 
 
-TILE_SWEEP_SHARES = ("a8w4_large", "a8w4_tp2", "a8w4_tp4")
-TILE_SWEEP_TOKENS = (1, 16, 64, 256, 1024, 4096, 8192)
+# Workloads and token buckets of the tile table (aiter PR 6090, section
+# Changes: token buckets 1-256, 1024, 4096, 8192 of the a8w4 block and its
+# tensor-parallel shares; the other workloads at their own token counts).
+TILE_SWEEP_POINTS = (
+    ("a8w4_large", (1, 16, 64, 256, 1024, 4096, 8192)),
+    ("a8w4_tp2", (1, 16, 64, 256, 1024, 4096, 8192)),
+    ("a8w4_tp4", (1, 16, 64, 256, 1024, 4096, 8192)),
+    ("w4a16_qwen3moe_t128", (128,)),
+    ("w8a8_t2048", (2048,)),
+    ("w4a8_qwen3moe_t128", (128, 2048)),
+    ("w4a16_skewed_t8192", (8192,)),
+    ("w4a8_skewed_t8192", (8192,)),
+)
 TILE_SWEEP_BLOCKS = (16, 32, 64, 128)
+SCHEME_CODE_C = {"w4a16": 0, "w8a8": 1, "a8w4": 2, "w4a8": 3}
+
+
+def _knob_values(scheme: str, bm: int, inter: int, hidden: int) -> dict:
+    """The tile knobs that apply to a call, and the values the sweep tries
+    (the library refuses the others).  Keys are QMOE_TILE fields."""
+    resident = scheme in ("a8w4", "w8a8") and inter <= 1024
+    kv = {"s1runs": (0, 1)}
+    if bm >= 64:
+        kv["s1w"] = (4, 8)
+    if bm <= 32:
+        kv["s1r"] = (4,)
+    if resident:
+        nt = hidden // 256
+        kv["s2p"] = tuple(p for p in (1, 2, 4, 8, 16) if nt % p == 0 and
+                          (scheme != "w8a8" or p <= 16))
+        if bm >= 32:
+            kv["s2h"] = (0, 1)
+    elif bm >= 64:
+        kv["s2w"] = (4, 8)
+    return kv
+
+
+def _env_str(cfg: dict) -> str:
+    return ",".join(f"{k}={v}" for k, v in sorted(cfg.items()))
+
+
+def _table_row(sh, T: int, bm: int, cfg: dict) -> str:
+    """One C initializer of the tile table (field order of TileRow)."""
+    c = {"s1w": 0, "s1r": 0, "s1runs": -1, "s2w": 0, "s2p": 0, "s2h": -1}
+    c.update(cfg)
+    return ("{%d, %d, %d, %d, %d, %d, %d, {%d, %d, %d, %d, %d, %d}},"
+            % (SCHEME_CODE_C[sh.scheme], sh.hidden, sh.inter, sh.experts, sh.topk, T, bm,
+               c["s1w"], c["s1r"], c["s1runs"], c["s2w"], c["s2p"], c["s2h"]))
 
 
 def tile_sweep(args, torch) -> None:
-    """Step time of every block_m for the large a8w4 block and its tensor-
-    parallel shares (inter 1024, 512, 256) at each token bucket.  Inputs are
-    drawn once per share at 8192 tokens; a bucket takes the leading tokens.
-    Accuracy gate: a block_m counts only if its output equals the block_m 16
-    output bit for bit (the row tiles change neither the order nor the
-    precision of any sum).  One JSON line per (share, tokens, block_m), then
-    one per (share, tokens) naming the fastest gated block_m."""
+    """Tile table by a gated sweep.  For each workload and token bucket: every
+    block_m with the library's other choices, then, at the fastest block_m,
+    each other knob in turn (stage-1 block waves, ring depth, schedule;
+    stage-2 waves, column passes, half tiles), a value kept when it is at
+    least 2% faster (the step's run-to-run spread is about 1%).  Accuracy gate: a configuration counts only if its
+    output equals the reference (block_m 16, the library's choices) bit for
+    bit.  Inputs are drawn once per workload at its largest bucket; a bucket
+    takes the leading tokens.  One JSON line per timed configuration, one per
+    bucket with the chosen row; --emit-table writes the rows as the
+    library's tile_table.inc."""
     from quantized_mixture_experts_moe_amd import ops, synth
     from quantized_mixture_experts_moe_amd.shapes import shape_by_name
 
     dev = torch.device("cuda:0")
     flush = torch.ones(64 << 20, dtype=torch.int64, device=dev)
-    for base in TILE_SWEEP_SHARES:
-        full = shape_by_name(f"{base}@T{max(TILE_SWEEP_TOKENS)}")
+    rows = []
+    for base, buckets in TILE_SWEEP_POINTS:
+        if args.tile_only and base not in args.tile_only.split(","):
+            continue
+        full = shape_by_name(base).with_tokens(max(buckets))
         inp = synth.make_inputs(full)
         g = {}
         for key, a in inp.items():
             if a is not None:
-                g[key] = torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+                g[key] = torch.from_numpy(np.ascontiguousarray(a.view(np.int16) if a.dtype ==
+                                                              np.uint16 else a)).to(dev)
+        if full.scheme == "w4a16":
+            g["x"] = g["x"].view(torch.bfloat16)
         W = ops.prepack_weights(full.scheme, {kk: g.pop(kk) for kk in
                                               ("w13", "w13_scale", "w2", "w2_scale")})
         del inp
         E, k = full.experts, full.topk
-        for T in TILE_SWEEP_TOKENS:
+        f32 = full.scheme == "w8a8"
+        for T in buckets:
             sh = full.with_tokens(T)
-            gt = {"logits": g["logits"][:T], "x": g["x"][:T], "x_scale": g["x_scale"][:T]}
-            ref, times = None, {}
-            for bm in TILE_SWEEP_BLOCKS:
+            gt = {"logits": g["logits"][:T], "x": g["x"][:T],
+                  "x_scale": None if "x_scale" not in g else g["x_scale"][:T]}
+
+            def measure(bm, cfg):
+                os.environ["QMOE_TILE"] = _env_str(cfg)
                 ids = torch.empty((T, k), dtype=torch.int32, device=dev)
                 tw = torch.empty((T, k), dtype=torch.float32, device=dev)
                 _, _, al = ops.route_align(gt["logits"], k, bm, ids, tw)
                 y, ws = ops.grouped_ffn(sh.scheme, gt["x"], gt["x_scale"], W, al, E, k)
-                out_bf16, _ = ops.combine(y, tw, want_bf16=True, want_f32=False)
+                ob, of = ops.combine(y, tw, want_bf16=True, want_f32=f32)
 
                 def eager_step():
                     ops.route_align(gt["logits"], k, bm, ids, tw, out=al)
                     ops.grouped_ffn(sh.scheme, gt["x"], gt["x_scale"], W, al, E, k, ws=ws,
                                     y_pairs=y)
-                    ops.combine(y, tw, out_bf16=out_bf16, out_f32=None, want_f32=False)
+                    ops.combine(y, tw, out_bf16=ob, out_f32=of, want_f32=f32)
 
                 torch.cuda.synchronize()
-                if ref is None:
-                    ref = out_bf16.clone()
-                gate = bool(torch.equal(out_bf16, ref))
                 ms, med = graph_step_ms(torch, ops, args, flush, dict(
                     shape=sh, g=gt, W=W, ids=ids, tw=tw, al=al, y=y, ws=ws, bm=bm,
-                    out_bf16=out_bf16, out_f32=None), eager_step)
-                if gate:
-                    times[bm] = ms
-                print(json.dumps({"tile_sweep": base, "inter": sh.inter, "tokens": T,
-                                  "block_m": bm, "ms_per_step": round(ms, 4),
-                                  "ms_median": round(med, 4), "gate_bitexact": gate}), flush=True)
+                    out_bf16=ob, out_f32=of), eager_step)
+                outs = (ob.clone(), of.clone() if f32 else None)
                 del y, ws, al
-            best = min(times, key=times.get)
-            print(json.dumps({"tile_best": base, "inter": sh.inter, "tokens": T, "block_m": best,
-                              "ms_per_step": round(times[best], 4)}), flush=True)
+                return ms, outs
+
+            ref = None
+            best = None  # (ms, bm, cfg)
+            for bm in TILE_SWEEP_BLOCKS:
+                ms, outs = measure(bm, {})
+                if ref is None:
+                    ref = outs
+                gate = torch.equal(outs[0], ref[0]) and (not f32 or torch.equal(outs[1], ref[1]))
+                print(json.dumps({"tile_sweep": base, "tokens": T, "block_m": bm, "cfg": "",
+                                  "ms_per_step": round(ms, 4), "gate_bitexact": gate}),
+                      flush=True)
+                if gate and (best is None or ms < best[0]):
+                    best = (ms, bm, {})
+            ms0, bm, cfg = best
+            default_ms = ms0
+            for knob, values in _knob_values(sh.scheme, bm, sh.inter, sh.hidden).items():
+                for v in values:
+                    trial = dict(cfg)
+                    trial[knob] = v
+                    ms, outs = measure(bm, trial)
+                    gate = torch.equal(outs[0], ref[0]) and (not f32 or
+                                                             torch.equal(outs[1], ref[1]))
+                    print(json.dumps({"tile_sweep": base, "tokens": T, "block_m": bm,
+                                      "cfg": _env_str(trial), "ms_per_step": round(ms, 4),
+                                      "gate_bitexact": gate}), flush=True)
+                    if gate and ms < best[0] * 0.98:
+                        best = (ms, bm, trial)
+                cfg = best[2]
+            os.environ.pop("QMOE_TILE", None)
+            row = _table_row(sh, T, best[1], best[2])
+            rows.append(row)
+            print(json.dumps({"tile_best": base, "tokens": T, "block_m": best[1],
+                              "cfg": _env_str(best[2]), "ms_per_step": round(best[0], 4),
+                              "library_choices_ms": round(default_ms, 4), "row": row}),
+                  flush=True)
         del g, W
         torch.cuda.empty_cache()
+    if args.emit_table:
+        src = os.path.join(ROOT, "quantized_mixture_experts_moe_amd", "csrc", "tile_table.inc")
+        with open(src) as f:
+            head = [line for line in f if line.startswith("//")]
+        with open(args.emit_table, "w") as f:
+            f.writelines(head)
+            for row in rows:
+                f.write(row + "\n")
+        log(f"wrote {len(rows)} rows to {args.emit_table}")
 
 
 def main():
@@ -464,8 +556,13 @@ def main():
                     help="run every workload of the sweep, one JSON line each (CPU baseline on a "
                          "shorter sample per workload unless --no-cpu-baseline)")
     ap.add_argument("--tile-sweep", action="store_true",
-                    help="time every block_m for the a8w4 block and its tensor-parallel shares "
-                         "at each token bucket")
+                    help="gated tile sweep (block_m, blocks, prefetch ring, schedule, stage-2 "
+                         "passes) per workload and token bucket")
+    ap.add_argument("--tile-only", default="",
+                    help="comma-separated workloads of the tile sweep (default: all)")
+    ap.add_argument("--emit-table", default="",
+                    help="with --tile-sweep: write the chosen rows, with the comment lines of "
+                         "the library's tile_table.inc, to this file")
     ap.add_argument("--block-m", type=int, default=0)
     ap.add_argument("--eager", action="store_true",
                     help="time the eager launches only (no HIP graph of the step)")

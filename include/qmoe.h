@@ -158,6 +158,21 @@ qmoe_status qmoe_route(const float* logits, int32_t T, int32_t E, int32_t k,
                        int32_t* topk_ids, float* topk_w, void* stream);
 
 /* ---------------------------------------------------------------------
+ * qmoe_default_block_m -- the tile height (block_m) to give qmoe_align and
+ * qmoe_grouped_ffn for a shape and token count: the gfx950 tile table's
+ * entry for the shape's token bucket (built by a tile sweep with a bit-exact
+ * accuracy gate, aiter PR 6090, section Test Plan), else a rule on the mean
+ * rows per expert.  qmoe_grouped_ffn takes the rest of that table entry
+ * (blocks, prefetch depth, column passes) when it is called with this
+ * block_m; any block_m gives the same results bit for bit.  Returns 0 for
+ * invalid arguments.  The environment variable QMOE_TILE
+ * ("s1w=8,s1r=4,s1runs=1,s2w=4,s2p=8,s2h=0", any subset) overrides those
+ * other choices in qmoe_grouped_ffn for sweeps; a malformed or inapplicable
+ * value makes qmoe_grouped_ffn return QMOE_ERR_INVALID_ARG.               */
+int32_t qmoe_default_block_m(int32_t scheme, int32_t T, int32_t H, int32_t I, int32_t E,
+                             int32_t k);
+
+/* ---------------------------------------------------------------------
  * qmoe_align -- group the P = T*k (token, slot) pairs by expert.
  * sorted_pair_ids[cap]: for experts e = 0..E-1 in order, the pair ids
  *   p = t*k+j with topk_ids[t,j] == e in ascending order, then the sentinel

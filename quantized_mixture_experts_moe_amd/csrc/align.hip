@@ -338,13 +338,15 @@ __global__ __launch_bounds__(kSmallT) void align_small_kernel(
 
 // Routing and grouping of a small batch in one launch (the decode regime,
 // where every launch of the step counts; vLLM issue, section Problem: decode
-// is bound by weight streaming and dispatch count).  Each of the 16 waves
-// routes one token (route_common.h), writes its ids and weights out and
-// keeps the ids in LDS; the block then groups them as align_small_kernel
-// does.  Up to 16 tokens: with more, each wave would route several tokens
-// one after the other (64 tokens measured 44 us, against ~22 us for the
-// routing kernel's one wave per token on many blocks followed by the
-// single-block align).
+// is bound by weight streaming and dispatch count).  Up to 16 tokens, so at
+// most 256 pairs: each of the 16 waves routes one token (route_common.h) and
+// keeps its ids in LDS; then per-expert counts by LDS atomics, the
+// block_m-padded offsets by a block scan, each pair's rank inside its expert
+// by counting the earlier pairs with the same id (pair ids ascend with the
+// token, so this is the stable order), and per non-empty expert its tile
+// entries and sentinels.  No per-wave expert masks: with this few pairs the
+// mask clearing and per-expert popcounts of align_small_kernel (16 x E
+// words) cost more than the grouping itself.
 constexpr int kRouteAlignMaxT = kSmallWaves;
 
 template <int EPL>
@@ -354,20 +356,54 @@ __global__ __launch_bounds__(kSmallT) void route_align_small_kernel(
     int32_t* __restrict__ tile_expert, int32_t* __restrict__ offsets,
     int32_t* __restrict__ num_padded, int32_t* __restrict__ flags) {
   __shared__ int s_ids[kRouteAlignMaxT * 16];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  for (int t = wave; t < T; t += kSmallWaves) {  // one token per wave (T <= 16)
+  __shared__ int s_cnt[kMaxExperts];
+  __shared__ int s_off[kMaxExperts + 1];
+  __shared__ int s_wave[kSmallWaves];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int P = T * k;
+  const int bm = 1 << bm_shift;
+  for (int e = tid; e < E; e += kSmallT) s_cnt[e] = 0;
+  if (wave < T) {  // one token per wave
     int e;
     float w;
-    rt::route_token<EPL>(logits + (size_t)t * E, E, k, &e, &w);
+    rt::route_token<EPL>(logits + (size_t)wave * E, E, k, &e, &w);
     if (lane < k) {
-      ids[(size_t)t * k + lane] = e;
-      wts[(size_t)t * k + lane] = w;
-      s_ids[t * k + lane] = e;
+      ids[(size_t)wave * k + lane] = e;
+      wts[(size_t)wave * k + lane] = w;
+      s_ids[wave * k + lane] = e;
     }
   }
   __syncthreads();
-  align_small_body([&](int t, int j) { return s_ids[t * k + j]; }, T, k, E, bm_shift, cap,
-                   sorted, tile_expert, offsets, num_padded, flags);
+  const int my_e = tid < P ? s_ids[tid] : -1;  // the routing gives ids in [0, E)
+  if (tid < P) atomicAdd(&s_cnt[my_e], 1);
+  __syncthreads();
+  const int tot = tid < E ? s_cnt[tid] : 0;
+  const int pe = ((tot + bm - 1) >> bm_shift) << bm_shift;
+  const int off = block_excl_scan(pe, s_wave);
+  if (tid < E) {
+    s_off[tid] = off;
+    offsets[tid] = off;
+  }
+  if (tid == E - 1) {
+    s_off[E] = off + pe;
+    offsets[E] = off + pe;
+    *num_padded = off + pe;
+    *flags = 0;  // routed ids are in range and distinct within a token
+  }
+  __syncthreads();
+  if (tid < P) {
+    int rank = 0;
+    for (int q = 0; q < tid; q++) rank += s_ids[q] == my_e;
+    sorted[s_off[my_e] + rank] = tid;
+  }
+  if (tid < E && tot > 0) {
+    const int o = s_off[tid], end = s_off[tid + 1];
+    for (int i = o >> bm_shift; i < (end >> bm_shift); i++) tile_expert[i] = tid;
+    for (int i = o + tot; i < end; i++) sorted[i] = P;
+  }
+  const int npad = s_off[E];
+  for (int i = npad + tid; i < cap; i += kSmallT) sorted[i] = P;
+  for (int i = (npad >> bm_shift) + tid; i < (cap >> bm_shift); i += kSmallT) tile_expert[i] = -1;
 }
 
 // count + scan + scatter in two launches for nchunks <= kPlaceMaxChunks:
@@ -541,10 +577,9 @@ hipError_t launch_route_align(const float* logits, int T, int E, int k, int bloc
   if (T < 1 || T > kRouteAlignMaxT || k > 16 || E > kMaxExperts) return hipErrorInvalidValue;
   if (block_m < 16 || block_m > 128 || (block_m & (block_m - 1)) != 0) return hipErrorInvalidValue;
   const int bm_shift = __builtin_ctz((unsigned)block_m);
-  const size_t lds_small = (size_t)kSmallWaves * E * sizeof(unsigned long long);
 #define QMOE_RA_CASE(EPL)                                                                   \
   if (E <= 64 * EPL) {                                                                      \
-    hipLaunchKernelGGL(route_align_small_kernel<EPL>, dim3(1), dim3(kSmallT), lds_small, s, \
+    hipLaunchKernelGGL(route_align_small_kernel<EPL>, dim3(1), dim3(kSmallT), 0, s,         \
                        logits, T, k, E, bm_shift, cap, ids, w, sorted, tile_expert, offsets, \
                        num_padded, flags);                                                  \
     return hipGetLastError();                                                               \

@@ -3,8 +3,12 @@
 // memory or synchronises, except qmoe_check_flags.
 #include <hip/hip_runtime.h>
 
+#include <stdlib.h>
+#include <string.h>
+
 #include <algorithm>
 #include <mutex>
+#include <string>
 
 #include "qmoe.h"
 #include "qmoe_internal.h"
@@ -92,6 +96,78 @@ static FfnWs ffn_ws_layout(const qmoe_ffn_desc& d) {
   return w;
 }
 
+// ---------------------------------------------------------------------------
+// Tile configuration of one grouped-FFN call.  Every choice here changes
+// only how the work is split (tile heights, blocks, prefetch depth, column
+// passes), never the order or precision of a sum, so all give the same bits.
+struct TileCfg {
+  int s1_waves;   // stage-1 block: 4 or 8 waves (8 needs block_m >= 64); 0 = rule
+  int s1_ring;    // stage-1 weight prefetch ring: 0 = kernel's pick, 4 = four steps
+  int s1_runs;    // stage-1 schedule: -1 = rule, 0 = strided items, 1 = runs of row tiles
+  int s2_waves;   // row-major stage 2 (W4A16, W4A8, I > 1024): as s1_waves
+  int s2_passes;  // resident stage 2: column passes per work item; 0 = rule
+  int s2_half;    // resident stage 2: -1 = rule, 0 = whole tiles, 1 = half tiles
+};
+constexpr TileCfg kRuleCfg = {0, 0, -1, 0, 0, -1};
+
+struct TileRow {
+  int scheme, H, I, E, k, t_max, block_m;
+  TileCfg cfg;
+};
+static const TileRow kTileTable[] = {
+#include "tile_table.inc"
+    {-1, 0, 0, 0, 0, 0, 0, kRuleCfg}};  // end marker
+
+static const TileRow* table_row(int scheme, int T, int H, int I, int E, int k) {
+  for (const TileRow* r = kTileTable; r->scheme >= 0; r++)
+    if (r->scheme == scheme && r->H == H && r->I == I && r->E == E && r->k == k && T <= r->t_max)
+      return r;
+  return nullptr;
+}
+
+// Tile height by rule, from the mean rows per expert (pairs / E), where the
+// table has no row: up to 12 rows per expert 16; up to 40, 64 (one or two
+// tiles per expert); up to 96, 128 (one tile per expert, weights read once);
+// above, 64 (a second 128-row tile would be mostly padding), except a8w4
+// with an intermediate of 1024 or more above 128 rows, where 128-row tiles
+// taken in runs (an expert's second tile reads its weights from the
+// memory-side cache) measured faster.
+static int rule_block_m(int scheme, int T, int I, int E, int k) {
+  const double mean_rows = (double)T * k / E;
+  if (mean_rows <= 12) return 16;
+  if (mean_rows <= 40) return 64;
+  if (mean_rows <= 96) return 128;
+  if (scheme == QMOE_A8W4_MXFP4 && mean_rows > 128 && I >= 1024) return 128;
+  return 64;
+}
+
+// QMOE_TILE="s1w=8,s1r=4,s1runs=1,s2w=4,s2p=8,s2h=0" overrides fields of the
+// configuration (for tile sweeps).  Returns false on a malformed string.
+static bool parse_tile_env(TileCfg& c) {
+  const char* e = getenv("QMOE_TILE");
+  if (e == nullptr || *e == 0) return true;
+  const char* p = e;
+  while (*p) {
+    const char* eq = strchr(p, '=');
+    if (eq == nullptr) return false;
+    const std::string key(p, eq - p);
+    char* end = nullptr;
+    const long v = strtol(eq + 1, &end, 10);
+    if (end == eq + 1) return false;
+    if (key == "s1w") c.s1_waves = (int)v;
+    else if (key == "s1r") c.s1_ring = (int)v;
+    else if (key == "s1runs") c.s1_runs = (int)v;
+    else if (key == "s2w") c.s2_waves = (int)v;
+    else if (key == "s2p") c.s2_passes = (int)v;
+    else if (key == "s2h") c.s2_half = (int)v;
+    else return false;
+    p = end;
+    if (*p == ',') p++;
+    else if (*p != 0) return false;
+  }
+  return true;
+}
+
 // Block shape of the grouped GEMMs: sub-tiles per wave and waves per block.
 // 8-wave blocks (one per CU) halve the activation traffic per weight byte;
 // measured on the 128-row tiles they win for stage 1 of the 4-bit-weight
@@ -153,6 +229,14 @@ qmoe_status qmoe_route(const float* logits, int32_t T, int32_t E, int32_t k, int
   if (T == 0) return QMOE_OK;
   if (!logits || !topk_ids || !topk_w) return QMOE_ERR_INVALID_ARG;
   return hip_status(launch_route(logits, T, E, k, topk_ids, topk_w, (hipStream_t)stream));
+}
+
+int32_t qmoe_default_block_m(int32_t scheme, int32_t T, int32_t H, int32_t I, int32_t E,
+                             int32_t k) {
+  if (scheme < 0 || scheme > 3 || T < 0 || H <= 0 || I <= 0 || E < 1 || k < 1 || k > E)
+    return 0;
+  if (const TileRow* row = table_row(scheme, T, H, I, E, k)) return row->block_m;
+  return rule_block_m(scheme, T, I, E, k);
 }
 
 size_t qmoe_align_capacity(int32_t T, int32_t k, int32_t E, int32_t block_m) {
@@ -360,10 +444,27 @@ static qmoe_status grouped_ffn_impl(const qmoe_ffn_desc* d, const void* x, const
   g1.num_padded = num_padded;
   GemmArgs g2 = g1;
 
+  // Tile configuration: the table's row for this shape and token bucket
+  // when its block_m is the caller's, else the rules; QMOE_TILE overrides.
+  TileCfg cfg = kRuleCfg;
+  if (const TileRow* row = table_row(d->scheme, d->T, d->H, d->I, d->E, d->k))
+    if (row->block_m == d->block_m) cfg = row->cfg;
+  if (!parse_tile_env(cfg)) return QMOE_ERR_INVALID_ARG;
+  const bool resident = stage2_resident_ok(d->scheme, d->I);
+  GemmShape gs1 = choose_shape(d->scheme, 1, d->block_m);
+  GemmShape gs2 = choose_shape(d->scheme, 2, d->block_m);
+  auto waves_ok = [&](int w) { return w == 0 || w == 4 || (w == 8 && d->block_m >= 64); };
+  if (!waves_ok(cfg.s1_waves) || !waves_ok(cfg.s2_waves) ||
+      (cfg.s1_ring != 0 && cfg.s1_ring != 4) || cfg.s1_runs < -1 || cfg.s1_runs > 1 ||
+      cfg.s2_half < -1 || cfg.s2_half > 1 || cfg.s2_passes < 0 ||
+      (cfg.s2_half == 1 && (!resident || d->block_m < 32)) ||
+      (cfg.s2_passes > 0 && !resident) || (cfg.s2_waves != 0 && resident))
+    return QMOE_ERR_INVALID_ARG;
+  if (cfg.s1_waves) gs1.waves = cfg.s1_waves;
+  if (cfg.s2_waves) gs2.waves = cfg.s2_waves;
+
   g1.N = 2 * d->I;
   g1.K = d->H;
-  const GemmShape gs1 = choose_shape(d->scheme, 1, d->block_m);
-  const GemmShape gs2 = choose_shape(d->scheme, 2, d->block_m);
   g1.ntiles_n = d->I / stage_cols(1, gs1.nsub, gs1.waves);
   g1.a = x;
   g1.a_scale = x_scale;
@@ -380,17 +481,44 @@ static qmoe_status grouped_ffn_impl(const qmoe_ffn_desc* d, const void* x, const
                  (long)d->T * d->k > (long)d->E * d->block_m)
                     ? 1
                     : 0;
+  if (cfg.s1_runs >= 0) g1.schedule = cfg.s1_runs;
+  // Stage-2 work split, settled (and checked) before anything is launched.
+  // Where stage 1 takes runs of row tiles (several 128-row tiles per
+  // expert), stage 2 takes each tile as two 64-row work items.
+  const bool half_tiles =
+      resident && (cfg.s2_half >= 0 ? cfg.s2_half == 1 : g1.schedule == 1 && d->block_m >= 32);
+  int passes = 1;
+  if (resident) {
+    // Column passes per work item: as many as keep at least four items per
+    // CU (by the capacity's tile count), so every item copies its rows to
+    // LDS once for as many passes as possible.
+    g2.ntiles_n = d->H / stage2_resident_cols();
+    const long tiles = (long)cap / (half_tiles ? d->block_m / 2 : d->block_m);
+    for (int p = g2.ntiles_n; p >= 1; p--) {
+      if (g2.ntiles_n % p != 0 || p > stage2_resident_max_passes(d->scheme)) continue;
+      passes = p;
+      if (tiles * (g2.ntiles_n / p) >= 4L * device_cu_count()) break;
+    }
+    if (cfg.s2_passes > 0) {
+      if (g2.ntiles_n % cfg.s2_passes != 0 ||
+          cfg.s2_passes > stage2_resident_max_passes(d->scheme))
+        return QMOE_ERR_INVALID_ARG;
+      passes = cfg.s2_passes;
+    }
+  } else {
+    g2.ntiles_n = d->H / stage_cols(2, gs2.nsub, gs2.waves);
+  }
+
   auto mark = [&](int i) -> hipError_t {
     return events ? hipEventRecord((hipEvent_t)events[i], s) : hipSuccess;
   };
   hipError_t e = mark(0);
   const bool packed = (d->flags & QMOE_FLAG_PREPACKED) != 0;
   if (e == hipSuccess)
-    e = launch_gemm(d->scheme, 1, d->block_m, packed, gs1.nsub, gs1.waves, g1, s);
+    e = launch_gemm(d->scheme, 1, d->block_m, packed, gs1.nsub, gs1.waves, cfg.s1_ring, g1, s);
   if (e == hipSuccess) e = mark(1);
   if (e != hipSuccess) return hip_status(e);
 
-  const bool resident = stage2_resident_ok(d->scheme, d->I);
   // The resident stage 2 quantizes h itself while it copies each row tile
   // into LDS (one launch and one pass over h fewer) up to kFuseRequantPairs
   // pairs.  Beyond that its copy of fp32 rows, which no other block on the
@@ -411,24 +539,6 @@ static qmoe_status grouped_ffn_impl(const qmoe_ffn_desc* d, const void* x, const
   g2.schedule = 0;
   g2.N = d->H;
   g2.K = d->I;
-  // Where stage 1 takes runs of row tiles (several 128-row tiles per
-  // expert), stage 2 takes each tile as two 64-row work items.
-  const bool half_tiles = resident && g1.schedule == 1;
-  int passes = 1;
-  if (resident) {
-    // Column passes per work item: as many as keep at least four items per
-    // CU (by the capacity's tile count), so every item copies its rows to
-    // LDS once for as many passes as possible.
-    g2.ntiles_n = d->H / stage2_resident_cols();
-    const long tiles = (long)cap / (half_tiles ? d->block_m / 2 : d->block_m);
-    for (int p = g2.ntiles_n; p >= 1; p--) {
-      if (g2.ntiles_n % p != 0 || p > stage2_resident_max_passes(d->scheme)) continue;
-      passes = p;
-      if (tiles * (g2.ntiles_n / p) >= 4L * device_cu_count()) break;
-    }
-  } else {
-    g2.ntiles_n = d->H / stage_cols(2, gs2.nsub, gs2.waves);
-  }
   if (fuse_requant) {
     // fp32 h and the per-column-tile maxima; quantized in the row copy.
     g2.a = wsb + lay.h;
@@ -446,7 +556,7 @@ static qmoe_status grouped_ffn_impl(const qmoe_ffn_desc* d, const void* x, const
   g2.out = y_pairs;
   g2.dump = dump ? reinterpret_cast<int32_t*>(wsb + lay.acc2) : nullptr;
   e = resident ? launch_stage2_resident(d->scheme, d->block_m, half_tiles, packed, g2, passes, s)
-               : launch_gemm(d->scheme, 2, d->block_m, packed, gs2.nsub, gs2.waves, g2, s);
+               : launch_gemm(d->scheme, 2, d->block_m, packed, gs2.nsub, gs2.waves, 0, g2, s);
   if (e == hipSuccess) e = mark(3);
   return hip_status(e);
 }

@@ -48,8 +48,10 @@ hipError_t launch_align(const int32_t* ids, int T, int k, int E, int block_m, in
                         int32_t* tile_expert, int32_t* offsets, int32_t* num_padded,
                         int32_t* chunk_counts, int32_t* chunk_flags, int32_t* totals,
                         int32_t* flags, int cap, hipStream_t s);
+// ring: 0 = the depth the kernel picks (8 steps for tiles of up to 32 rows,
+// 16 for a8w4, when the K loop has a multiple of 8 steps; else 4), 4 = four.
 hipError_t launch_gemm(int scheme, int stage, int block_m, bool packed, int nsub, int waves,
-                       const GemmArgs& g, hipStream_t s);
+                       int ring, const GemmArgs& g, hipStream_t s);
 // Stage 2 with the tile's activation rows resident in LDS (gemm_s2.hip):
 // available for the one-byte-activation schemes with I <= 1024; its column
 // passes are stage2_resident_cols() wide and a work item covers `passes`

@@ -28,7 +28,7 @@ ABI_VERSION = 3
 EXPORTS = (
     "qmoe_abi_version", "qmoe_status_str", "qmoe_last_hip_error", "qmoe_route",
     "qmoe_align_capacity", "qmoe_align_workspace", "qmoe_align", "qmoe_check_flags",
-    "qmoe_align_noalloc", "qmoe_route_align",
+    "qmoe_align_noalloc", "qmoe_route_align", "qmoe_default_block_m",
     "qmoe_grouped_ffn_workspace", "qmoe_grouped_ffn_debug_offsets", "qmoe_grouped_ffn",
     "qmoe_grouped_ffn_profiled", "qmoe_combine", "qmoe_prepack",
 )
@@ -78,6 +78,8 @@ def _lib() -> ctypes.CDLL:
     L.qmoe_align_workspace.argtypes = [i32, i32, i32]
     L.qmoe_align.restype = ctypes.c_int
     L.qmoe_align.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+    L.qmoe_default_block_m.restype = ctypes.c_int32
+    L.qmoe_default_block_m.argtypes = [i32, i32, i32, i32, i32, i32]
     L.qmoe_route_align.restype = ctypes.c_int
     L.qmoe_route_align.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.qmoe_align_noalloc.restype = ctypes.c_int

@@ -116,32 +116,15 @@ def shape_by_name(name: str) -> MoEShape:
 
 
 def default_block_m(shape: MoEShape) -> int:
-    """Tile height for a shape, from the mean rows per expert (measured on
-    one MI355X for the workloads of the sweep).
+    """Tile height for a shape: the library's qmoe_default_block_m, i.e. the
+    gfx950 tile table's entry for the shape and token bucket (a sweep with a
+    bit-exact accuracy gate, ``bench.py --tile-sweep``), else its rule on the
+    mean rows per expert."""
+    from . import ops  # the library binding (loaded lazily: ops imports this module)
 
-    Row tiles never straddle experts and each row tile streams its expert's
-    weights once, so taller tiles read the weights fewer times but carry
-    more padding (skipped in 16-row groups).  Up to 12 rows per expert: 16.
-    Up to 40: 64 (one or two tiles per expert; 32 measured slower).  Up to
-    96: 128 (one tile per expert, weights read once).  Above 96 with an even
-    routing, 64: a second 128-row tile would be mostly padding; except for
-    a8w4 above 128 rows with the full intermediate (1024), where 128-row
-    tiles taken in runs of consecutive row tiles (an expert's second tile
-    reads its weights from the memory-side cache) measured faster; with a
-    tensor-parallel share of it (512, 256) 64 is faster there (5% and 9% at
-    8192 tokens).  Skewed routing keeps 128 for its heavy experts.
-
-    ``bench.py --tile-sweep`` times every block_m for the large a8w4 block
-    and its shares at each token bucket (1 to 8192 tokens); this rule is
-    within 2% of the fastest gated choice at every point of that table.
-    """
-    mean_rows = shape.pairs / shape.experts
-    if mean_rows <= 12:
-        return 16
-    if mean_rows <= 40:
-        return 64
-    if mean_rows <= 96 or shape.zipf_s:
-        return 128
-    if shape.scheme == "a8w4" and mean_rows > 128 and shape.inter >= 1024:
-        return 128
-    return 64
+    bm = int(ops.lib().qmoe_default_block_m(SCHEME_CODE[shape.scheme], shape.tokens,
+                                            shape.hidden, shape.inter, shape.experts,
+                                            shape.topk))
+    if bm == 0:
+        raise ValueError(f"no tile height for {shape}")
+    return bm

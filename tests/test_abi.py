@@ -210,3 +210,24 @@ def test_prepack_validation():
     assert L.qmoe_prepack(2, 2, 32, 256, a, b, c, None, None) == INV       # a8w4 needs scales_out
     assert L.qmoe_prepack(2, 2, 32, 256, a, b, ctypes.c_void_p(0x100010), d, None) == INV  # overlap
     assert L.qmoe_prepack(2, 2, 32, 256, ctypes.c_void_p(0x100008), b, c, d, None) == INV  # align
+
+
+def test_default_block_m_query():
+    """qmoe_default_block_m: the tile table's row where there is one, else
+    the rule on mean rows per expert; 0 for invalid arguments."""
+    L = ops.lib()
+    q = L.qmoe_default_block_m
+    # rule (shapes without a table row): mean rows per expert = T*k/E
+    assert q(2, 1, 2048, 1024, 500, 10) == 16        # 0.02 rows
+    assert q(2, 1000, 2048, 1024, 500, 10) == 64     # 20 rows
+    assert q(1, 2048, 2048, 768, 130, 8) == 64       # 126 rows, not a8w4
+    assert q(2, 4000, 2048, 1024, 500, 10) == 128    # 80 rows
+    assert q(2, 8000, 2048, 1024, 500, 10) == 128    # 160 rows, a8w4, inter 1024
+    assert q(2, 8000, 2048, 512, 500, 10) == 64      # 160 rows, a8w4 share
+    assert q(0, 8000, 2048, 1024, 500, 10) == 64     # 160 rows, not a8w4
+    # table rows: the skewed long prefill keeps 128-row tiles for its heavy
+    # experts, although its mean (160 rows) alone would give 64
+    assert q(0, 8192, 4096, 1024, 512, 10) == 128
+    for bad in ((4, 16, 256, 128, 8, 2), (0, -1, 256, 128, 8, 2), (0, 16, 256, 128, 8, 9),
+                (0, 16, 0, 128, 8, 2)):
+        assert q(*bad) == 0

@@ -594,6 +594,64 @@ def test_skewed_w4a16_t8192_every_token(prepacked):
     _parity_large(W4A16_SKEWED, 8192, prepacked)
 
 
+# ------------------------------------------------------------------ tile configurations
+
+TILE_OVERRIDES = ["s1w=4", "s1w=8", "s1r=4", "s1runs=0", "s1runs=1", "s2w=8", "s2p=1",
+                  "s2p=2", "s2p=8", "s2h=0", "s2h=1", "s1w=8,s1runs=1,s2p=4,s2h=1"]
+
+
+@pytest.mark.parametrize("scheme,I,bm", [("a8w4", 256, 64), ("a8w4", 256, 128),
+                                         ("w4a16", 256, 128), ("w4a8", 256, 64),
+                                         ("w8a8", 256, 16)])
+def test_tile_overrides_give_the_same_bits(scheme, I, bm, monkeypatch):
+    """Every tile configuration the sweep may pick (QMOE_TILE) splits the
+    work differently but keeps the order and precision of every sum: the
+    outputs equal the default configuration's bit for bit.  Settings that do
+    not apply to the call, and malformed strings, are refused before
+    anything is launched."""
+    sh = MoEShape(f"tiles_{scheme}", scheme, tokens=700, hidden=512, inter=I, experts=8,
+                  topk=2, seed=71)
+    _flush(f"tile overrides {scheme} bm={bm}")
+    inp = synth.make_inputs(sh)
+    g = gpu_inputs(inp)
+    W = ops.prepack_weights(scheme, {k: g[k] for k in WEIGHT_KEYS})
+    f32 = scheme == "w8a8"
+
+    def run():
+        r = ops.moe_forward(scheme, g["logits"], g["x"], g["x_scale"], W, sh.topk, bm,
+                            want_f32=f32)
+        torch.cuda.synchronize()
+        return r["out"].clone(), (r["out_f32"].clone() if f32 else None)
+
+    monkeypatch.delenv("QMOE_TILE", raising=False)
+    ref = run()
+    resident = scheme in ("a8w4", "w8a8")
+    tried = 0
+    for ov in TILE_OVERRIDES:
+        monkeypatch.setenv("QMOE_TILE", ov)
+        fields = dict(kv.split("=") for kv in ov.split(","))
+        applies = True
+        if ("s1w" in fields and fields["s1w"] == "8" and bm < 64) or \
+           ("s2w" in fields and (resident or bm < 64)) or \
+           ("s2h" in fields and fields["s2h"] == "1" and (not resident or bm < 32)) or \
+           ("s2p" in fields and (not resident or (sh.hidden // 256) % int(fields["s2p"]))):
+            applies = False
+        if not applies:
+            with pytest.raises(ops.QmoeError):
+                run()
+            continue
+        got = run()
+        assert torch.equal(got[0], ref[0]), ov
+        if f32:
+            assert torch.equal(got[1], ref[1]), ov
+        tried += 1
+    assert tried >= 4
+    for bad in ("bogus", "s1w=", "s1w=3", "s2p=3", "s1r=6", "s1w=4;s2p=2"):
+        monkeypatch.setenv("QMOE_TILE", bad)
+        with pytest.raises(ops.QmoeError):
+            run()
+
+
 # ------------------------------------------------------------------ prepack layout
 
 def _np_prepack(scheme, codes, scales):
