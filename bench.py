@@ -170,11 +170,14 @@ def cpu_baseline(shape, inp, target_s: float = 15.0) -> dict:
             "tokens_per_s": total_tok / elapsed}
 
 
-SWEEP = ("w4a16_qwen3moe_t128", "w8a8_t2048", "a8w4_large@T1", "a8w4_large@T4",
-         "a8w4_large@T16", "a8w4_large@T64", "a8w4_large@T256",
+SWEEP = ("w4a16_qwen3moe_t128", "w8a8_t2048", "a8w4_large@T1", "a8w4_large@T2",
+         "a8w4_large@T4", "a8w4_large@T16", "a8w4_large@T64", "a8w4_large@T256",
          "a8w4_large@T1024", "a8w4_large@T4096", "a8w4_large@T8192", "a8w4_tp2@T4096",
          "a8w4_tp4@T4096", "w4a16_skewed_t8192", "w4a8_qwen3moe_t128", "w4a8_t2048",
          "w4a8_skewed_t8192")
+# Batches the sweep also runs through the other path (the one-launch
+# qmoe_decode above 2 tokens, the multi-launch path at 1-2 tokens).
+SWEEP_BOTH_PATHS = ("a8w4_large@T1", "a8w4_large@T2", "a8w4_large@T4", "a8w4_large@T16")
 
 
 def stage_flops(shape) -> dict:
@@ -184,20 +187,25 @@ def stage_flops(shape) -> dict:
             "stage2": 2.0 * shape.hidden * shape.inter * P, "combine": 0.0}
 
 
-def graph_step_ms(torch, ops, args, flush, b: dict, eager_step):
-    """Mean and median GPU time of one step run as a HIP graph: the four
-    launches (route, align, grouped FFN, combine) captured once and replayed,
-    so that no host launch gap sits between them.  The cache flush stays
-    outside the graph and outside the events.  The last replay's outputs
-    must equal a following eager step's bit for bit."""
-    sh, g, E, k = b["shape"], b["g"], b["shape"].experts, b["shape"].topk
+def graph_step_ms(torch, ops, args, flush, b: dict, eager_step, body=None, outs=None):
+    """Mean and median GPU time of one step run as a HIP graph: the step's
+    launches (route and align, grouped FFN, combine; or the one decode
+    launch: ``body``) captured once and replayed, so that no host launch gap
+    sits between them.  The cache flush stays outside the graph and outside
+    the events.  The last replay's outputs must equal a following eager
+    step's bit for bit."""
+    sh = b["shape"]
+    if body is None:
+        g, E, k = b["g"], sh.experts, sh.topk
 
-    def body():
-        ops.route_align(g["logits"], k, b["bm"], b["ids"], b["tw"], out=b["al"])
-        ops.grouped_ffn(sh.scheme, g["x"], g["x_scale"], b["W"], b["al"], E, k, ws=b["ws"],
-                        y_pairs=b["y"])
-        ops.combine(b["y"], b["tw"], out_bf16=b["out_bf16"], out_f32=b["out_f32"],
-                    want_f32=b["out_f32"] is not None)
+        def body():
+            ops.route_align(g["logits"], k, b["bm"], b["ids"], b["tw"], out=b["al"])
+            ops.grouped_ffn(sh.scheme, g["x"], g["x_scale"], b["W"], b["al"], E, k,
+                            ws=b["ws"], y_pairs=b["y"])
+            ops.combine(b["y"], b["tw"], out_bf16=b["out_bf16"], out_f32=b["out_f32"],
+                        want_f32=b["out_f32"] is not None)
+    if outs is None:
+        outs = [t for t in (b["out_bf16"], b["out_f32"]) if t is not None]
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -230,15 +238,121 @@ def graph_step_ms(torch, ops, args, flush, b: dict, eager_step):
         ev[0][1].record()
         torch.cuda.synchronize()
         ms = np.array([ev[0][0].elapsed_time(ev[0][1]) / args.steps])
-    got = [t.clone() for t in (b["out_bf16"], b["out_f32"]) if t is not None]
+    got = [t.clone() for t in outs]
     eager_step()
     torch.cuda.synchronize()
-    want = [t for t in (b["out_bf16"], b["out_f32"]) if t is not None]
-    if not all(torch.equal(x, y) for x, y in zip(got, want)):
+    if not all(torch.equal(x, y) for x, y in zip(got, outs)):
         raise SystemExit("bench: graph replay output differs from the eager step")
     del graph
     log(f"{sh.name}: graph step {float(ms.mean()):.4f} ms")
     return float(ms.mean()), float(np.median(ms))
+
+
+def roofline_of(shape, dom: str, kern_ms: float, nbytes: float, flops: float) -> dict:
+    """Roofline entry of the dominant kernel: its bound from the arithmetic
+    intensity against the ridge point peak_flops / peak_bandwidth."""
+    peak_tf = MFMA_PEAK_TFLOPS[shape.scheme]
+    if flops / nbytes > peak_tf * 1e12 / (HBM_PEAK_GBS * 1e9):
+        achieved = flops / (kern_ms * 1e-3) / 1e12
+        return {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak_tf,
+                "unit": "TFLOP/s", "frac": round(achieved / peak_tf, 4)}
+    achieved = nbytes / (kern_ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+
+
+def run_decode_workload(shape, inp, g, W, layout, args, torch, with_cpu, cpu_seconds) -> dict:
+    """A batch of up to 16 tokens through qmoe_decode: the whole layer in one
+    launch (routing from the logits to the combined output)."""
+    from quantized_mixture_experts_moe_amd import ops
+
+    T, E, k, H = shape.tokens, shape.experts, shape.topk, shape.hidden
+    dev = torch.device("cuda:0")
+    f32 = shape.scheme == "w8a8"
+    r = ops.decode_forward(shape.scheme, g["logits"], g["x"], g["x_scale"], W, k, want_f32=f32,
+                           want_y=False)
+    ws = r["ws"]
+    out = {key: r[key] for key in ("topk_ids", "topk_w", "out", "out_f32")}
+    torch.cuda.synchronize()
+    touched = int(torch.unique(out["topk_ids"]).numel())
+    flush = None if args.no_flush else torch.ones(64 << 20, dtype=torch.int64, device=dev)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for row in evs:
+        for e in row:
+            e.record()
+    torch.cuda.synchronize()
+
+    def launch():
+        ops.decode_forward(shape.scheme, g["logits"], g["x"], g["x_scale"], W, k, want_f32=f32,
+                           ws=ws, want_y=False, out=out)
+
+    def step(ev=None):
+        if flush is not None:
+            torch.amax(flush)
+        if ev is not None:
+            ev[0].record()
+        launch()
+        if ev is not None:
+            ev[1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    step_ms = np.array([evs[i][0].elapsed_time(evs[i][1]) for i in range(args.steps)])
+    # One launch per step: the events around it give the step's GPU time; a
+    # HIP graph of a single kernel only adds the graph launch (reported
+    # apart as ms_per_step_graph).
+    eager_ms = float(step_ms.mean()) if flush is not None else wall_ms
+    ms_per_step = eager_ms
+    graph_ms = None
+    outs = [t for t in (out["out"], out["out_f32"]) if t is not None]
+    if not args.eager:
+        graph_ms, _ = graph_step_ms(torch, ops, args, flush, dict(shape=shape), launch,
+                                    body=launch, outs=outs)
+    if ops.check_flags(ws) != 0:
+        raise SystemExit("bench: the decode kernel reported a timed-out wait")
+    kern = {"decode": float(step_ms.mean())}
+    log(f"{shape.name}: one-launch decode kernel {kern['decode']:.4f} ms (eager events)")
+    flops = shape.useful_flops()
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    ab = algorithmic_bytes(shape, touched)
+    roof = roofline_of(shape, "decode", kern["decode"], ab["step"], flops)
+    roof.update({"traffic": None, "kernel": f"decode ({shape.scheme}, one launch)",
+                 "kernel_ms": round(kern["decode"], 4), "algorithmic_bytes": int(ab["step"]),
+                 "algorithmic_flops": flops})
+    step_gbs = ab["step"] / (ms_per_step * 1e-3) / 1e9
+    res = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": DTYPE[shape.scheme], "data": "synthetic (seeded generator, weights random)",
+        "config": {"workload": shape.name, "scheme": shape.scheme, "tokens": T, "hidden": H,
+                   "inter": shape.inter, "experts": E, "topk": k, "path": "qmoe_decode",
+                   "touched_experts": touched, "weight_layout": layout,
+                   "cache_flush_between_steps": flush is not None,
+                   "parallelism": "none (1 GPU)"},
+        "ms_per_step_median": round(float(np.median(step_ms)), 4),
+        "timing": "HIP events around the step's one launch",
+        "ms_per_step_eager": round(eager_ms, 4),
+        "ms_per_step_graph": None if graph_ms is None else round(graph_ms, 4),
+        "wall_ms_per_step": round(wall_ms, 4),
+        "tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
+        "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
+        "step_mfma_frac": round(tflops / MFMA_PEAK_TFLOPS[shape.scheme], 4),
+        "kernel_ms": {n: round(v, 4) for n, v in kern.items()},
+        "roofline": roof,
+        "ms_per_step_stat": "mean over the timed steps (median in ms_per_step_median)",
+    }
+    if with_cpu:
+        res["cpu_baseline"] = cpu_baseline(shape, inp, cpu_seconds)
+    del ws, flush
+    torch.cuda.empty_cache()
+    return res
 
 
 def run_workload(name: str, args, torch, with_cpu: bool, cpu_seconds: float = 20.0) -> dict:
@@ -267,6 +381,10 @@ def run_workload(name: str, args, torch, with_cpu: bool, cpu_seconds: float = 20
         for key in ("w13", "w13_scale", "w2", "w2_scale"):
             del g[key]
     T, E, k, H = shape.tokens, shape.experts, shape.topk, shape.hidden
+    one_launch = (T <= ops.DECODE_MAX_TOKENS and args.decode) or \
+        (T <= ops.DECODE_PREFERRED_MAX_TOKENS and not args.grouped)
+    if one_launch:
+        return run_decode_workload(shape, inp, g, W, layout, args, torch, with_cpu, cpu_seconds)
     ids = torch.empty((T, k), dtype=torch.int32, device=dev)
     tw = torch.empty((T, k), dtype=torch.float32, device=dev)
     _, _, al = ops.route_align(g["logits"], k, bm, ids, tw)
@@ -336,18 +454,7 @@ def run_workload(name: str, args, torch, with_cpu: bool, cpu_seconds: float = 20
     sf = stage_flops(shape)
     dom = max(("stage1", "stage2", "combine"), key=lambda n: kern[n])
     peak_tf = MFMA_PEAK_TFLOPS[shape.scheme]
-    # Bound of the dominant kernel: arithmetic intensity against the ridge
-    # point peak_flops / peak_bandwidth.
-    ai = sf[dom] / ab[dom]
-    mfma_bound = ai > peak_tf * 1e12 / (HBM_PEAK_GBS * 1e9)
-    if mfma_bound:
-        achieved = sf[dom] / (kern[dom] * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak_tf,
-                "unit": "TFLOP/s", "frac": round(achieved / peak_tf, 4)}
-    else:
-        achieved = ab[dom] / (kern[dom] * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    roof = roofline_of(shape, dom, kern[dom], ab[dom], sf[dom])
     traffic = None
     c = DOMINANT_COUNTERS
     if (dom == c["kernel"] and shape.name == c["workload"] and bm == c["block_m"]
@@ -365,6 +472,7 @@ def run_workload(name: str, args, torch, with_cpu: bool, cpu_seconds: float = 20
         "dtype": DTYPE[shape.scheme], "data": "synthetic (seeded generator, weights random)",
         "config": {"workload": shape.name, "scheme": shape.scheme, "tokens": T, "hidden": H,
                    "inter": shape.inter, "experts": E, "topk": k, "block_m": bm,
+                   "path": "route_align + grouped_ffn + combine",
                    "touched_experts": touched, "weight_layout": layout,
                    "cache_flush_between_steps": flush is not None,
                    "parallelism": "none (1 GPU)"},
@@ -571,6 +679,12 @@ def main():
                          "layout qmoe_prepack writes once at set-up, outside the timed steps)")
     ap.add_argument("--no-flush", action="store_true",
                     help="no cache flush between timed steps (steps run back to back)")
+    ap.add_argument("--grouped", action="store_true",
+                    help="batches of up to 2 tokens take the multi-launch path (route and "
+                         "align, grouped FFN, combine) instead of the one-launch qmoe_decode")
+    ap.add_argument("--decode", action="store_true",
+                    help="batches of up to 16 tokens take the one-launch qmoe_decode (the "
+                         "default choice sends only batches of up to 2 tokens there)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -605,6 +719,11 @@ def main():
         for name in SWEEP:
             print(json.dumps(run_workload(name, args, torch, not args.no_cpu_baseline,
                                           min(args.cpu_seconds, 8.0))), flush=True)
+            if name in SWEEP_BOTH_PATHS:
+                other = argparse.Namespace(**vars(args))
+                t = int(name.split("@T")[1])
+                other.grouped, other.decode = t <= 2, t > 2
+                print(json.dumps(run_workload(name, other, torch, False)), flush=True)
         return
     res = run_workload(args.workload, args, torch, not args.no_cpu_baseline, args.cpu_seconds)
     print(json.dumps(res), flush=True)

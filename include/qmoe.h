@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define QMOE_ABI_VERSION 3
+#define QMOE_ABI_VERSION 4
 
 typedef enum {
   QMOE_OK = 0,
@@ -291,6 +291,48 @@ qmoe_status qmoe_grouped_ffn_profiled(const qmoe_ffn_desc* d, const void* x,
 qmoe_status qmoe_combine(const void* y_pairs, int32_t y_dtype, const float* topk_w,
                          int32_t T, int32_t k, int32_t H, uint16_t* out_bf16,
                          float* out_f32, void* stream);
+
+/* ---------------------------------------------------------------------
+ * qmoe_decode -- the whole layer for a small batch in ONE launch: routing
+ * as qmoe_route, the grouping of the pairs by expert, stage 1 with the
+ * fused silu(gate)*up epilogue, the scheme's requantization of h, stage 2
+ * and the weighted combine as qmoe_combine.  In the decode regime every
+ * expert GEMM has at most a few rows and the step is bound by weight
+ * streaming and by the number of dependent launches (vLLM issue, section
+ * Problem; aiter PR 6090, section Changes: token bucket 1-256); the
+ * kernel resolves the dependencies between the steps inside the launch.
+ * topk_ids, topk_w, y_pairs, out_bf16 and out_f32 equal those of
+ * qmoe_route -> qmoe_align -> qmoe_grouped_ffn -> qmoe_combine bit for bit.
+ * d: scheme, T (1..QMOE_DECODE_MAX_TOKENS; 0 launches nothing), H, I, E, k
+ *   (k <= 16) and flags (QMOE_FLAG_PREPACKED only) as for
+ *   qmoe_grouped_ffn; block_m is not used.
+ * logits fp32 [T,E]; x, x_scale and w as for qmoe_grouped_ffn.
+ * topk_ids int32 [T,k], topk_w fp32 [T,k]: written (as qmoe_route).
+ * y_pairs: optional [T*k, H] (bf16; fp32 for W8A8), row = pair: written
+ *   when non-NULL (the workspace holds them otherwise).
+ * out_bf16 / out_f32 [T,H]: at least one non-NULL.
+ * ws: qmoe_decode_workspace(d) bytes, 256-byte aligned, ZEROED ONCE before
+ *   its first use (it holds arrival counters; every call that completes
+ *   leaves them zero, so the same workspace serves any number of calls
+ *   ordered on one stream, for every T of the same H, I, E, k, scheme).
+ *   Calls that overlap in time must not share a workspace.  Its flag word
+ *   (qmoe_check_flags(ws, ...)) gets bit 2 if a wait inside the kernel ran
+ *   out of time (100 ms; it cannot happen while the kernel's units run in
+ *   launch order, and means the outputs are wrong and the workspace must be
+ *   zeroed again).
+ * Requirements as for qmoe_grouped_ffn.  QMOE_ERR_UNSUPPORTED for T above
+ * QMOE_DECODE_MAX_TOKENS or E above 1024; QMOE_ERR_INVALID_ARG for null
+ * pointers, a short workspace, bad sizes, flags other than
+ * QMOE_FLAG_PREPACKED, a QMOE_DECODE_RING environment value other than 4
+ * or 6 (the K loops' prefetch depth) or a QMOE_DECODE_G value other than
+ * 1, 2, 4 or 8 dividing H / 128 (32-column chunks per stage-2 work unit);
+ * both only change how the work is split, for measurements.             */
+#define QMOE_DECODE_MAX_TOKENS 16
+size_t qmoe_decode_workspace(const qmoe_ffn_desc* d);
+qmoe_status qmoe_decode(const qmoe_ffn_desc* d, const float* logits, const void* x,
+                        const float* x_scale, const qmoe_weights* w, int32_t* topk_ids,
+                        float* topk_w, void* y_pairs, uint16_t* out_bf16, float* out_f32,
+                        void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -202,6 +202,52 @@ static qmoe_status check_desc(const qmoe_ffn_desc* d) {
   return QMOE_OK;
 }
 
+// Descriptor check of qmoe_decode (block_m is not used).
+static qmoe_status check_decode_desc(const qmoe_ffn_desc* d) {
+  if (d == nullptr) return QMOE_ERR_INVALID_ARG;
+  if (d->scheme < 0 || d->scheme > 3) return QMOE_ERR_INVALID_ARG;
+  if (d->T < 0 || d->H <= 0 || d->I <= 0 || d->E <= 0 || d->k < 1 || d->k > d->E || d->k > 16)
+    return QMOE_ERR_INVALID_ARG;
+  if (d->H % 32 != 0 || d->I % 32 != 0) return QMOE_ERR_INVALID_ARG;
+  if (d->flags & ~QMOE_FLAG_PREPACKED) return QMOE_ERR_INVALID_ARG;
+  if (d->T > decode_max_tokens() || d->E > 1024) return QMOE_ERR_UNSUPPORTED;
+  if (d->H % 256 != 0) return QMOE_ERR_UNSUPPORTED;
+  if (d->I % (d->scheme == QMOE_A8W4_MXFP4 ? 256 : 128) != 0) return QMOE_ERR_UNSUPPORTED;
+  // One expert's W13 or W2 codes are addressed with 32-bit byte offsets.
+  const uint64_t wrow = d->scheme == QMOE_W8A8_PERCHAN ? 2 : 1;  // weight bytes per 2 elements
+  if ((uint64_t)2 * d->I * d->H * wrow / 2 >= (1ull << 32)) return QMOE_ERR_UNSUPPORTED;
+  return QMOE_OK;
+}
+
+// A wait inside the decode kernel gives up after 100 ms of the device's
+// constant-rate clock.
+static uint64_t decode_spin_ticks() {
+  static std::mutex mu;
+  static uint64_t cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cached[dev] == 0) {
+    int khz = 0;
+    if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess ||
+        khz < 1)
+      khz = 100000;
+    cached[dev] = (uint64_t)khz * 100;
+  }
+  return cached[dev];
+}
+
+// Prefetch depth of the decode kernel's K loops: QMOE_DECODE_RING (4 or 6)
+// or 4.  0 for an invalid value.  (QMOE_DECODE_G, read in qmoe_decode,
+// overrides the stage-2 chunks per unit for measurements.)
+static int decode_ring() {
+  const char* e = getenv("QMOE_DECODE_RING");
+  if (e == nullptr || *e == 0) return 4;
+  if (strcmp(e, "4") == 0) return 4;
+  if (strcmp(e, "6") == 0) return 6;
+  return 0;
+}
+
 }  // namespace qmoe
 
 using namespace qmoe;
@@ -623,6 +669,46 @@ qmoe_status qmoe_combine(const void* y_pairs, int32_t y_dtype, const float* topk
     return QMOE_ERR_INVALID_ARG;
   return hip_status(launch_combine(y_pairs, y_dtype == QMOE_DT_F32, topk_w, T, k, H, out_bf16,
                                    out_f32, (hipStream_t)stream));
+}
+
+size_t qmoe_decode_workspace(const qmoe_ffn_desc* d) {
+  if (check_decode_desc(d) != QMOE_OK) return 0;
+  return decode_ws_layout(d->scheme, d->H, d->I, d->E, d->k).total;
+}
+
+qmoe_status qmoe_decode(const qmoe_ffn_desc* d, const float* logits, const void* x,
+                        const float* x_scale, const qmoe_weights* w, int32_t* topk_ids,
+                        float* topk_w, void* y_pairs, uint16_t* out_bf16, float* out_f32,
+                        void* ws, size_t ws_bytes, void* stream) {
+  const qmoe_status st = check_decode_desc(d);
+  if (st != QMOE_OK) return st;
+  if (d->T == 0) return QMOE_OK;
+  const bool quant_act = d->scheme != QMOE_W4A16_G32;
+  if (!logits || !x || !w || !w->w13 || !w->w13_scale || !w->w2 || !w->w2_scale || !topk_ids ||
+      !topk_w || !ws || (quant_act && !x_scale) || (!out_bf16 && !out_f32))
+    return QMOE_ERR_INVALID_ARG;
+  const size_t scale_align = d->scheme == QMOE_W4A8_G32 ? 8 : 4;
+  if (!aligned(x, 16) || !aligned(w->w13, 16) || !aligned(w->w2, 16) || !aligned(ws, 256) ||
+      !aligned(w->w13_scale, scale_align) || !aligned(w->w2_scale, scale_align) ||
+      (y_pairs && !aligned(y_pairs, 16)))
+    return QMOE_ERR_INVALID_ARG;
+  if (ws_bytes < decode_ws_layout(d->scheme, d->H, d->I, d->E, d->k).total)
+    return QMOE_ERR_INVALID_ARG;
+  const int ring = decode_ring();
+  if (ring == 0) return QMOE_ERR_INVALID_ARG;
+  int chunks = decode_stage2_chunks(d->T, d->H, d->E, d->k);
+  if (const char* e = getenv("QMOE_DECODE_G"); e != nullptr && *e != 0) {
+    chunks = atoi(e);
+    if ((chunks != 1 && chunks != 2 && chunks != 4 && chunks != 8) ||
+        (d->H / 32) % (4 * chunks) != 0)
+      return QMOE_ERR_INVALID_ARG;
+  }
+  return hip_status(launch_decode(d->scheme, (d->flags & QMOE_FLAG_PREPACKED) != 0, ring,
+                                  chunks, d->T,
+                                  d->H, d->I, d->E, d->k, logits, x, x_scale, w->w13,
+                                  w->w13_scale, w->w2, w->w2_scale, topk_ids, topk_w, y_pairs,
+                                  out_bf16, out_f32, ws, decode_spin_ticks(),
+                                  (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -83,4 +83,26 @@ hipError_t launch_route_align(const float* logits, int T, int E, int k, int bloc
                               hipStream_t s);
 int device_cu_count();
 
+// The whole layer for up to decode_max_tokens() tokens in one launch
+// (decode.hip).  Workspace byte offsets; the first counter_bytes hold the
+// counters, which must be zero before the first call (every completed call
+// leaves them zero).
+struct DecodeWs {
+  size_t flags, route_cnt, slot_flag, slot_rec, s1cnt, ready, ccnt, counter_bytes;
+  size_t h32, pmax, hs, hq, y, total;
+};
+int decode_max_tokens();
+DecodeWs decode_ws_layout(int scheme, int H, int I, int E, int k);
+// ring: weight + activation prefetch depth of a unit's K loop (4 or 6);
+// chunks: 32-column chunks per stage-2 unit (1, 2, 4 or 8, with H / 32 a
+// multiple of 4 * chunks).
+int decode_stage2_chunks(int T, int H, int E, int k);
+hipError_t launch_decode(int scheme, bool packed, int ring, int chunks, int T, int H, int I,
+                         int E, int k,
+                         const float* logits, const void* x, const float* x_scale,
+                         const void* w13, const void* w13_scale, const void* w2,
+                         const void* w2_scale, int32_t* topk_ids, float* topk_w, void* y,
+                         uint16_t* out_bf16, float* out_f32, void* ws, uint64_t spin_ticks,
+                         hipStream_t s);
+
 }  // namespace qmoe

@@ -22,7 +22,7 @@ QMOE_FLAG_DUMP_ACC = 1
 QMOE_FLAG_PREPACKED = 2
 # QMOE_ABI_VERSION of the include/qmoe.h this binding follows; loading a
 # library that reports another version fails.
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 # Every symbol include/qmoe.h declares.
 EXPORTS = (
@@ -30,8 +30,17 @@ EXPORTS = (
     "qmoe_align_capacity", "qmoe_align_workspace", "qmoe_align", "qmoe_check_flags",
     "qmoe_align_noalloc", "qmoe_route_align", "qmoe_default_block_m",
     "qmoe_grouped_ffn_workspace", "qmoe_grouped_ffn_debug_offsets", "qmoe_grouped_ffn",
-    "qmoe_grouped_ffn_profiled", "qmoe_combine", "qmoe_prepack",
+    "qmoe_grouped_ffn_profiled", "qmoe_combine", "qmoe_prepack", "qmoe_decode_workspace",
+    "qmoe_decode",
 )
+# Largest batch qmoe_decode takes (QMOE_DECODE_MAX_TOKENS).
+DECODE_MAX_TOKENS = 16
+# Batches up to this size take the one-launch qmoe_decode in moe_forward's
+# automatic choice: measured on one MI355X for the 512-expert top-10 a8w4
+# block, the one launch is faster at 1 and 2 tokens (45.8 against 47.2 us,
+# 61.4 against 65.4 us), even at 4 and slower from 8 tokens on, where the
+# grouped kernels stream the weights at a higher rate.
+DECODE_PREFERRED_MAX_TOKENS = 2
 
 
 class QmoeError(RuntimeError):
@@ -102,6 +111,11 @@ def _lib() -> ctypes.CDLL:
     L.qmoe_combine.argtypes = [vp, i32, vp, i32, i32, i32, vp, vp, vp]
     L.qmoe_prepack.restype = ctypes.c_int
     L.qmoe_prepack.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp]
+    L.qmoe_decode_workspace.restype = sz
+    L.qmoe_decode_workspace.argtypes = [ctypes.POINTER(FfnDesc)]
+    L.qmoe_decode.restype = ctypes.c_int
+    L.qmoe_decode.argtypes = [ctypes.POINTER(FfnDesc), vp, vp, vp, ctypes.POINTER(Weights), vp,
+                              vp, vp, vp, vp, vp, sz, vp]
     _LIB = L
     return L
 
@@ -346,9 +360,17 @@ def combine(y_pairs: torch.Tensor, topk_w: torch.Tensor, want_bf16: bool = True,
 
 def moe_forward(scheme: str, logits: torch.Tensor, x: torch.Tensor,
                 x_scale: Optional[torch.Tensor], weights: dict, k: int, block_m: int,
-                flags: int = 0, want_f32: bool = False, fused_routing: bool = False) -> dict:
+                flags: int = 0, want_f32: bool = False, fused_routing: bool = False,
+                path: str = "grouped") -> dict:
     """route -> align -> grouped_ffn -> combine, all on the current stream
-    (``fused_routing``: route and align through qmoe_route_align)."""
+    (``fused_routing``: route and align through qmoe_route_align).
+    ``path="auto"`` sends batches of up to DECODE_PREFERRED_MAX_TOKENS tokens
+    (without debug flags) to the one-launch qmoe_decode instead; its outputs
+    are the same bits."""
+    if path not in ("grouped", "auto"):
+        raise ValueError(f"path must be 'grouped' or 'auto', not {path!r}")
+    if path == "auto" and flags == 0 and 0 < x.shape[0] <= DECODE_PREFERRED_MAX_TOKENS:
+        return decode_forward(scheme, logits, x, x_scale, weights, k, want_f32=want_f32)
     E = logits.shape[1]
     if fused_routing:
         ids, w, al = route_align(logits, k, block_m)
@@ -359,3 +381,58 @@ def moe_forward(scheme: str, logits: torch.Tensor, x: torch.Tensor,
     out_bf16, out_f32 = combine(y, w, want_bf16=True, want_f32=want_f32)
     return {"topk_ids": ids, "topk_w": w, "align": al, "y_pairs": y, "ws": ws,
             "out": out_bf16, "out_f32": out_f32}
+
+
+# ---------------------------------------------------------------- one-launch decode
+
+def decode_workspace(scheme: str, H: int, I: int, E: int, k: int, flags: int = 0) -> int:
+    """qmoe_decode_workspace (bytes; sized for every T up to DECODE_MAX_TOKENS)."""
+    return int(_lib().qmoe_decode_workspace(ctypes.byref(make_desc(scheme, 1, H, I, E, k, 16,
+                                                                   flags))))
+
+
+def decode_forward(scheme: str, logits: torch.Tensor, x: torch.Tensor,
+                   x_scale: Optional[torch.Tensor], weights: dict, k: int,
+                   want_f32: bool = False, ws: Optional[torch.Tensor] = None,
+                   y_pairs: Optional[torch.Tensor] = None, want_y: bool = True,
+                   out: Optional[dict] = None) -> dict:
+    """qmoe_decode: the whole layer in one launch for T <= DECODE_MAX_TOKENS.
+    ``ws`` must come from a previous call (or be zero-filled): the library
+    keeps arrival counters in it that each call leaves at zero."""
+    T, H = x.shape
+    E = logits.shape[1]
+    I = weights["w13"].shape[1] // 2
+    dev = x.device
+    flags = QMOE_FLAG_PREPACKED if weights.get("prepacked", False) else 0
+    desc = make_desc(scheme, T, H, I, E, k, 16, flags)
+    need = int(_lib().qmoe_decode_workspace(ctypes.byref(desc)))
+    if need == 0:
+        raise QmoeError(QMOE_ERR_INVALID_ARG if T <= DECODE_MAX_TOKENS else QMOE_ERR_UNSUPPORTED,
+                        "qmoe_decode_workspace")
+    if ws is None or ws.numel() < need:
+        ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+    out = {} if out is None else out
+    ids = out.get("topk_ids")
+    if ids is None:
+        ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = out.get("topk_w")
+    if w is None:
+        w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    if want_y and y_pairs is None:
+        ydt = torch.float32 if scheme == "w8a8" else torch.bfloat16
+        y_pairs = torch.empty((T * k, H), dtype=ydt, device=dev)
+    ob = out.get("out")
+    if ob is None:
+        ob = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    of = out.get("out_f32")
+    if want_f32 and of is None:
+        of = torch.empty((T, H), dtype=torch.float32, device=dev)
+    wts = Weights(_ptr(weights["w13"]), _ptr(weights["w13_scale"]), _ptr(weights["w2"]),
+                  _ptr(weights["w2_scale"]))
+    _check(_lib().qmoe_decode(ctypes.byref(desc), _ptr(logits), _ptr(x), _ptr(x_scale),
+                              ctypes.byref(wts), _ptr(ids), _ptr(w), _ptr(y_pairs), _ptr(ob),
+                              _ptr(of) if want_f32 else None, _ptr(ws), ws.numel(),
+                              _stream(dev)), "qmoe_decode")
+    return {"topk_ids": ids, "topk_w": w, "y_pairs": y_pairs, "ws": ws, "out": ob,
+            "out_f32": of if want_f32 else None}
+

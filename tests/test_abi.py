@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = ops.lib()
-    assert L.qmoe_abi_version() == 3 == ops.ABI_VERSION
+    assert L.qmoe_abi_version() == 4 == ops.ABI_VERSION
     for s in range(4):
         assert L.qmoe_status_str(s)
     assert L.qmoe_status_str(99) == b"unknown status"
@@ -179,6 +179,52 @@ def test_ffn_workspace_and_desc_validation():
     bad_scheme = ops.FfnDesc(4, 64, 512, 256, 8, 2, 32, 0)
     assert ops.grouped_ffn_workspace(bad_scheme) == 0
     assert call(bad_scheme) == ops.QMOE_ERR_INVALID_ARG
+
+
+def test_decode_workspace_and_validation(monkeypatch):
+    """qmoe_decode: the workspace does not depend on T (one zeroed workspace
+    serves every batch size of a layer); every bad argument is refused before
+    anything is launched."""
+    L = ops.lib()
+    INV, UNS = ops.QMOE_ERR_INVALID_ARG, ops.QMOE_ERR_UNSUPPORTED
+    ws_of = lambda d: L.qmoe_decode_workspace(ctypes.byref(d))
+    n = ws_of(_desc(T=1))
+    assert n > 0 and n % 256 == 0
+    assert ws_of(_desc(T=16)) == n == ws_of(_desc(T=5, block_m=48))  # block_m is not used
+    assert ws_of(_desc(T=1, k=4)) > n
+    for bad in (_desc(T=17), _desc(k=17, E=32), _desc(flags=ops.QMOE_FLAG_DUMP_ACC),
+                _desc(T=-1), _desc(H=100), ops.FfnDesc(4, 1, 512, 256, 8, 2, 16, 0)):
+        assert ws_of(bad) == 0
+    p = ctypes.c_void_p(0x1000)
+    w = ops.Weights(p, p, p, p)
+
+    def call(d, ws=1 << 40, xs=p, logits=p, ob=p, of=None, wsp=p, w=w):
+        return L.qmoe_decode(ctypes.byref(d), logits, p, xs, ctypes.byref(w), p, p, None, ob, of,
+                             wsp, ws, None)
+
+    assert call(_desc(T=0)) == ops.QMOE_OK
+    assert call(_desc(T=17)) == UNS
+    assert call(_desc(T=1, E=2000)) == UNS
+    assert call(_desc(T=1, H=288)) == UNS
+    assert call(_desc(T=1, I=128)) == UNS  # a8w4 needs I % 256
+    assert call(_desc(T=1, k=17, E=32)) == INV
+    assert call(_desc(T=1, flags=ops.QMOE_FLAG_DUMP_ACC)) == INV
+    assert call(_desc(T=1), logits=None) == INV
+    assert call(_desc(T=1), ob=None, of=None) == INV
+    assert call(_desc(T=1), xs=None) == INV  # a8w4 needs x_scale
+    assert call(_desc(T=1), ws=n - 1) == INV
+    assert call(_desc(T=1), wsp=ctypes.c_void_p(0x1010)) == INV  # 256-byte alignment
+    w_mis = ops.Weights(p, ctypes.c_void_p(0x1004), p, p)
+    assert call(_desc(T=1, scheme="w4a8", I=128), w=w_mis) == INV  # 8-byte w4a8 scales
+    assert L.qmoe_decode(None, p, p, p, ctypes.byref(w), p, p, None, p, None, p, 1 << 40,
+                         None) == INV
+    monkeypatch.setenv("QMOE_DECODE_RING", "5")
+    assert call(_desc(T=1)) == INV
+    monkeypatch.delenv("QMOE_DECODE_RING")
+    monkeypatch.setenv("QMOE_DECODE_G", "3")
+    assert call(_desc(T=1)) == INV
+    monkeypatch.setenv("QMOE_DECODE_G", "8")  # H 512: 16 chunks, not a multiple of 32
+    assert call(_desc(T=1)) == INV
 
 
 def test_combine_validation():

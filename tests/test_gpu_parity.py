@@ -188,6 +188,36 @@ def _run_gpu(shape, inp, bm=None, flags=0, prepacked=False, fused_routing=False)
     return r
 
 
+def _run_decode(shape, inp, prepacked=False, ws=None):
+    """qmoe_decode on the same inputs (one launch); the workspace of a
+    previous call may be passed on."""
+    g = gpu_inputs(inp)
+    W = {k: g[k] for k in WEIGHT_KEYS}
+    if prepacked:
+        W = ops.prepack_weights(shape.scheme, W)
+    r = ops.decode_forward(shape.scheme, g["logits"], g["x"], g["x_scale"], W, shape.topk,
+                           want_f32=shape.scheme == "w8a8", ws=ws)
+    torch.cuda.synchronize()
+    return r
+
+
+def _decode_flags(ws):
+    return ops.check_flags(ws)
+
+
+def _same_outputs(d, r, scheme):
+    """Every output of the one-launch decode equals the grouped path's."""
+    assert torch.equal(d["topk_ids"], r["topk_ids"])
+    assert torch.equal(d["topk_w"], r["topk_w"])
+    assert torch.equal(d["y_pairs"].view(torch.int16) if d["y_pairs"].dtype == torch.bfloat16
+                       else d["y_pairs"].view(torch.int32),
+                       r["y_pairs"].view(torch.int16) if r["y_pairs"].dtype == torch.bfloat16
+                       else r["y_pairs"].view(torch.int32))
+    assert torch.equal(d["out"].view(torch.int16), r["out"].view(torch.int16))
+    if scheme == "w8a8":
+        assert torch.equal(d["out_f32"].view(torch.int32), r["out_f32"].view(torch.int32))
+
+
 def _unsort(dump_rows, sorted_ids, P):
     """Rows indexed by sorted slot -> rows indexed by pair id."""
     s = sorted_ids[: dump_rows.shape[0]]
@@ -532,8 +562,15 @@ def _parity_large(base, T, prepacked, fused_routing=False):
     P = T * sh.topk
     ref = O.combine(sh.scheme, y_ref[:P], w_o[:T])
     ref["y_pairs"] = y_ref[:P]
-    _check_layer(case, sh.scheme, r, ids_o[:T], w_o[:T], ref, bm,
-                 (T, sh.hidden, sh.inter, sh.experts, sh.topk))
+    dims = (T, sh.hidden, sh.inter, sh.experts, sh.topk)
+    _check_layer(case, sh.scheme, r, ids_o[:T], w_o[:T], ref, bm, dims)
+    if T <= ops.DECODE_MAX_TOKENS:
+        # The one-launch decode path: the grouped path's outputs bit for bit,
+        # hence the same parity against the oracle.
+        _flush(f"one-launch decode {sh.name}")
+        d = _run_decode(sh, inp_t, prepacked)
+        _same_outputs(d, r, sh.scheme)
+        _check_layer(case + " one launch", sh.scheme, d, ids_o[:T], w_o[:T], ref, bm, dims)
 
 
 @pytest.mark.timeout(900)
