@@ -80,7 +80,8 @@ __host__ __device__ inline int count_mod(int lo, int hi, int x) {
 struct DecodeArgs {
   int T, H, I, E, k, P, smax, c1, c2;
   int G;   // 32-column chunks per stage-2 unit (c2 = H / (32 G) units per slot)
-  int u0;  // first stage-1 unit (T rounded up to whole workgroups)
+  int u0;  // first stage-1 unit (T rounded up to whole workgroups; 0 with local routing)
+  int local_route;  // every workgroup routes the batch itself (T <= 2)
   const float* logits;
   const void* x;
   const float* x_scale;
@@ -180,6 +181,7 @@ struct AlignLds {
   int32_t pre[32];
   int32_t cnt[kMaxTokens * 16];
   uint8_t rows[kMaxTokens * 16 * kMaxTokens];  // [slot][row]: pair id (< 256)
+  float wts[kWaves * 16];                      // routing weights (local routing)
 };
 
 // Groups the P = T*k pairs into slots: slot = rank of the pair's expert among
@@ -203,11 +205,11 @@ __device__ inline int stage2_block(const DecodeArgs& g, int j) {
   return (g.u0 + g.smax * g.c1 + j * g.c2) / kWaves;
 }
 
-__device__ void group_pairs(const DecodeArgs& g, AlignLds& L, bool ids_ready) {
+// The grouping in LDS (one wave): L.cnt[slot] = rows, L.rows[slot][row] =
+// pair id, L.ids[P + slot] = expert; returns the number of slots.
+__device__ int group_core(const DecodeArgs& g, AlignLds& L) {
   const int lane = threadIdx.x & 63;
   const int P = g.P, W = (g.E + 31) >> 5;
-  if (!ids_ready)
-    for (int i = lane; i < P; i += 64) L.ids[i] = cload(&g.topk_ids[i]);
   if (lane < 32) L.bits[lane] = 0u;
   wave_lds_sync();
   for (int i = lane; i < P; i += 64) {
@@ -248,20 +250,28 @@ __device__ void group_pairs(const DecodeArgs& g, AlignLds& L, bool ids_ready) {
     }
     wave_lds_sync();
   }
+  return nact;
+}
+
+// Record word w (0-4) of slot j (see group_pairs), from the LDS grouping.
+__device__ inline uint32_t record_word(const DecodeArgs& g, const AlignLds& L, int nact, int j,
+                                       int w) {
+  if (j >= nact) return 0u;
+  if (w == 0) return (uint32_t)L.ids[g.P + j] | ((uint32_t)L.cnt[j] << 16);
+  const uint8_t* r = &L.rows[j * kMaxTokens + 4 * (w - 1)];
+  return (uint32_t)r[0] | ((uint32_t)r[1] << 8) | ((uint32_t)r[2] << 16) | ((uint32_t)r[3] << 24);
+}
+
+__device__ void group_pairs(const DecodeArgs& g, AlignLds& L, bool ids_ready) {
+  const int lane = threadIdx.x & 63;
+  if (!ids_ready)
+    for (int i = lane; i < g.P; i += 64) L.ids[i] = cload(&g.topk_ids[i]);
+  wave_lds_sync();
+  const int nact = group_core(g, L);
   // Words 0-4 of every record (rows 0 for the slots past nact).
   for (int idx = lane; idx < g.smax * 5; idx += 64) {
     const int j = idx / 5, w = idx - 5 * (idx / 5);
-    uint32_t v = 0;
-    if (j < nact) {
-      if (w == 0) {
-        v = (uint32_t)L.ids[P + j] | ((uint32_t)L.cnt[j] << 16);
-      } else {
-        const uint8_t* r = &L.rows[j * kMaxTokens + 4 * (w - 1)];
-        v = (uint32_t)r[0] | ((uint32_t)r[1] << 8) | ((uint32_t)r[2] << 16) |
-            ((uint32_t)r[3] << 24);
-      }
-    }
-    cstore(reinterpret_cast<uint32_t*>(&g.slot_rec[j * 8 + w]), v);
+    cstore(reinterpret_cast<uint32_t*>(&g.slot_rec[j * 8 + w]), record_word(g, L, nact, j, w));
   }
   release();
   for (int idx = lane; idx < kCopies * g.smax; idx += 64) {
@@ -272,17 +282,48 @@ __device__ void group_pairs(const DecodeArgs& g, AlignLds& L, bool ids_ready) {
   }
 }
 
+__device__ inline void route_one(const DecodeArgs& g, int t, int* e, float* w) {
+  const float* row = g.logits + (size_t)t * g.E;
+  if (g.E <= 256)
+    rt::route_token<4>(row, g.E, g.k, e, w);
+  else if (g.E <= 512)
+    rt::route_token<8>(row, g.E, g.k, e, w);
+  else
+    rt::route_token<16>(row, g.E, g.k, e, w);
+}
+
+// Local routing (T <= 2 <= kWaves): every workgroup routes the whole batch
+// itself, wave t routing token t, and groups it in LDS; it keeps its own
+// slot's record in s_rec and the routing weights in L.wts.  Workgroup 0
+// also writes topk_ids and topk_w.  No unit waits for another's routing.
+__device__ void route_local(const DecodeArgs& g, AlignLds& L, int j, uint32_t* s_rec) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (wave < g.T) {
+    int e = 0;
+    float w = 0.f;
+    route_one(g, wave, &e, &w);
+    if (lane < g.k) {
+      L.ids[wave * g.k + lane] = e;
+      L.wts[wave * g.k + lane] = w;
+      if (blockIdx.x == 0) {
+        g.topk_ids[wave * g.k + lane] = e;
+        g.topk_w[wave * g.k + lane] = w;
+      }
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const int nact = group_core(g, L);
+    if (lane < 5) s_rec[lane] = record_word(g, L, nact, j, lane);
+  }
+  __syncthreads();
+}
+
 __device__ void route_unit(const DecodeArgs& g, int t, AlignLds& L) {
   const int lane = threadIdx.x & 63;
   int e = 0;
   float w = 0.f;
-  const float* row = g.logits + (size_t)t * g.E;
-  if (g.E <= 256)
-    rt::route_token<4>(row, g.E, g.k, &e, &w);
-  else if (g.E <= 512)
-    rt::route_token<8>(row, g.E, g.k, &e, &w);
-  else
-    rt::route_token<16>(row, g.E, g.k, &e, &w);
+  route_one(g, t, &e, &w);
   if (lane < g.k) {
     cstore(&g.topk_ids[t * g.k + lane], e);
     cstore(&g.topk_w[t * g.k + lane], w);
@@ -492,7 +533,7 @@ struct SlotRows {
 // the record may be stale: every index then still stays inside its buffer.)
 __device__ inline bool enter_slot(const DecodeArgs& g, int j, SlotRows& r, uint32_t* s_rec) {
   const int lane = threadIdx.x & 63;
-  if ((threadIdx.x >> 6) == 0) {
+  if (!g.local_route && (threadIdx.x >> 6) == 0) {
     int32_t* flag = &g.slot_flag[(blockIdx.x % kCopies) * g.smax + j];
     wait_set(flag, g);
     if (lane < 5) s_rec[lane] = (uint32_t)cload(&g.slot_rec[j * 8 + lane]);
@@ -607,7 +648,7 @@ __device__ void stage1_unit(const DecodeArgs& g, int j, int c, uint32_t* s_rec) 
 // out[t, c*32 + lane] for lanes 0..31: the combine's recipe (fp32, slot
 // order j = 0..k-1, acc = acc + w*y without a fused multiply-add).
 template <bool F32>
-__device__ inline void combine_cols(const DecodeArgs& g, int t, int c) {
+__device__ inline void combine_cols(const DecodeArgs& g, int t, int c, const float* lds_w) {
   const int lane = threadIdx.x & 63;
   if (lane >= 32) return;
   const int col = c * 32 + lane;
@@ -619,7 +660,8 @@ __device__ inline void combine_cols(const DecodeArgs& g, int t, int c) {
       v = cload(reinterpret_cast<const float*>(g.y) + idx);
     else
       v = __uint_as_float((uint32_t)cload(reinterpret_cast<const uint16_t*>(g.y) + idx) << 16);
-    acc = acc + cload(&g.topk_w[(size_t)t * g.k + j]) * v;
+    const float wj = g.local_route ? lds_w[t * g.k + j] : cload(&g.topk_w[(size_t)t * g.k + j]);
+    acc = acc + wj * v;
   }
   const size_t o = (size_t)t * g.H + col;
   if (g.out_f32 != nullptr) g.out_f32[o] = acc;
@@ -627,7 +669,8 @@ __device__ inline void combine_cols(const DecodeArgs& g, int t, int c) {
 }
 
 template <int S, bool PK, int R>
-__device__ void stage2_unit(const DecodeArgs& g, int j, int cg, uint32_t* s_rec) {
+__device__ void stage2_unit(const DecodeArgs& g, int j, int cg, uint32_t* s_rec,
+                            const float* lds_w) {
   using T_ = Tr<S>;
   using Acc = typename T_::Acc;
   SlotRows sr;
@@ -711,7 +754,7 @@ __device__ void stage2_unit(const DecodeArgs& g, int j, int cg, uint32_t* s_rec)
     const int r = __builtin_ctzll(mask);
     mask &= mask - 1;
     const int t = __shfl(sr.pair, r, 64) / g.k;
-    for (int gi = 0; gi < g.G; gi++) combine_cols<S == kW8A8>(g, t, cg * g.G + gi);
+    for (int gi = 0; gi < g.G; gi++) combine_cols<S == kW8A8>(g, t, cg * g.G + gi, lds_w);
   }
 }
 
@@ -728,12 +771,17 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs g) {
   }
   int v = u - g.u0;
   const int n1 = g.smax * g.c1;
+  if (g.local_route) {
+    // The workgroup's slot (the same for its four units).
+    const int vb = blockIdx.x * kWaves - g.u0;
+    route_local(g, lds, vb < n1 ? vb / g.c1 : (vb - n1) / g.c2, s_rec);
+  }
   if (v < n1) {
     stage1_unit<S, PK, R>(g, v / g.c1, v % g.c1, s_rec);
     return;
   }
   v -= n1;
-  if (v < g.smax * g.c2) stage2_unit<S, PK, R>(g, v / g.c2, v % g.c2, s_rec);
+  if (v < g.smax * g.c2) stage2_unit<S, PK, R>(g, v / g.c2, v % g.c2, s_rec, lds.wts);
 }
 
 }  // namespace
@@ -797,17 +845,18 @@ static hipError_t launch_s(const DecodeArgs& g, bool packed, int ring, unsigned 
   return ring == 6 ? launch_t<S, false, 6>(g, blocks, s) : launch_t<S, false, 4>(g, blocks, s);
 }
 
-// 32-column chunks per stage-2 unit: the largest of 4, 2 that leaves a
-// multiple of four units per slot and at least 2048 stage-2 units (about
-// two waves per SIMD: fewer units leave the chip idle at the end of stage
-// 2), else 1.  More chunks per unit amortize its fixed costs (the flag, the
-// activation reads, the arrival counts) over more weight bytes.  Measured
-// on the 512-expert top-10 block (hidden 4096): 1 chunk best at 1 token, 2
-// at 2-8 tokens (within 2-3%), 4 at 16; 8 never.
+// 32-column chunks per stage-2 unit.  More chunks per unit amortize its
+// fixed costs (the flag, the activation reads, the arrival counts) over more
+// weight bytes; fewer leave more units to fill the chip.  Measured on the
+// 512-expert top-10 block (hidden 4096, 128 columns of 32): 1 chunk best at
+// 1 token (1280 one-chunk units), 2 at 2-8 tokens, 4 at 16 tokens (4800
+// four-chunk units); 8 never.  So: 4 chunks when that still leaves 4096
+// units, else 2 when one-chunk units would number 2048 or more, else 1 (and
+// always a multiple of four units per slot).
 int decode_stage2_chunks(int T, int H, int E, int k) {
-  const int smax = std::min(E, T * k);
-  for (int G = 4; G > 1; G /= 2)
-    if ((H / 32) % (4 * G) == 0 && (long)smax * (H / 32 / G) >= 2048) return G;
+  const long units1 = (long)std::min(E, T * k) * (H / 32);
+  if ((H / 32) % 16 == 0 && units1 / 4 >= 4096) return 4;
+  if ((H / 32) % 8 == 0 && units1 >= 2048) return 2;
   return 1;
 }
 
@@ -826,7 +875,11 @@ hipError_t launch_decode(int scheme, bool packed, int ring, int chunks, int T, i
   g.c1 = I / 16;
   g.G = chunks;
   g.c2 = H / 32 / g.G;
-  g.u0 = (T + kWaves - 1) / kWaves * kWaves;
+  // Local routing up to 2 tokens: 1 token 45.8 -> 44.3 us, 2 tokens 61.4 ->
+  // 60.5 us; at 4 tokens every workgroup routing four tokens before it starts
+  // costs more than the hand-off (87.7 -> 94.4 us).
+  g.local_route = T <= 2 ? 1 : 0;
+  g.u0 = g.local_route ? 0 : (T + kWaves - 1) / kWaves * kWaves;
   g.logits = logits, g.x = x, g.x_scale = x_scale;
   g.w13 = w13, g.w13_scale = w13_scale, g.w2 = w2, g.w2_scale = w2_scale;
   g.topk_ids = topk_ids, g.topk_w = topk_w;
