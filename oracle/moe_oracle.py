@@ -29,7 +29,9 @@ What is computed, step by step:
 6. Combine: ``out[t] = sum_j w[t, j] * y[t*k + j]`` in slot order, a fixed
    order with no atomics (hip-ep PR, description: deterministic scatter order).
 
-Schemes: ``w4a16`` (exact fp64 arithmetic on the dequantized int4 weights),
+Schemes: ``w4a16`` (the int4 weights dequantised to bf16, q * s rounded to
+nearest even, as the vLLM issue lowers W4A16, sections Problem and
+Constraint; then exact fp64 arithmetic),
 ``w4a8`` (int4 weights upconverted for an integer product with int8
 activations: exact integer sums per 32-wide group, the group scales applied
 after them, exact in fp64; the int8 requantization of h decided in fp32 as
@@ -274,14 +276,17 @@ def quant_rows_e4m3(h: np.ndarray):
 
 
 def expert_w4a16(x_bits, w13, s13, w2, s2) -> dict:
+    """The W4A16 lowering the vLLM issue describes (section Problem and
+    Constraint): the packed int4 weights are dequantised to bf16 (q * s
+    rounded to nearest even), then a bf16 dot, here with exact fp64 sums."""
     inter = w13.shape[0] // 2
     x = bf16_bits_to_f64(x_bits)
-    gu = x @ dequant_int4_g32(w13, s13).T
+    gu = x @ round_to_bf16(dequant_int4_g32(w13, s13)).T
     g, u = gu[:, :inter], gu[:, inter:]
     with np.errstate(over="ignore"):
         h = g / (1.0 + np.exp(-g)) * u
     hin = round_to_bf16(h)
-    y = hin @ dequant_int4_g32(w2, s2).T
+    y = hin @ round_to_bf16(dequant_int4_g32(w2, s2)).T
     return {"gu": gu, "h": hin, "y": y}
 
 

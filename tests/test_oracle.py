@@ -225,7 +225,10 @@ def _dense_reference(scheme, inp, e, rows):
             lo = (b & 15) - 16 * ((b & 15) >= 8).to(torch.int16)
             hi = (b >> 4) - 16 * ((b >> 4) >= 8).to(torch.int16)
             q = torch.stack([lo, hi], -1).reshape(codes.shape[0], -1).double()
-            return q * torch.from_numpy(s.astype(np.float64)).repeat_interleave(32, 1)
+            w = q * torch.from_numpy(s.astype(np.float64)).repeat_interleave(32, 1)
+            # dequantised to bf16 (torch's round-to-nearest-even cast; q * s is
+            # exact in fp32)
+            return w.float().to(torch.bfloat16).double()
         W13 = deq(inp["w13"][e], inp["w13_scale"][e])
         W2 = deq(inp["w2"][e], inp["w2_scale"][e])
         gu = x @ W13.T
