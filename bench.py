@@ -54,9 +54,9 @@ WRITE_FACTOR = 1024 * 1.0
 # they were taken with; traffic is reported only while the sources match.
 DOMINANT_COUNTERS = {
     "kernel": "stage1",
-    "fetch_kib": 1195755.5,
-    "write_kib": 165122.7,
-    "sources_sha256_16": "b3aa8ab04ce22b8f",
+    "fetch_kib": 1195756.8,
+    "write_kib": 165123.6,
+    "sources_sha256_16": "3cd405d6f0d73775",
     "workload": "a8w4_large@T4096",
     "block_m": 128,
     "weight_layout": "prepacked",
