@@ -352,25 +352,31 @@ struct Slot {
   u32x4 a[Tr<S>::A_FRAG / 16];
 };
 
-// The K loop of one unit: acc[s] += rows (16, A) x weight rows of sub-tile s,
-// K steps 0..n-1 in order.  The weight loads of the first R steps are issued
-// before wait() returns; the activation loads after it.
-template <int S, bool PK, int R, bool COH, class Wait>
-__device__ inline void k_loop(const uint8_t* __restrict__ B, const uint8_t* __restrict__ Sc,
-                              const uint32_t (&boff)[2], const uint32_t (&soff)[2],
-                              const uint8_t* __restrict__ arow, int n,
-                              typename Tr<S>::Acc (&acc)[2], Wait wait) {
+// One K step of a unit: the loads of a ring slot and its MFMAs.  The
+// weight loads of sub-tile s start at code byte boff[s] and scale byte
+// soff[s] (K step 0); the activation loads at arow.
+template <int S, bool PK, bool COH>
+struct KStep {
   using T_ = Tr<S>;
-  constexpr int NF = T_::A_FRAG / 16;
-  constexpr int SB = (S == kW4A16 || S == kW4A8) ? 2 : 1;
-  (void)SB;
-  constexpr uint32_t B_KS = PK ? 16 * T_::B_STEP : T_::B_STEP;
-  constexpr uint32_t B_PIECE = PK ? 1024 : 16;
-  constexpr uint32_t S_KS = PK ? 128 : 8;
-  const int lane = threadIdx.x & 63, lq = lane >> 4;
-  const uint32_t sshift = ((PK ? lane : lq) & 1) * 16;
+  using Acc = typename T_::Acc;
+  static constexpr int NF = T_::A_FRAG / 16;
+  static constexpr uint32_t B_KS = PK ? 16 * T_::B_STEP : T_::B_STEP;
+  static constexpr uint32_t B_PIECE = PK ? 1024 : 16;
+  static constexpr uint32_t S_KS = PK ? 128 : 8;
+  const uint8_t* __restrict__ B;
+  const uint8_t* __restrict__ Sc;
+  const uint8_t* __restrict__ arow;
+  int lq;
+  uint32_t sshift;
 
-  auto load_b = [&](Slot<S>& sl, int ks) __attribute__((always_inline)) {
+  __device__ KStep(const uint8_t* b, const uint8_t* sc, const uint8_t* a) : B(b), Sc(sc), arow(a) {
+    const int lane = threadIdx.x & 63;
+    lq = lane >> 4;
+    sshift = ((PK ? lane : lq) & 1) * 16;
+  }
+
+  __device__ __attribute__((always_inline)) void load_b(Slot<S>& sl, const uint32_t (&boff)[2],
+                                                       const uint32_t (&soff)[2], int ks) const {
 #pragma unroll
     for (int s = 0; s < 2; s++) {
       const uint32_t o = boff[s] + (uint32_t)ks * B_KS;
@@ -394,8 +400,8 @@ __device__ inline void k_loop(const uint8_t* __restrict__ B, const uint8_t* __re
         sl.b[s].sc = 0;
       }
     }
-  };
-  auto load_a = [&](Slot<S>& sl, int ks) __attribute__((always_inline)) {
+  }
+  __device__ __attribute__((always_inline)) void load_a(Slot<S>& sl, int ks) const {
     const uint8_t* src = arow + (uint32_t)ks * T_::A_STEP;
     if constexpr (COH) {
       // Another wave wrote these rows: four device-coherent 32-bit loads
@@ -426,25 +432,33 @@ __device__ inline void k_loop(const uint8_t* __restrict__ B, const uint8_t* __re
       for (int f = 0; f < NF; f++)
         sl.a[f] = *reinterpret_cast<const u32x4*>(src + a_frag_offset<S, PK>(lq, f));
     }
-  };
-  auto compute = [&](const Slot<S>& sl) __attribute__((always_inline)) {
+  }
+  __device__ __attribute__((always_inline)) void compute(Acc (&acc)[2], const Slot<S>& sl) const {
 #pragma unroll
     for (int s = 0; s < 2; s++) mfma_step<S>(acc[s], sl.a, prepare_b<S, PK>(sl.b[s], sshift));
-  };
+  }
   // 24 wait states after the MFMAs wherever control may leave a run of
-  // steps (the main loop's back edge and exit, each step of the tail): the
-  // register allocator copies the accumulators between register files at
-  // those edges, and the compiler's wait-state count there measured short on
+  // steps (a loop's back edge and exit, each step of a tail): the register
+  // allocator copies the accumulators between register files at those
+  // edges, and the compiler's wait-state count there measured short on
   // gfx950: a copy of the last accumulator register 8 wait states after
   // v_mfma_i32_16x16x64_i8 (ahead of the other three, which came at 9-11)
   // still held the previous step's sum.  Every other read of an MFMA result
   // in this kernel comes at least 11 wait states after it.
-  auto pad = []() __attribute__((always_inline)) {
+  __device__ static __attribute__((always_inline)) void pad() {
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
     __builtin_amdgcn_sched_barrier(0);
-  };
+  }
+};
 
+// The K loop of one unit: acc[s] += rows (16, A) x weight rows of sub-tile s,
+// K steps 0..n-1 in order.  The weight loads of the first R steps are issued
+// before wait() returns; the activation loads after it.
+template <int S, bool PK, int R, bool COH, class Wait>
+__device__ inline void k_loop(const KStep<S, PK, COH>& ks, const uint32_t (&boff)[2],
+                              const uint32_t (&soff)[2], int n, typename Tr<S>::Acc (&acc)[2],
+                              Wait wait) {
   Slot<S> ring[R];
   if (n >= R) {
     // Steady state: step s computes from ring[s % R], then loads step s + R
@@ -452,29 +466,29 @@ __device__ inline void k_loop(const uint8_t* __restrict__ B, const uint8_t* __re
     // compiler's counter waits stay exact; the tail (the last R to 2R-1
     // steps) loads only what is still needed.
 #pragma unroll
-    for (int u = 0; u < R; u++) load_b(ring[u], u);
+    for (int u = 0; u < R; u++) ks.load_b(ring[u], boff, soff, u);
     wait();
 #pragma unroll
-    for (int u = 0; u < R; u++) load_a(ring[u], u);
+    for (int u = 0; u < R; u++) ks.load_a(ring[u], u);
     int s0 = 0;
     for (; s0 + 2 * R <= n; s0 += R) {
 #pragma unroll
       for (int u = 0; u < R; u++) {
-        compute(ring[u]);
-        load_b(ring[u], s0 + u + R);
-        load_a(ring[u], s0 + u + R);
+        ks.compute(acc, ring[u]);
+        ks.load_b(ring[u], boff, soff, s0 + u + R);
+        ks.load_a(ring[u], s0 + u + R);
       }
-      pad();
+      ks.pad();
     }
 #pragma unroll
     for (int u = 0; u < 2 * R; u++) {
       const int s = s0 + u;
       if (s < n) {
-        compute(ring[u % R]);
-        pad();
+        ks.compute(acc, ring[u % R]);
+        ks.pad();
         if (s + R < n) {
-          load_b(ring[u % R], s + R);
-          load_a(ring[u % R], s + R);
+          ks.load_b(ring[u % R], boff, soff, s + R);
+          ks.load_a(ring[u % R], s + R);
         }
       }
     }
@@ -482,18 +496,69 @@ __device__ inline void k_loop(const uint8_t* __restrict__ B, const uint8_t* __re
     // Fewer steps than ring slots: every step's loads up front.
 #pragma unroll
     for (int u = 0; u < R; u++)
-      if (u < n) load_b(ring[u], u);
+      if (u < n) ks.load_b(ring[u], boff, soff, u);
     wait();
 #pragma unroll
     for (int u = 0; u < R; u++)
-      if (u < n) load_a(ring[u], u);
+      if (u < n) ks.load_a(ring[u], u);
 #pragma unroll
     for (int u = 0; u < R; u++) {
       if (u < n) {
-        compute(ring[u]);
-        pad();
+        ks.compute(acc, ring[u]);
+        ks.pad();
       }
     }
+  }
+}
+
+// The K loops of nch chunks of a unit's weight rows as one stream of loads
+// (n a multiple of R; chunk c's rows start bchunk code bytes and schunk scale
+// bytes after chunk c-1's): acc[s] += rows (16, A) x weight rows of sub-tile
+// s over K steps 0..n-1, then epi(c, acc), for each chunk in turn.  Step s
+// computes from ring[s % R] and then loads the step R later into it; the
+// last R steps of a chunk load the next chunk's first R steps, so one
+// chunk's epilogue overlaps the loads of the next, and those of the last
+// chunk load nothing.
+template <int S, bool PK, int R, bool COH, class Wait, class Epi>
+__device__ inline void k_loop_chunks(const KStep<S, PK, COH>& ks, const uint32_t (&boff)[2],
+                                     const uint32_t (&soff)[2], uint32_t bchunk,
+                                     uint32_t schunk, int n, int nch, Wait wait, Epi epi) {
+  using Acc = typename Tr<S>::Acc;
+  Slot<S> ring[R];
+#pragma unroll
+  for (int u = 0; u < R; u++) ks.load_b(ring[u], boff, soff, u);
+  wait();
+#pragma unroll
+  for (int u = 0; u < R; u++) ks.load_a(ring[u], u);
+  for (int c = 0; c < nch; c++) {
+    Acc acc[2] = {Acc{0, 0, 0, 0}, Acc{0, 0, 0, 0}};
+    const uint32_t bo[2] = {boff[0] + c * bchunk, boff[1] + c * bchunk};
+    const uint32_t so[2] = {soff[0] + c * schunk, soff[1] + c * schunk};
+    int s0 = 0;
+    for (; s0 + R < n; s0 += R) {
+#pragma unroll
+      for (int u = 0; u < R; u++) {
+        ks.compute(acc, ring[u]);
+        ks.load_b(ring[u], bo, so, s0 + u + R);
+        ks.load_a(ring[u], s0 + u + R);
+      }
+      ks.pad();
+    }
+    if (c + 1 < nch) {
+      const uint32_t bn[2] = {bo[0] + bchunk, bo[1] + bchunk};
+      const uint32_t sn[2] = {so[0] + schunk, so[1] + schunk};
+#pragma unroll
+      for (int u = 0; u < R; u++) {
+        ks.compute(acc, ring[u]);
+        ks.load_b(ring[u], bn, sn, u);
+        ks.load_a(ring[u], u);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < R; u++) ks.compute(acc, ring[u]);
+    }
+    ks.pad();
+    epi(c, acc);
   }
 }
 
@@ -571,7 +636,8 @@ __device__ void stage1_unit(const DecodeArgs& g, int j, int c, uint32_t* s_rec) 
   const int tok = sr.pair / g.k;
   const uint8_t* arow = reinterpret_cast<const uint8_t*>(g.x) + (size_t)tok * H * T_::A_ELEM;
   Acc acc[2] = {Acc{0, 0, 0, 0}, Acc{0, 0, 0, 0}};
-  k_loop<S, PK, R, false>(B, Sc, boff, soff, arow, H / T_::BK, acc, [] {});
+  k_loop<S, PK, R, false>(KStep<S, PK, false>(B, Sc, arow), boff, soff, H / T_::BK, acc,
+                          [] {});
 
   // Epilogue: lane (lq, lr) holds rows 4lq + r of h column c*16 + lr.
   float ws[2] = {1.f, 1.f};
@@ -688,42 +754,42 @@ __device__ void stage2_unit(const DecodeArgs& g, int j, int cg, uint32_t* s_rec,
   float rsc[4] = {1.f, 1.f, 1.f, 1.f};
 #pragma unroll
   for (int r = 0; r < 4; r++) prow[r] = __shfl(sr.pair, 4 * lq + r, 64);
-  auto chunk = [&](int c, bool first) __attribute__((always_inline)) {
-    const int nrow[2] = {c * 32 + lr, c * 32 + 16 + lr};
-    uint32_t boff[2], soff[2];
-    weight_offsets<S, PK>(nrow, I, boff, soff);
-    Acc acc[2] = {Acc{0, 0, 0, 0}, Acc{0, 0, 0, 0}};
-    if (first) {
-      k_loop<S, PK, R, true>(B, Sc, boff, soff, arow, I / T_::BK, acc, [&] {
-        // Wave 0 polls the workgroup's copy of the flag.
-        if ((threadIdx.x >> 6) == 0) {
-          int32_t* f = &g.ready[(blockIdx.x % kCopies) * g.smax + j];
-          wait_set(f, g);
-          if (lane == 0) atomic_add(f, -1);
-        }
-        __syncthreads();
-      });
-      if constexpr (S != kW4A16) {
-#pragma unroll
-        for (int r = 0; r < 4; r++)
-          if (4 * lq + r < sr.nrows) rsc[r] = cload(&g.hs[prow[r]]);
-      }
-    } else {
-      k_loop<S, PK, R, true>(B, Sc, boff, soff, arow, I / T_::BK, acc, [] {});
+  const KStep<S, PK, true> ks(B, Sc, arow);
+  const int n = I / T_::BK;
+  // Wave 0 polls the workgroup's copy of the flag.
+  auto wait_ready = [&] {
+    if ((threadIdx.x >> 6) == 0) {
+      int32_t* f = &g.ready[(blockIdx.x % kCopies) * g.smax + j];
+      wait_set(f, g);
+      if (lane == 0) atomic_add(f, -1);
     }
-    float ws[2] = {1.f, 1.f};
+    __syncthreads();
+  };
+  auto load_rsc = [&] {
+    if constexpr (S != kW4A16) {
+#pragma unroll
+      for (int r = 0; r < 4; r++)
+        if (4 * lq + r < sr.nrows) rsc[r] = cload(&g.hs[prow[r]]);
+    }
+  };
+  // W8A8's per-column weight scales of 32-column chunk c.
+  auto load_ws = [&](int c, float (&ws)[2]) __attribute__((always_inline)) {
     if constexpr (S == kW8A8) {
 #pragma unroll
       for (int s = 0; s < 2; s++)
-        ws[s] = reinterpret_cast<const float*>(g.w2_scale)[(size_t)sr.e * H + nrow[s]];
+        ws[s] = reinterpret_cast<const float*>(g.w2_scale)[(size_t)sr.e * H + c * 32 + 16 * s + lr];
     }
+  };
+  // y of 32-column chunk c: lane (lq, lr) holds rows 4lq + r of columns
+  // c*32 + 16s + lr.
+  auto store = [&](int c, const Acc(&acc)[2], const float (&ws)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int r = 0; r < 4; r++) {
       if (4 * lq + r < sr.nrows) {
         const float rs = rsc[r];
 #pragma unroll
         for (int s = 0; s < 2; s++) {
-          const size_t o = (size_t)prow[r] * H + nrow[s];
+          const size_t o = (size_t)prow[r] * H + c * 32 + 16 * s + lr;
           if constexpr (S == kW8A8)
             cstore(reinterpret_cast<float*>(g.y) + o, ((float)acc[s][r] * rs) * ws[s]);
           else if constexpr (S == kA8W4 || S == kW4A8)
@@ -736,8 +802,46 @@ __device__ void stage2_unit(const DecodeArgs& g, int j, int cg, uint32_t* s_rec,
       }
     }
   };
-  chunk(cg * g.G, true);
-  for (int gi = 1; gi < g.G; gi++) chunk(cg * g.G + gi, false);
+  if (g.G > 1 && n % R == 0) {
+    // The unit's chunks as one stream of loads.  The row scales are loaded
+    // right after the flag (before the activation loads, so no wait for them
+    // holds up the K loop); each chunk's weight scales are loaded during the
+    // previous chunk's epilogue, long before they are used.
+    const int c0 = cg * g.G;
+    const int nrow[2] = {c0 * 32 + lr, c0 * 32 + 16 + lr};
+    uint32_t boff[2], soff[2];
+    weight_offsets<S, PK>(nrow, I, boff, soff);
+    float ws[2] = {1.f, 1.f};
+    load_ws(c0, ws);
+    k_loop_chunks<S, PK, R, true>(
+        ks, boff, soff, 32u * (uint32_t)kbytes, (uint32_t)I * SB, n, g.G,
+        [&] {
+          wait_ready();
+          load_rsc();
+        },
+        [&](int c, const Acc(&acc)[2]) __attribute__((always_inline)) {
+          store(c0 + c, acc, ws);
+          if (c + 1 < g.G) load_ws(c0 + c + 1, ws);
+        });
+  } else {
+    auto chunk = [&](int c, bool first) __attribute__((always_inline)) {
+      const int nrow[2] = {c * 32 + lr, c * 32 + 16 + lr};
+      uint32_t boff[2], soff[2];
+      weight_offsets<S, PK>(nrow, I, boff, soff);
+      Acc acc[2] = {Acc{0, 0, 0, 0}, Acc{0, 0, 0, 0}};
+      if (first) {
+        k_loop<S, PK, R, true>(ks, boff, soff, n, acc, wait_ready);
+        load_rsc();
+      } else {
+        k_loop<S, PK, R, true>(ks, boff, soff, n, acc, [] {});
+      }
+      float ws[2] = {1.f, 1.f};
+      load_ws(c, ws);
+      store(c, acc, ws);
+    };
+    chunk(cg * g.G, true);
+    for (int gi = 1; gi < g.G; gi++) chunk(cg * g.G + gi, false);
+  }
   release();
   // One arrival per row (lanes 0..15 hold rows 0..15); the last of a token's
   // k rows to arrive for this unit's columns combines them.

@@ -37,9 +37,9 @@ EXPORTS = (
 DECODE_MAX_TOKENS = 16
 # Batches up to this size take the one-launch qmoe_decode in moe_forward's
 # automatic choice: measured on one MI355X for the 512-expert top-10 a8w4
-# block, the one launch is faster at 1 and 2 tokens (44.2 against 47.0 us,
-# 60.3 against 64.9 us), slower from 4 tokens on (89.7 against 86.5 us; 16
-# tokens 0.239 against 0.203 ms), where the grouped kernels stream the
+# block, the one launch is faster at 1 and 2 tokens (44.6 against 47.2 us,
+# 59.6 against 65.0 us), slower from 4 tokens on (88.2 against 86.8 us; 16
+# tokens 0.235 against 0.203 ms), where the grouped kernels stream the
 # weights at a higher rate.
 DECODE_PREFERRED_MAX_TOKENS = 2
 
