@@ -61,7 +61,7 @@ namespace {
 using namespace gk;
 
 
-template <int S, int STAGE, int BM, bool PK, int NSUB, int WAVES, bool XT, int RING>
+template <int S, int STAGE, int BM, bool PK, int NSUB, int WAVES, bool XT, int RING, bool LB>
 __global__ __launch_bounds__(WAVES * 64)
     __attribute__((amdgpu_waves_per_eu(NSUB == 4 ? 1 : 2, NSUB == 4 ? 1 : 2))) void
     moe_gemm_kernel(GemmArgs g) {
@@ -386,18 +386,30 @@ __global__ __launch_bounds__(WAVES * 64)
   // K loop.  Step s computes from LDS slot s%2 and weight register set
   // s%RING.  A step first writes the activation rows of step s+1 (loaded one
   // step earlier) to the other LDS slot, then issues the activation loads of
-  // step s+2 and the weight loads of step s+RING-1, then runs the MFMAs of
+  // step s+2 and the weight loads of step s+RING-1 and runs the MFMAs of
   // step s; one barrier ends the step.  Load counters complete in order, so
-  // this order lets the wait for the activations skip the younger weight
-  // loads, which keep RING-1 steps to arrive.  Loads past the last step re-read the
-  // last step (cache hits): every step has the same shape and the
-  // compiler's counter waits stay exact.
+  // issuing the activations first lets the wait for them skip the younger
+  // weight loads.  The weight loads go in front of the MFMAs (LB false), or,
+  // with LB (tall tiles full of rows), behind them: every wave of the block
+  // issues its loads right after the barrier, and in front of a long run of
+  // MFMAs they stalled each wave's issue until the CU's memory pipeline had
+  // taken the block's 68 KiB of requests (a8w4 at 4096 tokens, timestamps
+  // per phase: 920 of ~4000 clocks per step); behind the MFMAs that drain
+  // overlaps them (stage 1 0.513 -> 0.492 ms), at the cost of issuing the
+  // weights a little later, which short tiles cannot afford.  Loads past the
+  // last step re-read the last step (cache hits): every step has the same
+  // shape and the compiler's counter waits stay exact.
   auto step = [&](int s, const BFrag<S>(&bc)[NSUB], BFrag<S>(&bl)[NSUB])
       __attribute__((always_inline)) {
     store_a(ar, (s + 1) & 1);
     load_a(ar, min(s + 2, n - 1));
-    load_b(bl, min(s + RING - 1, n - 1));
-    if (s < n) compute(s & 1, bc);
+    if constexpr (LB) {
+      if (s < n) compute(s & 1, bc);
+      load_b(bl, min(s + RING - 1, n - 1));
+    } else {
+      load_b(bl, min(s + RING - 1, n - 1));
+      if (s < n) compute(s & 1, bc);
+    }
     __syncthreads();
   };
   // RING steps from s0 (a multiple of RING): step s0+u computes from ring
@@ -478,8 +490,13 @@ __global__ __launch_bounds__(WAVES * 64)
           keep_epilogue_state();
           if (more) setup_rows(wn, buf ^ 1);
         }
-        load_b(bq[u - 1], more ? u - 1 : n - 1);
-        compute(s & 1, bq[u]);
+        if constexpr (LB) {
+          compute(s & 1, bq[u]);
+          load_b(bq[u - 1], more ? u - 1 : n - 1);
+        } else {
+          load_b(bq[u - 1], more ? u - 1 : n - 1);
+          compute(s & 1, bq[u]);
+        }
         __syncthreads();
       }
     } else {
@@ -612,14 +629,15 @@ __global__ __launch_bounds__(WAVES * 64)
   }
 }
 
-template <int S, int STAGE, int BM, bool PK, int NSUB, int WAVES, bool XT, int RING>
+template <int S, int STAGE, int BM, bool PK, int NSUB, int WAVES, bool XT, int RING,
+          bool LB = false>
 hipError_t launch_xt(const GemmArgs& g, hipStream_t s) {
   // Resident blocks per CU, queried once per kernel (a function-local
   // static: its initialisation is thread-safe).
   static const int blocks_per_cu = [] {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, moe_gemm_kernel<S, STAGE, BM, PK, NSUB, WAVES, XT, RING>, WAVES * 64, 0) !=
+            &n, moe_gemm_kernel<S, STAGE, BM, PK, NSUB, WAVES, XT, RING, LB>, WAVES * 64, 0) !=
             hipSuccess ||
         n < 1)
       n = 1;
@@ -627,7 +645,7 @@ hipError_t launch_xt(const GemmArgs& g, hipStream_t s) {
   }();
   int nblk = device_cu_count() * blocks_per_cu;
   nblk = nblk < 8 ? 8 : (nblk / 8) * 8;
-  hipLaunchKernelGGL((moe_gemm_kernel<S, STAGE, BM, PK, NSUB, WAVES, XT, RING>), dim3(nblk),
+  hipLaunchKernelGGL((moe_gemm_kernel<S, STAGE, BM, PK, NSUB, WAVES, XT, RING, LB>), dim3(nblk),
                      dim3(WAVES * 64), 0, s, g);
   return hipGetLastError();
 }
@@ -648,6 +666,14 @@ hipError_t launch_one(const GemmArgs& g, int ring, hipStream_t s) {
   if constexpr (BM <= (S == kA8W4 ? 16 : 32)) {
     if (nsteps % 8 == 0 && ring != 4)
       return launch_xt<S, STAGE, BM, PK, NSUB, WAVES, XT2, 8>(g, s);
+  }
+  if constexpr (BM == 128 && WAVES == 8) {
+    // Weight loads behind the MFMAs when the tiles are mostly full (48 or
+    // more rows per expert on average): measured 4-5% faster for a8w4 at
+    // 4096 and 8192 tokens and the skewed W4A16 prefill, 1.6% slower at 1024
+    // tokens (20 rows per expert).
+    if (nsteps >= 4 && nsteps % 4 == 0 && (long)g.P >= 48L * g.E)
+      return launch_xt<S, STAGE, BM, PK, NSUB, WAVES, XT2, 4, true>(g, s);
   }
   if (nsteps >= 4 && nsteps % 4 == 0)
     return launch_xt<S, STAGE, BM, PK, NSUB, WAVES, XT2, 4>(g, s);
