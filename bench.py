@@ -56,7 +56,7 @@ DOMINANT_COUNTERS = {
     "kernel": "stage1",
     "fetch_kib": 1195535.1,
     "write_kib": 165153.6,
-    "sources_sha256_16": "8aeb2bdbd8621d11",
+    "sources_sha256_16": "dcaf6b2a987e672c",
     "workload": "a8w4_large@T4096",
     "block_m": 128,
     "weight_layout": "prepacked",

@@ -166,7 +166,7 @@ qmoe_status qmoe_route(const float* logits, int32_t T, int32_t E, int32_t k,
  * (blocks, prefetch depth, column passes) when it is called with this
  * block_m; any block_m gives the same results bit for bit.  Returns 0 for
  * invalid arguments.  The environment variable QMOE_TILE
- * ("s1w=8,s1r=4,s1runs=1,s2w=4,s2p=8,s2h=0", any subset) overrides those
+ * ("s1w=8,s1r=4,s1runs=1,s1lb=1,s2w=4,s2p=8,s2h=0", any subset) overrides those
  * other choices in qmoe_grouped_ffn for sweeps; a malformed or inapplicable
  * value makes qmoe_grouped_ffn return QMOE_ERR_INVALID_ARG.               */
 int32_t qmoe_default_block_m(int32_t scheme, int32_t T, int32_t H, int32_t I, int32_t E,

@@ -107,8 +107,9 @@ struct TileCfg {
   int s2_waves;   // row-major stage 2 (W4A16, W4A8, I > 1024): as s1_waves
   int s2_passes;  // resident stage 2: column passes per work item; 0 = rule
   int s2_half;    // resident stage 2: -1 = rule, 0 = whole tiles, 1 = half tiles
+  int s1_late;    // stage-1 weight loads behind the MFMAs: -1 = rule, 0 = in front, 1 = behind
 };
-constexpr TileCfg kRuleCfg = {0, 0, -1, 0, 0, -1};
+constexpr TileCfg kRuleCfg = {0, 0, -1, 0, 0, -1, -1};
 
 struct TileRow {
   int scheme, H, I, E, k, t_max, block_m;
@@ -160,6 +161,7 @@ static bool parse_tile_env(TileCfg& c) {
     else if (key == "s2w") c.s2_waves = (int)v;
     else if (key == "s2p") c.s2_passes = (int)v;
     else if (key == "s2h") c.s2_half = (int)v;
+    else if (key == "s1lb") c.s1_late = (int)v;
     else return false;
     p = end;
     if (*p == ',') p++;
@@ -502,7 +504,8 @@ static qmoe_status grouped_ffn_impl(const qmoe_ffn_desc* d, const void* x, const
   auto waves_ok = [&](int w) { return w == 0 || w == 4 || (w == 8 && d->block_m >= 64); };
   if (!waves_ok(cfg.s1_waves) || !waves_ok(cfg.s2_waves) ||
       (cfg.s1_ring != 0 && cfg.s1_ring != 4) || cfg.s1_runs < -1 || cfg.s1_runs > 1 ||
-      cfg.s2_half < -1 || cfg.s2_half > 1 || cfg.s2_passes < 0 ||
+      cfg.s2_half < -1 || cfg.s2_half > 1 || cfg.s2_passes < 0 || cfg.s1_late < -1 ||
+      cfg.s1_late > 1 ||
       (cfg.s2_half == 1 && (!resident || d->block_m < 32)) ||
       (cfg.s2_passes > 0 && !resident) || (cfg.s2_waves != 0 && resident))
     return QMOE_ERR_INVALID_ARG;
@@ -561,7 +564,8 @@ static qmoe_status grouped_ffn_impl(const qmoe_ffn_desc* d, const void* x, const
   hipError_t e = mark(0);
   const bool packed = (d->flags & QMOE_FLAG_PREPACKED) != 0;
   if (e == hipSuccess)
-    e = launch_gemm(d->scheme, 1, d->block_m, packed, gs1.nsub, gs1.waves, cfg.s1_ring, g1, s);
+    e = launch_gemm(d->scheme, 1, d->block_m, packed, gs1.nsub, gs1.waves, cfg.s1_ring,
+                    cfg.s1_late, g1, s);
   if (e == hipSuccess) e = mark(1);
   if (e != hipSuccess) return hip_status(e);
 
@@ -602,7 +606,7 @@ static qmoe_status grouped_ffn_impl(const qmoe_ffn_desc* d, const void* x, const
   g2.out = y_pairs;
   g2.dump = dump ? reinterpret_cast<int32_t*>(wsb + lay.acc2) : nullptr;
   e = resident ? launch_stage2_resident(d->scheme, d->block_m, half_tiles, packed, g2, passes, s)
-               : launch_gemm(d->scheme, 2, d->block_m, packed, gs2.nsub, gs2.waves, 0, g2, s);
+               : launch_gemm(d->scheme, 2, d->block_m, packed, gs2.nsub, gs2.waves, 0, -1, g2, s);
   if (e == hipSuccess) e = mark(3);
   return hip_status(e);
 }

@@ -657,7 +657,7 @@ hipError_t launch_xt(const GemmArgs& g, hipStream_t s) {
 // cross-tile pipeline whenever its K loop has a multiple of the ring's
 // steps.
 template <int S, int STAGE, int BM, bool PK, int NSUB, int WAVES>
-hipError_t launch_one(const GemmArgs& g, int ring, hipStream_t s) {
+hipError_t launch_one(const GemmArgs& g, int ring, int late_b, hipStream_t s) {
   const int nsteps = g.K / Tr<S>::BK;
   // The cross-tile pipeline: stage 1 of every scheme; stage 2 here runs
   // only for w4a16 and for long intermediates of the one-byte schemes
@@ -672,7 +672,9 @@ hipError_t launch_one(const GemmArgs& g, int ring, hipStream_t s) {
     // more rows per expert on average): measured 4-5% faster for a8w4 at
     // 4096 and 8192 tokens and the skewed W4A16 prefill, 1.6% slower at 1024
     // tokens (20 rows per expert).
-    if (nsteps >= 4 && nsteps % 4 == 0 && (long)g.P >= 48L * g.E)
+    // (late_b: 1 forces this order, 0 the other one, -1 the rule.)
+    const bool late = late_b >= 0 ? late_b == 1 : (long)g.P >= 48L * g.E;
+    if (nsteps >= 4 && nsteps % 4 == 0 && late)
       return launch_xt<S, STAGE, BM, PK, NSUB, WAVES, XT2, 4, true>(g, s);
   }
   if (nsteps >= 4 && nsteps % 4 == 0)
@@ -685,13 +687,13 @@ hipError_t launch_one(const GemmArgs& g, int ring, hipStream_t s) {
 }
 
 template <int S, int STAGE, bool PK>
-hipError_t launch_bm(int block_m, int nsub, int waves, int ring, const GemmArgs& g,
+hipError_t launch_bm(int block_m, int nsub, int waves, int ring, int late_b, const GemmArgs& g,
                      hipStream_t s) {
 #ifdef QMOE_ENABLE_WIDE
   if (nsub == 4 && waves == 4) {
     switch (block_m) {
-      case 64: return launch_one<S, STAGE, 64, PK, 4, 4>(g, ring, s);
-      case 128: return launch_one<S, STAGE, 128, PK, 4, 4>(g, ring, s);
+      case 64: return launch_one<S, STAGE, 64, PK, 4, 4>(g, ring, late_b, s);
+      case 128: return launch_one<S, STAGE, 128, PK, 4, 4>(g, ring, late_b, s);
       default: return hipErrorInvalidValue;
     }
   }
@@ -699,41 +701,41 @@ hipError_t launch_bm(int block_m, int nsub, int waves, int ring, const GemmArgs&
   if (nsub != 2) return hipErrorInvalidValue;
   if (waves == 8) {
     switch (block_m) {
-      case 64: return launch_one<S, STAGE, 64, PK, 2, 8>(g, ring, s);
-      case 128: return launch_one<S, STAGE, 128, PK, 2, 8>(g, ring, s);
+      case 64: return launch_one<S, STAGE, 64, PK, 2, 8>(g, ring, late_b, s);
+      case 128: return launch_one<S, STAGE, 128, PK, 2, 8>(g, ring, late_b, s);
       default: return hipErrorInvalidValue;
     }
   }
   if (waves != 4) return hipErrorInvalidValue;
   switch (block_m) {
-    case 16: return launch_one<S, STAGE, 16, PK, 2, 4>(g, ring, s);
-    case 32: return launch_one<S, STAGE, 32, PK, 2, 4>(g, ring, s);
-    case 64: return launch_one<S, STAGE, 64, PK, 2, 4>(g, ring, s);
-    case 128: return launch_one<S, STAGE, 128, PK, 2, 4>(g, ring, s);
+    case 16: return launch_one<S, STAGE, 16, PK, 2, 4>(g, ring, late_b, s);
+    case 32: return launch_one<S, STAGE, 32, PK, 2, 4>(g, ring, late_b, s);
+    case 64: return launch_one<S, STAGE, 64, PK, 2, 4>(g, ring, late_b, s);
+    case 128: return launch_one<S, STAGE, 128, PK, 2, 4>(g, ring, late_b, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <int S, int STAGE>
-hipError_t launch_layout(bool packed, int block_m, int nsub, int waves, int ring,
+hipError_t launch_layout(bool packed, int block_m, int nsub, int waves, int ring, int late_b,
                          const GemmArgs& g, hipStream_t s) {
-  return packed ? launch_bm<S, STAGE, true>(block_m, nsub, waves, ring, g, s)
-                : launch_bm<S, STAGE, false>(block_m, nsub, waves, ring, g, s);
+  return packed ? launch_bm<S, STAGE, true>(block_m, nsub, waves, ring, late_b, g, s)
+                : launch_bm<S, STAGE, false>(block_m, nsub, waves, ring, late_b, g, s);
 }
 
 }  // namespace
 
 hipError_t launch_gemm(int scheme, int stage, int block_m, bool packed, int nsub, int waves,
-                       int ring, const GemmArgs& g, hipStream_t s) {
+                       int ring, int late_b, const GemmArgs& g, hipStream_t s) {
   switch (scheme * 2 + (stage - 1)) {
-    case 0: return launch_layout<kW4A16, 1>(packed, block_m, nsub, waves, ring, g, s);
-    case 1: return launch_layout<kW4A16, 2>(packed, block_m, nsub, waves, ring, g, s);
-    case 2: return launch_layout<kW8A8, 1>(packed, block_m, nsub, waves, ring, g, s);
-    case 3: return launch_layout<kW8A8, 2>(packed, block_m, nsub, waves, ring, g, s);
-    case 4: return launch_layout<kA8W4, 1>(packed, block_m, nsub, waves, ring, g, s);
-    case 5: return launch_layout<kA8W4, 2>(packed, block_m, nsub, waves, ring, g, s);
-    case 6: return launch_layout<kW4A8, 1>(packed, block_m, nsub, waves, ring, g, s);
-    case 7: return launch_layout<kW4A8, 2>(packed, block_m, nsub, waves, ring, g, s);
+    case 0: return launch_layout<kW4A16, 1>(packed, block_m, nsub, waves, ring, late_b, g, s);
+    case 1: return launch_layout<kW4A16, 2>(packed, block_m, nsub, waves, ring, late_b, g, s);
+    case 2: return launch_layout<kW8A8, 1>(packed, block_m, nsub, waves, ring, late_b, g, s);
+    case 3: return launch_layout<kW8A8, 2>(packed, block_m, nsub, waves, ring, late_b, g, s);
+    case 4: return launch_layout<kA8W4, 1>(packed, block_m, nsub, waves, ring, late_b, g, s);
+    case 5: return launch_layout<kA8W4, 2>(packed, block_m, nsub, waves, ring, late_b, g, s);
+    case 6: return launch_layout<kW4A8, 1>(packed, block_m, nsub, waves, ring, late_b, g, s);
+    case 7: return launch_layout<kW4A8, 2>(packed, block_m, nsub, waves, ring, late_b, g, s);
     default: return hipErrorInvalidValue;
   }
 }

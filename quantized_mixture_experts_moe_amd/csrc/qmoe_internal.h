@@ -50,8 +50,11 @@ hipError_t launch_align(const int32_t* ids, int T, int k, int E, int block_m, in
                         int32_t* flags, int cap, hipStream_t s);
 // ring: 0 = the depth the kernel picks (8 steps for tiles of up to 32 rows,
 // 16 for a8w4, when the K loop has a multiple of 8 steps; else 4), 4 = four.
+// late_b (128-row tiles of 8 waves): 1 = a step's weight loads behind its
+// MFMAs, 0 = in front of them, -1 = by the rule (behind at 48 or more pairs
+// per expert).
 hipError_t launch_gemm(int scheme, int stage, int block_m, bool packed, int nsub, int waves,
-                       int ring, const GemmArgs& g, hipStream_t s);
+                       int ring, int late_b, const GemmArgs& g, hipStream_t s);
 // Stage 2 with the tile's activation rows resident in LDS (gemm_s2.hip):
 // available for the one-byte-activation schemes with I <= 1024; its column
 // passes are stage2_resident_cols() wide and a work item covers `passes`
