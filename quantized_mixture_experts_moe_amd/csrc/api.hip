@@ -107,7 +107,9 @@ struct TileCfg {
   int s2_waves;   // row-major stage 2 (W4A16, W4A8, I > 1024): as s1_waves
   int s2_passes;  // resident stage 2: column passes per work item; 0 = rule
   int s2_half;    // resident stage 2: -1 = rule, 0 = whole tiles, 1 = half tiles
-  int s1_late;    // stage-1 weight loads behind the MFMAs: -1 = rule, 0 = in front, 1 = behind
+  // Stage-1 weight loads behind the MFMAs: -1 = rule, 0 = in front, 1 =
+  // behind (tile-table rows leave it out: the rule).
+  int s1_late = -1;
 };
 constexpr TileCfg kRuleCfg = {0, 0, -1, 0, 0, -1, -1};
 
