@@ -176,7 +176,7 @@ SWEEP = ("w4a16_qwen3moe_t128", "w8a8_t2048", "a8w4_large@T1", "a8w4_large@T2",
          "a8w4_tp4@T4096", "w4a16_skewed_t8192", "w4a8_qwen3moe_t128", "w4a8_t2048",
          "w4a8_skewed_t8192")
 # Batches the sweep also runs through the other path (the one-launch
-# qmoe_decode above 2 tokens, the multi-launch path at 1-2 tokens).
+# qmoe_decode above 4 tokens, the multi-launch path at 1-4 tokens).
 SWEEP_BOTH_PATHS = ("a8w4_large@T1", "a8w4_large@T2", "a8w4_large@T4", "a8w4_large@T16")
 
 
@@ -680,11 +680,11 @@ def main():
     ap.add_argument("--no-flush", action="store_true",
                     help="no cache flush between timed steps (steps run back to back)")
     ap.add_argument("--grouped", action="store_true",
-                    help="batches of up to 2 tokens take the multi-launch path (route and "
+                    help="batches of up to 4 tokens take the multi-launch path (route and "
                          "align, grouped FFN, combine) instead of the one-launch qmoe_decode")
     ap.add_argument("--decode", action="store_true",
                     help="batches of up to 16 tokens take the one-launch qmoe_decode (the "
-                         "default choice sends only batches of up to 2 tokens there)")
+                         "default choice sends only batches of up to 4 tokens there)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,

@@ -321,13 +321,16 @@ qmoe_status qmoe_combine(const void* y_pairs, int32_t y_dtype, const float* topk
  *   launch order, and means the outputs are wrong and the workspace must be
  *   zeroed again).
  * Requirements as for qmoe_grouped_ffn.  QMOE_ERR_UNSUPPORTED for T above
- * QMOE_DECODE_MAX_TOKENS or E above 1024; QMOE_ERR_INVALID_ARG for null
+ * QMOE_DECODE_MAX_TOKENS, E above 1024, or I above QMOE_DECODE_MAX_INTER
+ * in the schemes with quantized activations (each stage-2 workgroup holds
+ * 16 requantized h rows in LDS); QMOE_ERR_INVALID_ARG for null
  * pointers, a short workspace, bad sizes, flags other than
  * QMOE_FLAG_PREPACKED, a QMOE_DECODE_RING environment value other than 4
  * or 6 (the K loops' prefetch depth) or a QMOE_DECODE_G value other than
  * 1, 2, 4 or 8 dividing H / 128 (32-column chunks per stage-2 work unit);
  * both only change how the work is split, for measurements.             */
 #define QMOE_DECODE_MAX_TOKENS 16
+#define QMOE_DECODE_MAX_INTER 4096
 size_t qmoe_decode_workspace(const qmoe_ffn_desc* d);
 qmoe_status qmoe_decode(const qmoe_ffn_desc* d, const float* logits, const void* x,
                         const float* x_scale, const qmoe_weights* w, int32_t* topk_ids,

@@ -215,6 +215,7 @@ static qmoe_status check_decode_desc(const qmoe_ffn_desc* d) {
   if (d->H % 32 != 0 || d->I % 32 != 0) return QMOE_ERR_INVALID_ARG;
   if (d->flags & ~QMOE_FLAG_PREPACKED) return QMOE_ERR_INVALID_ARG;
   if (d->T > decode_max_tokens() || d->E > 1024) return QMOE_ERR_UNSUPPORTED;
+  if (d->scheme != QMOE_W4A16_G32 && d->I > QMOE_DECODE_MAX_INTER) return QMOE_ERR_UNSUPPORTED;
   if (d->H % 256 != 0) return QMOE_ERR_UNSUPPORTED;
   if (d->I % (d->scheme == QMOE_A8W4_MXFP4 ? 256 : 128) != 0) return QMOE_ERR_UNSUPPORTED;
   // One expert's W13 or W2 codes are addressed with 32-bit byte offsets.

@@ -29,9 +29,10 @@
 //    into slots and then publishes every slot's record (expert, rows),
 //    which releases the slot's workgroups;
 //  - stage-1 workgroups wait for their slot's record; the last stage-1 unit
-//    of a slot to finish requantizes the slot's h rows and sets ready[j];
+//    of a slot to finish sets ready[j];
 //  - stage-2 workgroups wait for the record, issue their weight loads, then
-//    wait for ready[j];
+//    wait for ready[j] and (quantized schemes) requantize the slot's h rows
+//    into their LDS;
 //  - the last stage-2 unit to write its 32 columns of a token's k rows
 //    (ccnt[t][c]) combines them.
 // One wave per workgroup polls a flag (of its copy, see kCopies) and hands
@@ -104,8 +105,8 @@ struct DecodeArgs {
   int32_t* ccnt;         // [T, c2]: stage-2 units finished per token and column group
   float* h32;            // [P, I]: fp32 h (requantized schemes)
   float* pmax;           // [P, c1]: |h| max per 16 columns
-  void* hq;              // [P, I]: stage-2 activations (codes; bf16 for W4A16)
-  float* hs;             // [P]: row scales of hq
+  void* hq;              // [P, I]: W4A16's bf16 h (the quantized schemes requantize
+                         // h32 into each stage-2 workgroup's LDS)
   uint64_t spin_ticks;
 };
 
@@ -352,10 +353,15 @@ struct Slot {
   u32x4 a[Tr<S>::A_FRAG / 16];
 };
 
+// Where a unit's activation rows are read from: global memory written
+// before the launch (x), global memory another wave wrote (device-coherent
+// loads), or this workgroup's LDS.
+enum ASrc { kFromGlobal, kFromCoherent, kFromLds };
+
 // One K step of a unit: the loads of a ring slot and its MFMAs.  The
 // weight loads of sub-tile s start at code byte boff[s] and scale byte
 // soff[s] (K step 0); the activation loads at arow.
-template <int S, bool PK, bool COH>
+template <int S, bool PK, int SRC>
 struct KStep {
   using T_ = Tr<S>;
   using Acc = typename T_::Acc;
@@ -403,7 +409,24 @@ struct KStep {
   }
   __device__ __attribute__((always_inline)) void load_a(Slot<S>& sl, int ks) const {
     const uint8_t* src = arow + (uint32_t)ks * T_::A_STEP;
-    if constexpr (COH) {
+    if constexpr (SRC == kFromLds) {
+      typedef __attribute__((address_space(3))) const uint8_t lds_u8;
+      typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+      const lds_u8* ls = (const lds_u8*)src;
+#pragma unroll
+      for (int f = 0; f < NF; f++) {
+        if constexpr (S == kW4A8) {
+          const u32x2 p0 = *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(
+              ls + 64 * f + 8 * lq);
+          const u32x2 p1 = *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(
+              ls + 64 * f + 32 + 8 * lq);
+          sl.a[f] = u32x4{p0.x, p0.y, p1.x, p1.y};
+        } else {
+          sl.a[f] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+              ls + a_frag_offset<S, PK>(lq, f));
+        }
+      }
+    } else if constexpr (SRC == kFromCoherent) {
       // Another wave wrote these rows: four device-coherent 32-bit loads
       // per 16 bytes (W4A8: two per 8-byte piece).
       auto w32 = [&](int off) __attribute__((always_inline)) {
@@ -455,8 +478,8 @@ struct KStep {
 // The K loop of one unit: acc[s] += rows (16, A) x weight rows of sub-tile s,
 // K steps 0..n-1 in order.  The weight loads of the first R steps are issued
 // before wait() returns; the activation loads after it.
-template <int S, bool PK, int R, bool COH, class Wait>
-__device__ inline void k_loop(const KStep<S, PK, COH>& ks, const uint32_t (&boff)[2],
+template <int S, bool PK, int R, int SRC, class Wait>
+__device__ inline void k_loop(const KStep<S, PK, SRC>& ks, const uint32_t (&boff)[2],
                               const uint32_t (&soff)[2], int n, typename Tr<S>::Acc (&acc)[2],
                               Wait wait) {
   Slot<S> ring[R];
@@ -519,8 +542,8 @@ __device__ inline void k_loop(const KStep<S, PK, COH>& ks, const uint32_t (&boff
 // last R steps of a chunk load the next chunk's first R steps, so one
 // chunk's epilogue overlaps the loads of the next, and those of the last
 // chunk load nothing.
-template <int S, bool PK, int R, bool COH, class Wait, class Epi>
-__device__ inline void k_loop_chunks(const KStep<S, PK, COH>& ks, const uint32_t (&boff)[2],
+template <int S, bool PK, int R, int SRC, class Wait, class Epi>
+__device__ inline void k_loop_chunks(const KStep<S, PK, SRC>& ks, const uint32_t (&boff)[2],
                                      const uint32_t (&soff)[2], uint32_t bchunk,
                                      uint32_t schunk, int n, int nch, Wait wait, Epi epi) {
   using Acc = typename Tr<S>::Acc;
@@ -636,8 +659,8 @@ __device__ void stage1_unit(const DecodeArgs& g, int j, int c, uint32_t* s_rec) 
   const int tok = sr.pair / g.k;
   const uint8_t* arow = reinterpret_cast<const uint8_t*>(g.x) + (size_t)tok * H * T_::A_ELEM;
   Acc acc[2] = {Acc{0, 0, 0, 0}, Acc{0, 0, 0, 0}};
-  k_loop<S, PK, R, false>(KStep<S, PK, false>(B, Sc, arow), boff, soff, H / T_::BK, acc,
-                          [] {});
+  k_loop<S, PK, R, kFromGlobal>(KStep<S, PK, kFromGlobal>(B, Sc, arow), boff, soff, H / T_::BK,
+                                acc, [] {});
 
   // Epilogue: lane (lq, lr) holds rows 4lq + r of h column c*16 + lr.
   float ws[2] = {1.f, 1.f};
@@ -679,30 +702,9 @@ __device__ void stage1_unit(const DecodeArgs& g, int j, int c, uint32_t* s_rec) 
   release();
   if (wave_add(&g.s1cnt[j], 1) != g.c1 - 1) return;
 
-  // The slot's last stage-1 unit: requantize its rows (W4A16 passes h on
-  // in bf16), then let its stage-2 units go.
+  // The slot's last stage-1 unit lets its stage-2 units go (they quantize
+  // the slot's rows themselves; W4A16 passes h on in bf16).
   if (lane == 0) atomic_set(&g.s1cnt[j], 0);
-  acquire();
-  if constexpr (S != kW4A16) {
-    constexpr bool FP8 = S == kA8W4;
-    for (int row = 0; row < sr.nrows; row++) {
-      const int p = __shfl(sr.pair, row, 64);
-      float a = 0.f;
-      for (int i = lane; i < g.c1; i += 64) a = fmaxf(a, cload(&g.pmax[(size_t)p * g.c1 + i]));
-      a = wave_max(a);
-      const float s = rq::row_scale<FP8>(a);
-      if (lane == 0) cstore(&g.hs[p], s);
-      const bool refine = s >= 0x1p-60f;
-      const float rc = 1.0f / s;
-      const float* src = g.h32 + (size_t)p * I;
-      uint32_t* dst = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(g.hq) + (size_t)p * I);
-      for (int i = lane; i < I / 4; i += 64) {
-        const float v0 = cload(src + 4 * i), v1 = cload(src + 4 * i + 1);
-        const float v2 = cload(src + 4 * i + 2), v3 = cload(src + 4 * i + 3);
-        cstore(dst + i, rq::quant4<FP8>(v0, v1, v2, v3, s, rc, refine));
-      }
-    }
-  }
   release();
   if (lane < kCopies) {
     const int b2 = stage2_block(g, j);
@@ -736,7 +738,7 @@ __device__ inline void combine_cols(const DecodeArgs& g, int t, int c, const flo
 
 template <int S, bool PK, int R>
 __device__ void stage2_unit(const DecodeArgs& g, int j, int cg, uint32_t* s_rec,
-                            const float* lds_w) {
+                            const float* lds_w, uint8_t* qrows) {
   using T_ = Tr<S>;
   using Acc = typename T_::Acc;
   SlotRows sr;
@@ -748,15 +750,29 @@ __device__ void stage2_unit(const DecodeArgs& g, int j, int cg, uint32_t* s_rec,
   const uint8_t* B = reinterpret_cast<const uint8_t*>(g.w2) + (size_t)sr.e * H * kbytes;
   const uint8_t* Sc =
       reinterpret_cast<const uint8_t*>(g.w2_scale) + (size_t)sr.e * H * (I / 32) * SB;
-  const uint8_t* arow = reinterpret_cast<const uint8_t*>(g.hq) + (size_t)sr.pair * I * T_::A_ELEM;
+  // The A rows: W4A16's bf16 h straight from global memory (device-coherent
+  // loads); the quantized schemes' rows from LDS, where the workgroup
+  // quantizes them (qrows: nrows rows of I codes, pitch I + 16 so that the
+  // fragment reads of 16 rows hit 16 different bank groups; qscale: their
+  // scales).
+  constexpr int SRC = S == kW4A16 ? kFromCoherent : kFromLds;
+  const int qpitch = I + 16;
+  float* const qscale = reinterpret_cast<float*>(qrows + kMaxTokens * qpitch);
+  const uint8_t* arow =
+      S == kW4A16 ? reinterpret_cast<const uint8_t*>(g.hq) + (size_t)sr.pair * I * T_::A_ELEM
+                  : qrows + (size_t)min(lr, sr.nrows - 1) * qpitch;
   // This lane's rows (4lq + r) of the epilogue: pair and h row scale.
   int prow[4];
   float rsc[4] = {1.f, 1.f, 1.f, 1.f};
 #pragma unroll
   for (int r = 0; r < 4; r++) prow[r] = __shfl(sr.pair, 4 * lq + r, 64);
-  const KStep<S, PK, true> ks(B, Sc, arow);
+  const KStep<S, PK, SRC> ks(B, Sc, arow);
   const int n = I / T_::BK;
-  // Wave 0 polls the workgroup's copy of the flag.
+  // Wave 0 polls the workgroup's copy of the flag; then (quantized schemes)
+  // the four waves requantize the slot's rows into LDS, wave w taking rows
+  // w, w + 4, ...: the row scale from the maxima of its 16-column groups,
+  // each group of four values to four codes (the recipe of the grouped
+  // path's requantization), and the row scales for the epilogue.
   auto wait_ready = [&] {
     if ((threadIdx.x >> 6) == 0) {
       int32_t* f = &g.ready[(blockIdx.x % kCopies) * g.smax + j];
@@ -764,12 +780,49 @@ __device__ void stage2_unit(const DecodeArgs& g, int j, int cg, uint32_t* s_rec,
       if (lane == 0) atomic_add(f, -1);
     }
     __syncthreads();
+    if constexpr (S != kW4A16) {
+      constexpr bool FP8 = S == kA8W4;
+      const int wave = threadIdx.x >> 6;
+      for (int r = wave; r < sr.nrows; r += kWaves) {
+        const int p = __shfl(sr.pair, r, 64);
+        const float* src = g.h32 + (size_t)p * I;
+        uint32_t* dst = reinterpret_cast<uint32_t*>(qrows + r * qpitch);
+        // The row maxima and the first 1024 values are loaded together.
+        float a = 0.f;
+        for (int i = lane; i < g.c1; i += 64) a = fmaxf(a, cload(&g.pmax[(size_t)p * g.c1 + i]));
+        float v[4][4];
+#pragma unroll
+        for (int b = 0; b < 4; b++) {
+          const int i = lane + 64 * b;
+          if (i < I / 4) {
+#pragma unroll
+            for (int e = 0; e < 4; e++) v[b][e] = cload(src + 4 * i + e);
+          }
+        }
+        a = wave_max(a);
+        const float sc = rq::row_scale<FP8>(a);
+        const bool refine = sc >= 0x1p-60f;
+        const float rc = 1.0f / sc;
+#pragma unroll
+        for (int b = 0; b < 4; b++) {
+          const int i = lane + 64 * b;
+          if (i < I / 4) dst[i] = rq::quant4<FP8>(v[b][0], v[b][1], v[b][2], v[b][3], sc, rc, refine);
+        }
+        for (int i = lane + 256; i < I / 4; i += 64) {
+          const float v0 = cload(src + 4 * i), v1 = cload(src + 4 * i + 1);
+          const float v2 = cload(src + 4 * i + 2), v3 = cload(src + 4 * i + 3);
+          dst[i] = rq::quant4<FP8>(v0, v1, v2, v3, sc, rc, refine);
+        }
+        if (lane == 0) qscale[r] = sc;
+      }
+      __syncthreads();
+    }
   };
   auto load_rsc = [&] {
     if constexpr (S != kW4A16) {
 #pragma unroll
       for (int r = 0; r < 4; r++)
-        if (4 * lq + r < sr.nrows) rsc[r] = cload(&g.hs[prow[r]]);
+        if (4 * lq + r < sr.nrows) rsc[r] = qscale[4 * lq + r];
     }
   };
   // W8A8's per-column weight scales of 32-column chunk c.
@@ -813,7 +866,7 @@ __device__ void stage2_unit(const DecodeArgs& g, int j, int cg, uint32_t* s_rec,
     weight_offsets<S, PK>(nrow, I, boff, soff);
     float ws[2] = {1.f, 1.f};
     load_ws(c0, ws);
-    k_loop_chunks<S, PK, R, true>(
+    k_loop_chunks<S, PK, R, SRC>(
         ks, boff, soff, 32u * (uint32_t)kbytes, (uint32_t)I * SB, n, g.G,
         [&] {
           wait_ready();
@@ -830,10 +883,10 @@ __device__ void stage2_unit(const DecodeArgs& g, int j, int cg, uint32_t* s_rec,
       weight_offsets<S, PK>(nrow, I, boff, soff);
       Acc acc[2] = {Acc{0, 0, 0, 0}, Acc{0, 0, 0, 0}};
       if (first) {
-        k_loop<S, PK, R, true>(ks, boff, soff, n, acc, wait_ready);
+        k_loop<S, PK, R, SRC>(ks, boff, soff, n, acc, wait_ready);
         load_rsc();
       } else {
-        k_loop<S, PK, R, true>(ks, boff, soff, n, acc, [] {});
+        k_loop<S, PK, R, SRC>(ks, boff, soff, n, acc, [] {});
       }
       float ws[2] = {1.f, 1.f};
       load_ws(c, ws);
@@ -866,6 +919,9 @@ template <int S, bool PK, int R>
 __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs g) {
   __shared__ AlignLds lds;
   __shared__ uint32_t s_rec[8];
+  // Quantized schemes: a stage-2 workgroup's requantized slot rows and
+  // their scales (decode_lds_bytes).
+  extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
   // The workgroup's four units: all routing units, or four column chunks of
   // one slot in one stage (u0, c1 and c2 are multiples of four).
   const int u = blockIdx.x * kWaves + (threadIdx.x >> 6);
@@ -885,7 +941,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs g) {
     return;
   }
   v -= n1;
-  if (v < g.smax * g.c2) stage2_unit<S, PK, R>(g, v / g.c2, v % g.c2, s_rec, lds.wts);
+  if (v < g.smax * g.c2) stage2_unit<S, PK, R>(g, v / g.c2, v % g.c2, s_rec, lds.wts, dyn_lds);
 }
 
 }  // namespace
@@ -924,11 +980,10 @@ DecodeWs decode_ws_layout(int scheme, int H, int I, int E, int k) {
     off = up(off + P * I * 4);
     w.pmax = off;
     off = up(off + P * c1 * 4);
-    w.hs = off;
-    off = up(off + P * 4);
+  } else {
+    w.hq = off;
+    off = up(off + P * I * 2);
   }
-  w.hq = off;
-  off = up(off + P * I * (w4a16 ? 2 : 1));
   w.y = off;
   off = up(off + P * H * (scheme == kW8A8 ? 4 : 2));
   w.total = off;
@@ -937,7 +992,8 @@ DecodeWs decode_ws_layout(int scheme, int H, int I, int E, int k) {
 
 template <int S, bool PK, int R>
 static hipError_t launch_t(const DecodeArgs& g, unsigned blocks, hipStream_t s) {
-  hipLaunchKernelGGL((decode_kernel<S, PK, R>), dim3(blocks), dim3(kWaves * 64), 0, s, g);
+  const size_t dyn = S == kW4A16 ? 0 : (size_t)kMaxTokens * (g.I + 16 + 4);
+  hipLaunchKernelGGL((decode_kernel<S, PK, R>), dim3(blocks), dim3(kWaves * 64), dyn, s, g);
   return hipGetLastError();
 }
 
@@ -998,8 +1054,7 @@ hipError_t launch_decode(int scheme, bool packed, int ring, int chunks, int T, i
   g.ccnt = reinterpret_cast<int32_t*>(base + L.ccnt);
   g.h32 = scheme == kW4A16 ? nullptr : reinterpret_cast<float*>(base + L.h32);
   g.pmax = scheme == kW4A16 ? nullptr : reinterpret_cast<float*>(base + L.pmax);
-  g.hs = scheme == kW4A16 ? nullptr : reinterpret_cast<float*>(base + L.hs);
-  g.hq = base + L.hq;
+  g.hq = scheme == kW4A16 ? base + L.hq : nullptr;
   g.spin_ticks = spin_ticks;
   const long units = (long)g.u0 + (long)g.smax * (g.c1 + g.c2);
   const unsigned blocks = (unsigned)((units + kWaves - 1) / kWaves);

@@ -92,7 +92,7 @@ int device_cu_count();
 // leaves them zero).
 struct DecodeWs {
   size_t flags, route_cnt, slot_flag, slot_rec, s1cnt, ready, ccnt, counter_bytes;
-  size_t h32, pmax, hs, hq, y, total;
+  size_t h32, pmax, hq, y, total;  // h32 and pmax: quantized schemes; hq: W4A16
 };
 int decode_max_tokens();
 DecodeWs decode_ws_layout(int scheme, int H, int I, int E, int k);

@@ -37,11 +37,12 @@ EXPORTS = (
 DECODE_MAX_TOKENS = 16
 # Batches up to this size take the one-launch qmoe_decode in moe_forward's
 # automatic choice: measured on one MI355X for the 512-expert top-10 a8w4
-# block, the one launch is faster at 1 and 2 tokens (44.6 against 47.2 us,
-# 59.6 against 65.0 us), slower from 4 tokens on (88.2 against 86.8 us; 16
-# tokens 0.235 against 0.203 ms), where the grouped kernels stream the
-# weights at a higher rate.
-DECODE_PREFERRED_MAX_TOKENS = 2
+# block (both paths on the same box), the one launch is faster at 1, 2 and
+# 4 tokens (42.3 against 47.1 us, 58.2 against 64.9 us, 85.6 against 87.1
+# us), level at 3 (72.1 against 71.6 us), slower from 6 tokens on (114.2
+# against 111.2 us; 8 tokens 140.5 against 132.2 us), where the grouped
+# kernels stream the weights at a higher rate.
+DECODE_PREFERRED_MAX_TOKENS = 4
 
 
 class QmoeError(RuntimeError):

@@ -207,6 +207,8 @@ def test_decode_workspace_and_validation(monkeypatch):
     assert call(_desc(T=1, E=2000)) == UNS
     assert call(_desc(T=1, H=288)) == UNS
     assert call(_desc(T=1, I=128)) == UNS  # a8w4 needs I % 256
+    assert call(_desc(T=1, I=4352)) == UNS  # quantized activations: I above 4096
+    assert ws_of(_desc(T=1, I=4352)) == 0
     assert call(_desc(T=1, k=17, E=32)) == INV
     assert call(_desc(T=1, flags=ops.QMOE_FLAG_DUMP_ACC)) == INV
     assert call(_desc(T=1), logits=None) == INV
