@@ -716,13 +716,15 @@ def main():
         tile_sweep(args, torch)
         return
     if args.sweep:
+        from quantized_mixture_experts_moe_amd import ops
         for name in SWEEP:
             print(json.dumps(run_workload(name, args, torch, not args.no_cpu_baseline,
                                           min(args.cpu_seconds, 8.0))), flush=True)
             if name in SWEEP_BOTH_PATHS:
                 other = argparse.Namespace(**vars(args))
                 t = int(name.split("@T")[1])
-                other.grouped, other.decode = t <= 2, t > 2
+                one_launch = t <= ops.DECODE_PREFERRED_MAX_TOKENS  # the default path
+                other.grouped, other.decode = one_launch, not one_launch
                 print(json.dumps(run_workload(name, other, torch, False)), flush=True)
         return
     res = run_workload(args.workload, args, torch, not args.no_cpu_baseline, args.cpu_seconds)
