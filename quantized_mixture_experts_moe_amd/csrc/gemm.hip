@@ -358,7 +358,14 @@ __global__ __launch_bounds__(WAVES * 64)
     // With FRAG2 the reads run one group ahead (two fragment buffers);
     // otherwise each group's reads directly precede its MFMAs and the other
     // wave on the SIMD covers the LDS latency (the 4-wave a8w4 128-row tile
-    // has no registers left for the second buffer).
+    // has no registers left for the second buffer).  In tiles of 64 rows or
+    // more the read ahead is unconditional (a group past the tile's rows
+    // reads rows it never uses): were it skipped on some path, the counter
+    // wait in front of the next group's MFMAs would have to assume the skip
+    // and wait for every read in flight, the next group's too (measured:
+    // stage 1 of the skewed W4A16 prefill 4% faster).  Shorter tiles, most
+    // often one 16-row group full, keep the check: the unused reads cost
+    // more there.
     constexpr bool FRAG2 = !(S == kA8W4 && BM >= 128 && (WAVES == 4 || STAGE == 2));
     auto compute = [&](int stage, const BFrag<S>(&bcr)[NSUB]) __attribute__((always_inline)) {
       BReady<S> bc[NSUB];
@@ -370,7 +377,8 @@ __global__ __launch_bounds__(WAVES * 64)
       for (int m = 0; m < MSUB; m++) {
         if (m < mvalid) {
           if constexpr (FRAG2) {
-            if (m + 1 < MSUB && m + 1 < mvalid) read_frag((m & 1) ? fa : fb, stage, m + 1);
+            if (m + 1 < MSUB && (BM >= 64 || m + 1 < mvalid))
+              read_frag((m & 1) ? fa : fb, stage, m + 1);
 #pragma unroll
             for (int s = 0; s < NSUB; s++) mfma_step<S>(acc[m][s], (m & 1) ? fb : fa, bc[s]);
           } else {
