@@ -103,7 +103,8 @@ static FfnWs ffn_ws_layout(const qmoe_ffn_desc& d) {
 struct TileCfg {
   int s1_waves;   // stage-1 block: 4 or 8 waves (8 needs block_m >= 64); 0 = rule
   int s1_ring;    // stage-1 weight prefetch ring: 0 = kernel's pick, 4 = four steps
-  int s1_runs;    // stage-1 schedule: -1 = rule, 0 = strided items, 1 = runs of row tiles
+  int s1_runs;    // stage-1 schedule: -1 = rule, 0 = strided items, 1 = runs of row tiles,
+                  // 2 = row tiles dealt to the XCDs (also stage 2's, row-major kernel)
   int s2_waves;   // row-major stage 2 (W4A16, W4A8, I > 1024): as s1_waves
   int s2_passes;  // resident stage 2: column passes per work item; 0 = rule
   int s2_half;    // resident stage 2: -1 = rule, 0 = whole tiles, 1 = half tiles
@@ -506,7 +507,7 @@ static qmoe_status grouped_ffn_impl(const qmoe_ffn_desc* d, const void* x, const
   GemmShape gs2 = choose_shape(d->scheme, 2, d->block_m);
   auto waves_ok = [&](int w) { return w == 0 || w == 4 || (w == 8 && d->block_m >= 64); };
   if (!waves_ok(cfg.s1_waves) || !waves_ok(cfg.s2_waves) ||
-      (cfg.s1_ring != 0 && cfg.s1_ring != 4) || cfg.s1_runs < -1 || cfg.s1_runs > 1 ||
+      (cfg.s1_ring != 0 && cfg.s1_ring != 4) || cfg.s1_runs < -1 || cfg.s1_runs > 2 ||
       cfg.s2_half < -1 || cfg.s2_half > 1 || cfg.s2_passes < 0 || cfg.s1_late < -1 ||
       cfg.s1_late > 1 ||
       (cfg.s2_half == 1 && (!resident || d->block_m < 32)) ||
@@ -529,9 +530,18 @@ static qmoe_status grouped_ffn_impl(const qmoe_ffn_desc* d, const void* x, const
   // stage-1 blocks take runs of consecutive row tiles (an expert's second
   // tile then reads its weights from the memory-side cache); measured
   // neutral or slower for the other schemes and tile heights.
+  // W4A16 and W4A8 tiles of 64 rows or more over 256 experts or more: row
+  // tiles dealt to the XCDs, so that each XCD gets the same mix of full and
+  // partial tiles (skewed 8192-token prefill over 512 experts: W4A16 step
+  // 2.76 -> 2.65 ms, W4A8 4.50 -> 4.23 ms; the 2048-token W4A8 step over 128
+  // experts, whose tiles are all about full, 2-3% slower with it, and the
+  // a8w4 8192-token step, which takes runs, 4.5% slower).
   g1.schedule = (d->scheme == QMOE_A8W4_MXFP4 && d->block_m == 128 &&
                  (long)d->T * d->k > (long)d->E * d->block_m)
                     ? 1
+                : ((d->scheme == QMOE_W4A16_G32 || d->scheme == QMOE_W4A8_G32) &&
+                   d->block_m >= 64 && d->E >= 256)
+                    ? 2
                     : 0;
   if (cfg.s1_runs >= 0) g1.schedule = cfg.s1_runs;
   // Stage-2 work split, settled (and checked) before anything is launched.
@@ -589,7 +599,7 @@ static qmoe_status grouped_ffn_impl(const qmoe_ffn_desc* d, const void* x, const
   e = mark(2);
   if (e != hipSuccess) return hip_status(e);
 
-  g2.schedule = 0;
+  g2.schedule = g1.schedule == 2 ? 2 : 0;  // the resident stage 2 splits its own work
   g2.N = d->H;
   g2.K = d->I;
   if (fuse_requant) {

@@ -118,22 +118,37 @@ __global__ __launch_bounds__(WAVES * 64)
   //    a block's consecutive items are consecutive row tiles of one column
   //    tile: when they belong to the same expert the second one reads the
   //    weights the first has just read (memory-side cache hits).  Taken
-  //    only when per_xcd is a multiple of ntiles_n (schedule 0 otherwise).
+  //    only when per_xcd is a multiple of ntiles_n (schedule 0 otherwise);
+  //  - schedule 2 (dealt row tiles): the XCD takes every eighth row tile
+  //    (m = xcd, xcd + 8, ...) with all its column tiles, the blocks of the
+  //    XCD strided over that list.  A row tile's activation rows still stay
+  //    on one XCD, and each XCD gets the same mix of full and partial tiles:
+  //    with skewed routing the contiguous shares of schedule 0 leave the
+  //    XCDs that hold the rarely routed experts' short tiles idle for the
+  //    last third of the kernel.
   const int total = num_m * g.ntiles_n;
   const int ichunk = (total + 7) >> 3;
   const int w_begin = min(total, xcd * ichunk), w_end = min(total, w_begin + ichunk);
   const int mchunk = (num_m + 7) >> 3;
   const int m_begin = min(num_m, xcd * mchunk), nm = min(num_m, m_begin + mchunk) - m_begin;
-  const bool runs = g.schedule == 1 && per_xcd % g.ntiles_n == 0;  // else schedule 0
+  const bool runs = g.schedule == 1 && per_xcd % g.ntiles_n == 0;  // else schedule 0 or 2
+  const bool dealt = g.schedule == 2;
+  const int dealt_total = (num_m > xcd ? (num_m - xcd + 7) >> 3 : 0) * g.ntiles_n;
   const int groups = per_xcd / g.ntiles_n, grp = slot / g.ntiles_n;
   const int run_nt = slot - grp * g.ntiles_n;
   const int run_begin = grp < groups ? (int)((long)grp * nm / groups) : nm;
   const int run_end = grp < groups ? (int)((long)(grp + 1) * nm / groups) : nm;
   auto valid = [&](int u) __attribute__((always_inline)) {
+    if (dealt) return slot + u * per_xcd < dealt_total;
     return runs ? run_begin + u < run_end : w_begin + slot + u * per_xcd < w_end;
   };
   auto decode = [&](int u, int& mt_out, int& nt_out) __attribute__((always_inline)) {
-    if (runs) {
+    if (dealt) {
+      const int i = slot + u * per_xcd;
+      const int r = i / g.ntiles_n;
+      mt_out = xcd + 8 * r;
+      nt_out = i - r * g.ntiles_n;
+    } else if (runs) {
       mt_out = m_begin + run_begin + u;
       nt_out = run_nt;
     } else {

@@ -39,7 +39,8 @@ struct GemmArgs {
                          // resident stage 2: read, to quantize h while copying it
   int pmax_stride;       // column tiles of stage 1 (row pitch of row_pmax)
   int32_t* dump;         // w8a8 debug accumulators or nullptr
-  int schedule;          // stage-1 work order: 0 strided items, 1 runs of row tiles
+  int schedule;          // work order: 0 strided items, 1 runs of row tiles, 2 row tiles
+                         // dealt to the XCDs
 };
 
 hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w,

@@ -60,7 +60,7 @@ def test_tile_table_rows_are_well_formed():
         assert sc in SCHEME_CODE.values() and 1 <= k <= E and t_max >= 1
         assert bm in (16, 32, 64, 128)
         assert s1w in (0, 4, 8) and (s1w != 8 or bm >= 64)
-        assert s1r in (0, 4) and s1runs in (-1, 0, 1) and s2h in (-1, 0, 1)
+        assert s1r in (0, 4) and s1runs in (-1, 0, 1, 2) and s2h in (-1, 0, 1)
         resident = sc in (1, 2) and I <= 1024
         assert s2w == 0 or (not resident and s2w in (4, 8))
         assert s2p == 0 or (resident and (H // 256) % s2p == 0)
