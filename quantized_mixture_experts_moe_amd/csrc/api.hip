@@ -64,7 +64,7 @@ static AlignWs align_ws_layout(int T, int E) {
 
 // Layout of qmoe_grouped_ffn's workspace.
 struct FfnWs {
-  size_t h, hq, hs, pmax, acc1, acc2, total;
+  size_t h, hq, hs, pmax, acc1, acc2, queue, total;
 };
 static FfnWs ffn_ws_layout(const qmoe_ffn_desc& d) {
   const size_t cap = qmoe_align_capacity(d.T, d.k, d.E, d.block_m);
@@ -92,7 +92,10 @@ static FfnWs ffn_ws_layout(const qmoe_ffn_desc& d) {
     w.acc2 = off;
     off = align_up(off + cap * H * 4, 256);
   }
-  w.total = std::max<size_t>(off, 256);
+  // The resident stage 2's per-XCD work-item counters (stage 1 zeroes them).
+  w.queue = off;
+  off = align_up(off + 8 * 4, 256);
+  w.total = off;
   return w;
 }
 
@@ -111,6 +114,9 @@ struct TileCfg {
   // Stage-1 weight loads behind the MFMAs: -1 = rule, 0 = in front, 1 =
   // behind (tile-table rows leave it out: the rule).
   int s1_late = -1;
+  // Resident stage 2: work items claimed from per-XCD counters (-1 = rule:
+  // with half tiles, 1 = on, 0 = the static split).
+  int s2_queue = -1;
 };
 constexpr TileCfg kRuleCfg = {0, 0, -1, 0, 0, -1, -1};
 
@@ -165,6 +171,7 @@ static bool parse_tile_env(TileCfg& c) {
     else if (key == "s2p") c.s2_passes = (int)v;
     else if (key == "s2h") c.s2_half = (int)v;
     else if (key == "s1lb") c.s1_late = (int)v;
+    else if (key == "s2q") c.s2_queue = (int)v;
     else return false;
     p = end;
     if (*p == ',') p++;
@@ -509,7 +516,7 @@ static qmoe_status grouped_ffn_impl(const qmoe_ffn_desc* d, const void* x, const
   if (!waves_ok(cfg.s1_waves) || !waves_ok(cfg.s2_waves) ||
       (cfg.s1_ring != 0 && cfg.s1_ring != 4) || cfg.s1_runs < -1 || cfg.s1_runs > 2 ||
       cfg.s2_half < -1 || cfg.s2_half > 1 || cfg.s2_passes < 0 || cfg.s1_late < -1 ||
-      cfg.s1_late > 1 ||
+      cfg.s1_late > 1 || cfg.s2_queue < -1 || cfg.s2_queue > 1 ||
       (cfg.s2_half == 1 && (!resident || d->block_m < 32)) ||
       (cfg.s2_passes > 0 && !resident) || (cfg.s2_waves != 0 && resident))
     return QMOE_ERR_INVALID_ARG;
@@ -570,6 +577,17 @@ static qmoe_status grouped_ffn_impl(const qmoe_ffn_desc* d, const void* x, const
   } else {
     g2.ntiles_n = d->H / stage_cols(2, gs2.nsub, gs2.waves);
   }
+
+  // With half tiles the resident stage 2 balances its items through
+  // per-XCD counters that stage 1 zeroes: at 8192 tokens of the a8w4 block
+  // about a quarter of the half tiles hold no rows, and the static split
+  // left blocks idle for a quarter of the kernel (stage 2 0.601 -> 0.481
+  // ms).  With whole tiles the items cost about the same and the claim's
+  // round trip at each item measured 1-4% slower.
+  const bool use_queue = resident && (cfg.s2_queue >= 0 ? cfg.s2_queue == 1 : half_tiles);
+  int32_t* const queue = use_queue ? reinterpret_cast<int32_t*>(wsb + lay.queue) : nullptr;
+  g1.queue = queue;
+  g2.queue = queue;
 
   auto mark = [&](int i) -> hipError_t {
     return events ? hipEventRecord((hipEvent_t)events[i], s) : hipSuccess;

@@ -442,6 +442,10 @@ __global__ __launch_bounds__(WAVES * 64)
     for (int u = 0; u < RING; u++) step(s0 + u, bq[u], bq[(u + RING - 1) % RING]);
   };
 
+  // The resident stage 2 that follows on the stream claims its work items
+  // from per-XCD counters; they start from zero here (per-lane stores).
+  if (STAGE == 1 && g.queue != nullptr && blockIdx.x == 0 && tid < 8) g.queue[tid] = 0;
+
   int wi = 0;  // the block's item counter
   if (!valid(0)) return;
   fetch_meta(wi);

@@ -97,6 +97,7 @@ moe_stage2_resident(GemmArgs g, int passes, int tile_div) {
   constexpr int kYEs = S == kA8W4 ? 2 : 4;  // output bytes per element
   constexpr int kYRows = 32, kYPitch = kS2Cols * kYEs + 16;
   __shared__ __attribute__((aligned(16))) uint8_t sY[SY == 2 ? kYRows * kYPitch : 16];
+  __shared__ int sItem;  // the work item the block claimed from its XCD's queue
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lq = lane >> 4;
@@ -126,9 +127,20 @@ moe_stage2_resident(GemmArgs g, int passes, int tile_div) {
   Acc acc[MSUB][kS2Nsub];
   BFrag<S> b0[kS2Nsub], b1[kS2Nsub], b2[kS2Nsub], b3[kS2Nsub];
 
-  for (int wi = w_begin + slot; wi < w_end; wi += per_xcd) {
+  // Work items: with g.queue, the blocks of an XCD claim the items of its
+  // share one at a time from the XCD's counter (zeroed by stage 1, which
+  // runs before this kernel on the same stream), so that a block that drew
+  // short items (half tiles with few or no rows) takes more of them;
+  // otherwise block `slot` takes every per_xcd-th item.  Every item writes
+  // its own output rows, so the outputs do not depend on who took what.
+  for (int it = 0;; it++) {
+    if (g.queue != nullptr && tid == 0)
+      sItem = w_begin + __hip_atomic_fetch_add(&g.queue[xcd], 1, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();  // the previous item is done with sA / sRow / sScale; sItem is set
+    const int wi = g.queue != nullptr ? sItem : w_begin + slot + it * per_xcd;
+    if (wi >= w_end) break;
     const int mt = wi / nchunk, c = wi - mt * nchunk;
-    __syncthreads();  // the previous item is done with sA / sRow / sScale
     int valid_here = 0;
     if (tid < BM) {
       const int p = g.sorted_pair_ids[mt * BM + tid];

@@ -41,6 +41,8 @@ struct GemmArgs {
   int32_t* dump;         // w8a8 debug accumulators or nullptr
   int schedule;          // work order: 0 strided items, 1 runs of row tiles, 2 row tiles
                          // dealt to the XCDs
+  int32_t* queue;        // stage 1: zeroes queue[0..7] (block 0); resident stage 2: the
+                         // XCDs' work-item counters (nullptr: static split)
 };
 
 hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w,

@@ -635,7 +635,8 @@ def test_skewed_w4a16_t8192_every_token(prepacked):
 
 TILE_OVERRIDES = ["s1w=4", "s1w=8", "s1r=4", "s1runs=0", "s1runs=1", "s1lb=0", "s1lb=1",
                   "s2w=8", "s2p=1", "s2p=2", "s2p=8", "s2h=0", "s2h=1",
-                  "s1w=8,s1runs=1,s2p=4,s2h=1", "s1w=8,s1lb=1", "s1runs=2", "s1w=8,s1runs=2"]
+                  "s1w=8,s1runs=1,s2p=4,s2h=1", "s1w=8,s1lb=1", "s1runs=2", "s1w=8,s1runs=2", "s2q=0",
+                  "s2q=1,s2h=1"]
 
 
 @pytest.mark.parametrize("scheme,I,bm", [("a8w4", 256, 64), ("a8w4", 256, 128),
@@ -684,7 +685,7 @@ def test_tile_overrides_give_the_same_bits(scheme, I, bm, monkeypatch):
             assert torch.equal(got[1], ref[1]), ov
         tried += 1
     assert tried >= 4
-    for bad in ("bogus", "s1w=", "s1w=3", "s2p=3", "s1r=6", "s1w=4;s2p=2", "s1lb=2", "s1runs=3"):
+    for bad in ("bogus", "s1w=", "s1w=3", "s2p=3", "s1r=6", "s1w=4;s2p=2", "s1lb=2", "s1runs=3", "s2q=2"):
         monkeypatch.setenv("QMOE_TILE", bad)
         with pytest.raises(ops.QmoeError):
             run()
