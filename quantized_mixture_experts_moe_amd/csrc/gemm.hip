@@ -126,35 +126,35 @@ __global__ __launch_bounds__(WAVES * 64)
   //    with skewed routing the contiguous shares of schedule 0 leave the
   //    XCDs that hold the rarely routed experts' short tiles idle for the
   //    last third of the kernel.
-  const int total = num_m * g.ntiles_n;
-  const int ichunk = (total + 7) >> 3;
-  const int w_begin = min(total, xcd * ichunk), w_end = min(total, w_begin + ichunk);
+  // Schedules 0 and 2 share one form: item w of the XCD's list
+  // [w_begin, w_end) is row tile m0 + mstep * (w / ntiles_n), column tile
+  // w % ntiles_n.
+  const bool dealt = g.schedule == 2;
+  const int total = dealt ? (num_m > xcd ? (num_m - xcd + 7) >> 3 : 0) * g.ntiles_n
+                          : num_m * g.ntiles_n;
+  const int ichunk = dealt ? total : (total + 7) >> 3;
+  const int w_begin = dealt ? 0 : min(total, xcd * ichunk);
+  const int w_end = min(total, w_begin + ichunk);
+  const int m0 = dealt ? xcd : 0, mstep = dealt ? 8 : 1;
   const int mchunk = (num_m + 7) >> 3;
   const int m_begin = min(num_m, xcd * mchunk), nm = min(num_m, m_begin + mchunk) - m_begin;
   const bool runs = g.schedule == 1 && per_xcd % g.ntiles_n == 0;  // else schedule 0 or 2
-  const bool dealt = g.schedule == 2;
-  const int dealt_total = (num_m > xcd ? (num_m - xcd + 7) >> 3 : 0) * g.ntiles_n;
   const int groups = per_xcd / g.ntiles_n, grp = slot / g.ntiles_n;
   const int run_nt = slot - grp * g.ntiles_n;
   const int run_begin = grp < groups ? (int)((long)grp * nm / groups) : nm;
   const int run_end = grp < groups ? (int)((long)(grp + 1) * nm / groups) : nm;
   auto valid = [&](int u) __attribute__((always_inline)) {
-    if (dealt) return slot + u * per_xcd < dealt_total;
     return runs ? run_begin + u < run_end : w_begin + slot + u * per_xcd < w_end;
   };
   auto decode = [&](int u, int& mt_out, int& nt_out) __attribute__((always_inline)) {
-    if (dealt) {
-      const int i = slot + u * per_xcd;
-      const int r = i / g.ntiles_n;
-      mt_out = xcd + 8 * r;
-      nt_out = i - r * g.ntiles_n;
-    } else if (runs) {
+    if (runs) {
       mt_out = m_begin + run_begin + u;
       nt_out = run_nt;
     } else {
       const int w = w_begin + slot + u * per_xcd;
-      mt_out = w / g.ntiles_n;
-      nt_out = w - mt_out * g.ntiles_n;
+      const int r = w / g.ntiles_n;
+      mt_out = m0 + mstep * r;
+      nt_out = w - r * g.ntiles_n;
     }
   };
 
