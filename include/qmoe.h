@@ -166,8 +166,10 @@ qmoe_status qmoe_route(const float* logits, int32_t T, int32_t E, int32_t k,
  * (blocks, prefetch depth, column passes) when it is called with this
  * block_m; any block_m gives the same results bit for bit.  Returns 0 for
  * invalid arguments.  The environment variable QMOE_TILE
- * ("s1w=8,s1r=4,s1runs=1,s1lb=1,s2w=4,s2p=8,s2h=0", any subset) overrides those
- * other choices in qmoe_grouped_ffn for sweeps; a malformed or inapplicable
+ * ("s1w=8,s1r=4,s1runs=1,s1lb=1,s2w=4,s2p=8,s2h=0,s2q=1", any subset)
+ * overrides those other choices in qmoe_grouped_ffn for sweeps (s1runs: 0
+ * strided items, 1 runs of row tiles, 2 row tiles dealt to the XCDs; s2q:
+ * the resident stage 2's work queue off or on); a malformed or inapplicable
  * value makes qmoe_grouped_ffn return QMOE_ERR_INVALID_ARG.               */
 int32_t qmoe_default_block_m(int32_t scheme, int32_t T, int32_t H, int32_t I, int32_t E,
                              int32_t k);
@@ -249,7 +251,9 @@ qmoe_status qmoe_align_noalloc(const int32_t* topk_ids, int32_t T, int32_t k, in
  * y_pairs: [T*k, H], row p = pair p, unweighted expert output; bf16 for
  *   W4A16, A8W4 and W4A8, fp32 for W8A8.
  * ws: workspace of at least qmoe_grouped_ffn_workspace(d) bytes, 256-byte
- *   aligned.
+ *   aligned; its contents need no initialisation (the call's first kernel
+ *   clears the work-queue counters the last one uses).  Calls that share a
+ *   workspace must be ordered on one stream.
  * Requirements: H % 256 == 0, I % 128 == 0 (I % 256 for A8W4), k <= E;
  *   W4A8 scales 8-byte aligned;
  *   below 4 GiB each: x (T*H elements), the stage-2 activations (cap*I
