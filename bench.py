@@ -511,13 +511,15 @@ TILE_SWEEP_POINTS = (
 )
 TILE_SWEEP_BLOCKS = (16, 32, 64, 128)
 SCHEME_CODE_C = {"w4a16": 0, "w8a8": 1, "a8w4": 2, "w4a8": 3}
+# QMOE_TILE values that mean "the library's rule" for every tile knob.
+TILE_NEUTRAL = {"s1w": 0, "s1r": 0, "s1runs": -1, "s2w": 0, "s2p": 0, "s2h": -1}
 
 
 def _knob_values(scheme: str, bm: int, inter: int, hidden: int) -> dict:
     """The tile knobs that apply to a call, and the values the sweep tries
     (the library refuses the others).  Keys are QMOE_TILE fields."""
     resident = scheme in ("a8w4", "w8a8") and inter <= 1024
-    kv = {"s1runs": (0, 1)}
+    kv = {"s1runs": (0, 1, 2)}
     if bm >= 64:
         kv["s1w"] = (4, 8)
     if bm <= 32:
@@ -553,7 +555,10 @@ def tile_sweep(args, torch) -> None:
     stage-2 waves, column passes, half tiles), a value kept when it is at
     least 2% faster (the step's run-to-run spread is about 1%).  Accuracy gate: a configuration counts only if its
     output equals the reference (block_m 16, the library's choices) bit for
-    bit.  Inputs are drawn once per workload at its largest bucket; a bucket
+    bit.  Every timed configuration sets all knobs (the rule's values where
+    it changes none), so the library's current table plays no part and each
+    emitted row is the configuration measured.  Inputs are drawn once per
+    workload at its largest bucket; a bucket
     takes the leading tokens.  One JSON line per timed configuration, one per
     bucket with the chosen row; --emit-table writes the rows as the
     library's tile_table.inc."""
@@ -586,7 +591,10 @@ def tile_sweep(args, torch) -> None:
                   "x_scale": None if "x_scale" not in g else g["x_scale"][:T]}
 
             def measure(bm, cfg):
-                os.environ["QMOE_TILE"] = _env_str(cfg)
+                # Every knob given (the rule's value where the trial sets
+                # none), so that no tile-table entry of the library applies
+                # and the emitted row is exactly the configuration timed.
+                os.environ["QMOE_TILE"] = _env_str({**TILE_NEUTRAL, **cfg})
                 ids = torch.empty((T, k), dtype=torch.int32, device=dev)
                 tw = torch.empty((T, k), dtype=torch.float32, device=dev)
                 _, _, al = ops.route_align(gt["logits"], k, bm, ids, tw)
