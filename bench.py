@@ -56,7 +56,7 @@ DOMINANT_COUNTERS = {
     "kernel": "stage1",
     "fetch_kib": 1195528.5,
     "write_kib": 165148.4,
-    "sources_sha256_16": "bf5222c2c9fef1f6",
+    "sources_sha256_16": "bf2cf1111afff413",
     "workload": "a8w4_large@T4096",
     "block_m": 128,
     "weight_layout": "prepacked",

@@ -46,9 +46,11 @@
 // and takes that block's e8m0 scale from its own lane.  a_frag_offset()
 // gathers the A bytes to match.
 //
-// Schedule: a persistent grid (a multiple of 8 blocks, one slice of the work
-// list per XCD); work item = (row tile, column tile), row tile major, so the
-// blocks of one XCD share the same gathered activation rows in their L2.
+// Schedule: a persistent grid (a multiple of 8 blocks, one share of the work
+// list per XCD: a contiguous slice, or every eighth row tile where tiles of
+// very different fill would leave some XCDs idle); work item = (row tile,
+// column tile), row tile major, so the blocks of one XCD share the same
+// gathered activation rows in their L2.
 // Between the tiles of a block the stream of loads does not stop: in stage 1
 // (K steps a multiple of four) the K loop's last three steps issue the next
 // tile's first activation and weight loads, and the epilogue runs while they
